@@ -1,0 +1,180 @@
+// svdq_quantize_act kernel: smoothing + rank-r down-projection + symmetric
+// INT4 group-64 quantisation of the activations, in one pass over X.
+//
+// The fusion of the low-rank down-projection with input quantisation is the
+// one the remio.ai page attributes to the original Nunchaku engine (section
+// "SVDQuant moves hard values out of 4-bit"); here it is re-derived for CDNA4:
+//  - one workgroup owns 16 token rows; its 8 waves take the 64-wide groups of
+//    K round-robin, so every row is read from HBM exactly once with 128-byte
+//    contiguous row segments per group;
+//  - a lane holds 16 consecutive channels of one row (two dwordx4 loads);
+//    the four lanes of a row (lanes l, l^16, l^32, l^48) reduce the group
+//    absmax with two cross-lane max steps;
+//  - the same registers feed the down-projection on the bf16 MFMA
+//    (16x16x32), with X_hat split into bf16 hi + lo so the product keeps
+//    ~16 mantissa bits; L1 is stored transposed so B-operand loads are
+//    contiguous;
+//  - per-wave fp32 partials of X_hat L1 are reduced across the 8 waves in LDS
+//    in a fixed order (deterministic, no atomics).
+#include "common.h"
+
+namespace {
+
+constexpr int ROWS = 16;
+constexpr int WAVES = 8;
+
+// Quantise one lane's 16 values of a group: returns packed nibbles (8 bytes)
+// given the group's fp32 reciprocal `inv` (0 when the scale is 0).
+DEV uint32_t code_nibble(float v, float inv) {
+    float t = v * inv;                         // one fp32 multiply (no contraction)
+    t = __builtin_rintf(t);                    // round half to even
+    t = fminf(fmaxf(t, -7.0f), 7.0f);
+    uint32_t mag = (uint32_t)(int)fabsf(t);
+    uint32_t sgn = (__float_as_uint(t) >> 28) & 8u;   // sign bit -> bit 3
+    return (t != 0.0f) ? (mag | sgn) : 0u;
+}
+
+template <int RT>   // RT = rank / 16 (0..8)
+__global__ __launch_bounds__(ROWS * 32) void act_quant_kernel(
+    const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t ldx,
+    const float* __restrict__ inv_lambda, const uint16_t* __restrict__ l1t,
+    uint8_t* __restrict__ qx, uint16_t* __restrict__ sx, float* __restrict__ xl1)
+{
+    extern __shared__ float smem[];
+    const int G = (int)(K / 64);
+    float* s_inv = smem;                                   // [K]
+    uint16_t* s_sx = (uint16_t*)(smem + K);                // [ROWS][G]
+    float* s_xl1 = smem + K + ((ROWS * G + 1) / 2);        // [WAVES][ROWS][16*RT]
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int64_t m0 = (int64_t)blockIdx.x * ROWS;
+
+    for (int64_t k = tid; k < K; k += ROWS * 32)
+        s_inv[k] = inv_lambda ? inv_lambda[k] : 1.0f;
+    __syncthreads();
+
+    const int r = lane & 15, p = lane >> 4;
+    const int64_t row = m0 + r;
+    const bool valid = row < M;
+    const uint16_t* xrow = x + row * ldx;
+
+    v4f acc[RT > 0 ? RT : 1];
+#pragma unroll
+    for (int t = 0; t < (RT > 0 ? RT : 1); ++t) acc[t] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    for (int g = wave; g < G; g += WAVES) {
+        const int kb = g * 64 + 16 * p;
+        uint4 a0 = {0, 0, 0, 0}, a1 = {0, 0, 0, 0};
+        if (valid) {
+            a0 = *(const uint4*)(xrow + kb);
+            a1 = *(const uint4*)(xrow + kb + 8);
+        }
+        const uint32_t w[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+        float v[16];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            v[2 * j] = bf16_lo_to_f32(w[j]) * s_inv[kb + 2 * j];
+            v[2 * j + 1] = bf16_hi_to_f32(w[j]) * s_inv[kb + 2 * j + 1];
+        }
+        float amax = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) amax = fmaxf(amax, fabsf(v[j]));
+        amax = fmaxf(amax, __shfl_xor(amax, 16));
+        amax = fmaxf(amax, __shfl_xor(amax, 32));
+        const float s32 = fminf(amax / 7.0f, 65504.0f);
+        const _Float16 s16 = (_Float16)s32;
+        const float sf = (float)s16;
+        const float inv = (sf > 0.0f) ? 1.0f / sf : 0.0f;
+
+        uint32_t pk0 = 0, pk1 = 0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            pk0 |= code_nibble(v[j], inv) << (4 * j);
+            pk1 |= code_nibble(v[8 + j], inv) << (4 * j);
+        }
+        if (valid) {
+            *(uint2*)(qx + row * (K / 2) + g * 32 + 8 * p) = make_uint2(pk0, pk1);
+            if (p == 0) s_sx[r * G + g] = __builtin_bit_cast(uint16_t, s16);
+        }
+
+        if constexpr (RT > 0) {
+            // X_hat split into bf16 hi + lo; step 0 uses v[0..7], step 1 v[8..15].
+            v8bf ah0, al0, ah1, al1;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                __bf16 h0 = (__bf16)v[j];
+                __bf16 h1 = (__bf16)v[8 + j];
+                ah0[j] = h0;
+                ah1[j] = h1;
+                al0[j] = (__bf16)(v[j] - (float)h0);
+                al1[j] = (__bf16)(v[8 + j] - (float)h1);
+            }
+#pragma unroll
+            for (int t = 0; t < RT; ++t) {
+                const uint16_t* lrow = l1t + (int64_t)(16 * t + r) * K + kb;
+                const v8bf b0 = *(const v8bf*)(lrow);
+                const v8bf b1 = *(const v8bf*)(lrow + 8);
+                acc[t] = mfma_bf16_16x16x32(ah0, b0, acc[t]);
+                acc[t] = mfma_bf16_16x16x32(al0, b0, acc[t]);
+                acc[t] = mfma_bf16_16x16x32(ah1, b1, acc[t]);
+                acc[t] = mfma_bf16_16x16x32(al1, b1, acc[t]);
+            }
+        }
+    }
+
+    if constexpr (RT > 0) {
+        // C layout (16x16): lane holds column (lane & 15), rows 4 * (lane >> 4) + i.
+        const int RK = 16 * RT;
+#pragma unroll
+        for (int t = 0; t < RT; ++t)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                s_xl1[(wave * ROWS + 4 * p + i) * RK + 16 * t + r] = acc[t][i];
+    }
+    __syncthreads();
+
+    // scales: one contiguous row segment per token row
+    for (int e = tid; e < ROWS * G; e += ROWS * 32) {
+        const int rr = e / G, gg = e % G;
+        if (m0 + rr < M) sx[(m0 + rr) * G + gg] = s_sx[e];
+    }
+    if constexpr (RT > 0) {
+        const int RK = 16 * RT;
+        for (int e = tid; e < ROWS * RK; e += ROWS * 32) {
+            const int rr = e / RK;
+            if (m0 + rr >= M) continue;
+            float s = 0.0f;
+#pragma unroll
+            for (int w = 0; w < WAVES; ++w) s += s_xl1[w * ROWS * RK + e];
+            xl1[(m0 + rr) * RK + (e % RK)] = s;
+        }
+    }
+}
+
+}  // namespace
+
+size_t act_quant_smem_bytes(int64_t K, int rank) {
+    const int64_t G = K / 64;
+    return sizeof(float) * (K + (ROWS * G + 1) / 2 + (size_t)WAVES * ROWS * rank);
+}
+
+hipError_t launch_act_quant(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
+                            const float* inv_lambda, const uint16_t* l1t, int rank,
+                            uint8_t* qx, uint16_t* sx, float* xl1, hipStream_t stream)
+{
+    const dim3 grid((unsigned)((M + ROWS - 1) / ROWS)), block(ROWS * 32);
+    const size_t smem = act_quant_smem_bytes(K, rank);
+    switch (rank / 16) {
+#define CASE(RTV) case RTV: \
+        if (smem > 65536) \
+            (void)hipFuncSetAttribute((const void*)act_quant_kernel<RTV>, \
+                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem); \
+        hipLaunchKernelGGL(act_quant_kernel<RTV>, grid, block, smem, stream, \
+                           x, M, K, ldx, inv_lambda, l1t, qx, sx, xl1); break;
+        CASE(0) CASE(1) CASE(2) CASE(3) CASE(4) CASE(5) CASE(6) CASE(7) CASE(8)
+#undef CASE
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}

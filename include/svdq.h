@@ -1,0 +1,159 @@
+/*
+ * svdq.h -- C ABI of the MI355X (gfx950) SVDQuant W4A4 linear layer and the
+ * AWQ W4A16 GEMV.
+ *
+ * The method (remio.ai page "Nunchaku Diffusers support cuts VRAM but hardware
+ * still sets the rules", section "SVDQuant moves hard values out of 4-bit";
+ * donmalab.com page, core-challenge section): activation outliers are moved
+ * into the weights by per-input-channel smoothing, a small 16-bit low-rank
+ * branch carries the hardest part of the smoothed weight, the residual runs
+ * with 4-bit weights and 4-bit activations, and the two results are added:
+ *
+ *     X_hat = X diag(inv_lambda)
+ *     Y     = X_hat L1 L2  +  sum_g sx[m,g] sw[n,g] P_g[m,n]  +  bias      (-> GELU)
+ *     P_g   = sum_{k in group g} qx[m,k] qw[n,k]          (exact integers)
+ *
+ * Attention and MLP projections take this W4A4 path; adaLN / modulation
+ * projections take AWQ W4A16 (4-bit weights, 16-bit activations) -- same
+ * pages, sections on the two layer types.
+ *
+ * Common conventions
+ *  - Every pointer is a DEVICE pointer owned by the caller; the library never
+ *    allocates, frees or keeps per-call state.
+ *  - `stream` is a hipStream_t (NULL = the null stream). Calls enqueue work
+ *    and return at once; they never synchronise. Stream order carries the
+ *    act -> GEMM dependency.
+ *  - Arguments are validated on the host before any HIP call. A failed check
+ *    returns its status and launches nothing; svdq_last_error() gives the
+ *    detail. There is no fallback path of any kind.
+ *  - M == 0 is valid: after the shape checks the call returns SVDQ_OK
+ *    without reading any pointer or touching the device.
+ *  - Group size is 64 along K; K must be a multiple of 64.
+ *  - 4-bit codes (format v1): rows are K-contiguous, byte i of a row holds
+ *    element 2i in bits 0-3 and element 2i+1 in bits 4-7. SVDQ codes are
+ *    sign-magnitude nibbles (bit 3 sign, bits 0-2 magnitude) in [-7, 7];
+ *    AWQ codes are unsigned nibbles 0..15.
+ *  - bf16 and fp16 values are passed as their 16-bit patterns.
+ */
+#ifndef SVDQ_H
+#define SVDQ_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    SVDQ_OK = 0,
+    SVDQ_ERR_NULL = 1,        /* a required pointer is NULL                     */
+    SVDQ_ERR_SHAPE = 2,       /* size / leading dimension / rank not allowed    */
+    SVDQ_ERR_ALIGN = 3,       /* pointer or leading dimension misaligned        */
+    SVDQ_ERR_UNSUPPORTED = 4, /* dtype / activation / option not supported      */
+    SVDQ_ERR_DEVICE = 5,      /* no device, or the device is not gfx950         */
+    SVDQ_ERR_HIP = 6          /* a HIP runtime call or a launch failed          */
+} svdq_status;
+
+typedef enum { SVDQ_DT_BF16 = 0, SVDQ_DT_F32 = 1 } svdq_dtype;
+typedef enum { SVDQ_ACT_NONE = 0, SVDQ_ACT_GELU_TANH = 1 } svdq_act;
+
+/* Capability check done up front (the remio.ai page, hardware section: the
+ * loader verifies GPU capability at start-up and unsupported combinations
+ * raise an error instead of running incompatible kernels). Returns SVDQ_OK
+ * when `device` exists and is gfx950, else SVDQ_ERR_DEVICE. */
+svdq_status svdq_check_device(int device);
+
+/* Static text for a status code; never NULL. */
+const char* svdq_status_string(svdq_status s);
+
+/* Detail of the last failure on the calling thread ("" if none). */
+const char* svdq_last_error(void);
+
+/* Library version: format version * 100 + revision. */
+int svdq_version(void);
+
+/*
+ * svdq_quantize_act -- fused smoothing + rank-r down-projection + INT4
+ * group-64 activation quantisation (the remio.ai page, same section: the
+ * original engine fused the low-rank down-projection with input quantisation).
+ *
+ *  x          bf16 [M][ldx], row m's K values contiguous (ldx >= K, ldx % 8 == 0)
+ *  inv_lambda fp32 [K] smoothing reciprocals, or NULL for lambda == 1
+ *  l1t        bf16 [rank][K]: row j is column j of L1 (the down-projection);
+ *             NULL iff rank == 0
+ *  rank       0..128, multiple of 16
+ *  qx         out: packed codes [M][K/2]
+ *  sx_f16     out: fp16 scales [M][K/64]
+ *  xl1        out: fp32 [M][rank] = X_hat L1 (NULL iff rank == 0)
+ *
+ * Per element: x_hat = fp32(x) * inv_lambda[k] (one fp32 multiply). Per
+ * (row, group): amax = max |x_hat|; s = fp16_rtne(min(amax / 7, 65504));
+ * if s == 0 all codes are 0, else q = clamp(rtne(x_hat * fp32(1 / s)), -7, 7).
+ * qx and sx are bit-exact with that definition. xl1 is accumulated in fp32
+ * (relative error about 1e-6).
+ * Alignment: x, l1t, qx, xl1 16-byte aligned; sx_f16 4-byte aligned.
+ */
+svdq_status svdq_quantize_act(const void* x, int64_t M, int64_t K, int64_t ldx,
+                              const float* inv_lambda, const void* l1t, int32_t rank,
+                              uint8_t* qx, void* sx_f16, float* xl1, void* stream);
+
+/*
+ * svdq_gemm_w4a4 -- 4-bit x 4-bit group GEMM with the low-rank up-projection,
+ * bias and optional GELU(tanh) in the epilogue (the remio.ai page, same
+ * section: the up-projection was fused with the 4-bit matmul).
+ *
+ *  qx, sx_f16  [M][K/2] codes and fp16 [M][K/64] scales from svdq_quantize_act
+ *  qw, sw_f16  [N][K/2] weight codes and fp16 [N][K/64] scales (residual R^T)
+ *  xl1         fp32 [M][rank] from svdq_quantize_act (NULL iff rank == 0)
+ *  l2t         bf16 [N][rank]: row n is column n of L2 (NULL iff rank == 0)
+ *  bias        bf16 [N] or NULL
+ *  act         SVDQ_ACT_NONE or SVDQ_ACT_GELU_TANH (applied in fp32)
+ *  y           out: [M][ldy] of y_dtype (bf16 RTNE of the fp32 result, or fp32)
+ *
+ * N % 8 == 0, ldy >= N, ldy % 8 == 0. The group partials P_g are exact; the
+ * fp32 result matches the fp64 definition to about 1e-6 relative.
+ * Alignment: every pointer 16-byte aligned except sx_f16 / sw_f16 (4 bytes).
+ */
+svdq_status svdq_gemm_w4a4(const uint8_t* qx, const void* sx_f16, int64_t M, int64_t K,
+                           const uint8_t* qw, const void* sw_f16, int64_t N,
+                           const float* xl1, const void* l2t, int32_t rank,
+                           const void* bias, int32_t act,
+                           void* y, int32_t y_dtype, int64_t ldy, void* stream);
+
+/*
+ * svdq_gemm_w4a4_partials -- test hook: the same device code path as
+ * svdq_gemm_w4a4 (same staging, same MFMA) with the scale epilogue replaced
+ * by a dump of the exact integer group partials P_g[m, n] for the rectangle
+ * rows [m0, m0 + mcount) x columns [n0, n0 + ncount).
+ *  p   out: int32 [mcount][ncount][K/64]
+ */
+svdq_status svdq_gemm_w4a4_partials(const uint8_t* qx, int64_t M, int64_t K,
+                                    const uint8_t* qw, int64_t N,
+                                    int64_t m0, int64_t mcount, int64_t n0, int64_t ncount,
+                                    int32_t* p, void* stream);
+
+/*
+ * awq_gemv_w4a16 -- AWQ W4A16 GEMV for the adaLN / modulation projections
+ * (donmalab.com page, section on the two schemes; remio.ai page, loading-path
+ * section): Y = (X diag(inv_s)) dequant(W) + bias with
+ * dequant(W)[k, n] = (q[n, k] - z[n, g]) * s[n, g] computed in registers.
+ *
+ *  x          bf16 [M][K] (1 <= M <= 16, dense rows)
+ *  inv_s      fp32 [K] reciprocal activation-aware channel scales, or NULL
+ *  qw         [N][K/2] unsigned 4-bit codes
+ *  scale_f16  fp16 [N][K/64];  zero_f16 fp16 [N][K/64] (integers 0..15)
+ *  bias       bf16 [N] or NULL
+ *  y          out: bf16 [M][N]
+ * N % 16 == 0. Accumulation is fp32; the result matches the fp64 definition
+ * to about 1e-5 relative before the bf16 rounding.
+ * Alignment: x, qw, y 16-byte aligned; scale/zero 4 bytes.
+ */
+svdq_status awq_gemv_w4a16(const void* x, int64_t M, int64_t K, const float* inv_s,
+                           const uint8_t* qw, const void* scale_f16, const void* zero_f16,
+                           int64_t N, const void* bias, void* y, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SVDQ_H */

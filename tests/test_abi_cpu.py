@@ -1,0 +1,131 @@
+"""Host-side checks of the C ABI that need no GPU: the library loads, exports
+every entry point include/svdq.h declares, and rejects malformed arguments
+with the documented status before touching the device (the remio.ai page,
+hardware section: unsupported combinations must raise clear errors rather
+than run incompatible kernels)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import bit_quantized_diffusion_svdq_amd as svdq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+OK, NULL, SHAPE, ALIGN, UNSUP, DEVICE = 0, 1, 2, 3, 4, 5
+
+# fake but well-aligned device addresses: validation must reject bad calls
+# before any of them is dereferenced or passed to HIP
+A = 0x7F0000000000
+B = 0x7F0000100000
+C = 0x7F0000200000
+D = 0x7F0000300000
+E = 0x7F0000400000
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return svdq.load_library()
+
+
+def _declared_functions():
+    src = open(os.path.join(ROOT, "include", "svdq.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\**(\w+)\s*\(", src, flags=re.M)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _declared_functions()
+    assert {"svdq_quantize_act", "svdq_gemm_w4a4", "awq_gemv_w4a16", "svdq_gemm_w4a4_partials",
+            "svdq_check_device", "svdq_status_string", "svdq_last_error", "svdq_version"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    for s in range(7):
+        assert lib.svdq_status_string(s)
+    assert lib.svdq_status_string(99) == b"unknown status"
+    assert lib.svdq_version() == 100
+
+
+def _act(lib, **kw):
+    a = dict(x=A, M=128, K=256, ldx=256, inv=None, l1t=B, rank=16, qx=C, sx=D, xl1=E)
+    a.update(kw)
+    return lib.svdq_quantize_act(a["x"], a["M"], a["K"], a["ldx"], a["inv"], a["l1t"], a["rank"],
+                                 a["qx"], a["sx"], a["xl1"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(K=100), SHAPE), (dict(K=0), SHAPE), (dict(M=-1), SHAPE), (dict(rank=8), SHAPE),
+    (dict(rank=144), SHAPE), (dict(ldx=128), SHAPE), (dict(ldx=260), ALIGN),
+    (dict(x=None), NULL), (dict(qx=None), NULL), (dict(sx=None), NULL),
+    (dict(l1t=None), NULL), (dict(xl1=None), NULL), (dict(x=A + 2), ALIGN), (dict(qx=C + 8), ALIGN),
+    (dict(K=1 << 20), SHAPE),
+])
+def test_quantize_act_rejects(lib, kw, status):
+    assert _act(lib, **kw) == status
+    assert lib.svdq_last_error()
+
+
+def _gemm(lib, **kw):
+    a = dict(qx=A, sx=B, M=64, K=256, qw=C, sw=D, N=128, xl1=E, l2t=E + 4096, rank=16,
+             bias=None, act=0, y=E + 65536, ydt=0, ldy=128)
+    a.update(kw)
+    return lib.svdq_gemm_w4a4(a["qx"], a["sx"], a["M"], a["K"], a["qw"], a["sw"], a["N"], a["xl1"],
+                              a["l2t"], a["rank"], a["bias"], a["act"], a["y"], a["ydt"], a["ldy"],
+                              None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(N=100), SHAPE), (dict(N=0), SHAPE), (dict(K=96), SHAPE), (dict(ldy=64), SHAPE),
+    (dict(ldy=132), ALIGN), (dict(act=2), UNSUP), (dict(ydt=3), UNSUP), (dict(qw=None), NULL),
+    (dict(y=None), NULL), (dict(xl1=None), NULL), (dict(rank=20), SHAPE), (dict(qw=C + 4), ALIGN),
+    (dict(y=E + 65536 + 8), ALIGN),
+])
+def test_gemm_rejects(lib, kw, status):
+    assert _gemm(lib, **kw) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(m0=-1), SHAPE), (dict(mcount=100), SHAPE), (dict(n0=64, ncount=100), SHAPE),
+    (dict(p=None), NULL), (dict(K=65), SHAPE),
+])
+def test_partials_rejects(lib, kw, status):
+    a = dict(qx=A, M=64, K=256, qw=C, N=128, m0=0, mcount=64, n0=0, ncount=128, p=E)
+    a.update(kw)
+    assert lib.svdq_gemm_w4a4_partials(a["qx"], a["M"], a["K"], a["qw"], a["N"], a["m0"],
+                                       a["mcount"], a["n0"], a["ncount"], a["p"], None) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(M=0), SHAPE), (dict(M=17), SHAPE), (dict(N=40), SHAPE), (dict(K=48), SHAPE),
+    (dict(zero=None), NULL), (dict(x=A + 4), ALIGN),
+])
+def test_gemv_rejects(lib, kw, status):
+    a = dict(x=A, M=4, K=256, inv=None, qw=B, scale=C, zero=D, N=64, bias=None, y=E)
+    a.update(kw)
+    assert lib.awq_gemv_w4a16(a["x"], a["M"], a["K"], a["inv"], a["qw"], a["scale"], a["zero"],
+                              a["N"], a["bias"], a["y"], None) == status
+
+
+def test_valid_arguments_without_gpu_report_device_error(lib):
+    """Well-formed calls on a machine without a gfx950 GPU stop at the
+    capability check (never a silent fallback)."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert _act(lib) == DEVICE
+    assert b"device" in lib.svdq_last_error().lower()
+    assert _gemm(lib) == DEVICE
+    assert lib.svdq_check_device(0) == DEVICE
+    with pytest.raises(svdq.SvdqError):
+        svdq.check_device(0)
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    import bit_quantized_diffusion_svdq_amd._lib as L
+    monkeypatch.setattr(L, "_LIB", None)
+    monkeypatch.setattr(L, "library_path", lambda: str(tmp_path / "libsvdq.so"))
+    with pytest.raises(RuntimeError, match="no fallback"):
+        L.load_library()

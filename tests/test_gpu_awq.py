@@ -1,0 +1,58 @@
+"""GPU parity of the AWQ W4A16 GEMV against the CPU oracle, through the C ABI."""
+import functools
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import awq as oawq, numfmt
+from gpu_util import dev, dev_f16, dev_u16, host_bf16_f64, note, rel_fro
+
+pytestmark = pytest.mark.gpu
+
+import bit_quantized_diffusion_svdq_amd as lib
+
+
+def run(x_bits, w):
+    return lib.awq_gemv(dev_u16(x_bits), dev(w.inv_s), dev(w.qw), dev_f16(w.scale), dev_f16(w.zero),
+                        dev_u16(w.bias) if w.bias is not None else None)
+
+
+def check(y, x_bits, w):
+    y64 = oawq.gemv(x_bits, w)
+    yg = host_bf16_f64(y)
+    assert rel_fro(yg, numfmt.bf16_bits_to_f32(oawq.output_bf16(y64))) <= 1e-4
+    assert rel_fro(yg, y64) <= 2e-3
+
+
+@functools.lru_cache(maxsize=None)
+def full_layer():
+    cfg = synth.CONFIGS["awq"]
+    li = synth.make_layer(cfg)
+    return li, oawq.prepare_awq(li.w, li.chan_scale, li.bias)
+
+
+def test_awq_full_size():
+    note("awq gemv full size 4 x 3072 -> 18432")
+    li, w = full_layer()
+    y = run(li.x, w)
+    y2 = run(li.x, w)
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
+    check(y, li.x, w)
+
+
+@pytest.mark.parametrize("M,K,N,scaled,bias", [(1, 64, 16, False, False), (16, 192, 48, True, True),
+                                               (7, 2048 + 192, 32, True, False), (3, 4096, 64, True, True)])
+def test_awq_shapes(M, K, N, scaled, bias):
+    note(f"awq gemv M={M} K={K} N={N}")
+    rng = np.random.default_rng(M * 1000 + K)
+    wb = synth.make_matrix_bf16(K, N, seed=K + N, std=0.02)
+    sc = rng.uniform(0.5, 2.0, K).astype(np.float32) if scaled else None
+    b = synth.make_matrix_bf16(1, N, seed=1, std=0.02)[0] if bias else None
+    w = oawq.prepare_awq(wb, sc, b)
+    x = synth.make_matrix_bf16(M, K, seed=M + 7)
+    y = run(x, w)
+    torch.cuda.synchronize()
+    check(y, x, w)

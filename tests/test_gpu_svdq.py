@@ -1,0 +1,213 @@
+"""GPU parity of the SVDQ W4A4 path against the CPU oracle, through the C ABI.
+
+Bars: packed activation codes and fp16 scales bit-exact; per-group integer
+partials bit-exact; xl1 relative Frobenius error <= 1e-4; fp32 output within
+1e-5 of the fp64 definition; bf16 output within 1e-4 of the fp64 result
+rounded to bf16 and within the 2e-3 gate of the unrounded fp64 result.
+"""
+import functools
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import numfmt, svdq as osv
+from gpu_util import (DevSvdq, dev, dev_f16, dev_u16, host_bf16_f64, host_u16, note,
+                            rel_fro)
+
+pytestmark = pytest.mark.gpu
+
+import bit_quantized_diffusion_svdq_amd as lib
+
+
+@functools.lru_cache(maxsize=None)
+def layer(name, M=None):
+    cfg = synth.CONFIGS[name]
+    li = synth.make_layer(cfg, M=M)
+    w = osv.prepare_svdq(li.x, li.w, li.bias, cfg.rank)
+    return cfg, li, w
+
+
+def run_act(x_bits, dw, rank):
+    x = dev_u16(x_bits)
+    return lib.quantize_act(x, dw.inv_lambda, dw.l1t, rank)
+
+
+def check_act(qa, qx, sx, xl1, rank):
+    assert np.array_equal(qx.cpu().numpy(), qa.qx), "packed codes differ"
+    assert np.array_equal(sx.cpu().numpy().view(np.uint16), qa.sx.view(np.uint16)), "scales differ"
+    if rank:
+        e = rel_fro(xl1.cpu().numpy(), qa.xl1)
+        assert e <= 1e-4, e
+
+
+@pytest.mark.parametrize("name,M", [("tiny", None), ("qkv", None), ("tiny", 77), ("mlp_fc1", 4608)])
+def test_act_quant_parity(name, M):
+    note(f"act_quant {name} M={M}")
+    cfg, li, w = layer(name, M)
+    dw = DevSvdq(w)
+    qx, sx, xl1 = run_act(li.x, dw, cfg.rank)
+    torch.cuda.synchronize()
+    qa = osv.quantize_act(li.x, w.inv_lambda, w.l1)
+    check_act(qa, qx, sx, xl1, cfg.rank)
+
+
+@pytest.mark.parametrize("rank,use_inv", [(0, False), (0, True), (32, False), (128, True)])
+def test_act_quant_ranks_and_no_smoothing(rank, use_inv):
+    note(f"act_quant rank={rank} inv={use_inv}")
+    M, K = 45, 320
+    x = synth.make_matrix_bf16(M, K, seed=5, std=2.0)
+    rng = np.random.default_rng(6)
+    inv = rng.uniform(0.2, 3.0, K).astype(np.float32) if use_inv else None
+    l1 = numfmt.f32_to_bf16_bits((rng.standard_normal((K, rank)) * 0.1).astype(np.float32))
+    xd = dev_u16(x)
+    qx, sx, xl1 = lib.quantize_act(xd, dev(inv) if use_inv else None,
+                                   dev_u16(np.ascontiguousarray(l1.T)) if rank else None, rank)
+    torch.cuda.synchronize()
+    qa = osv.quantize_act(x, inv, l1 if rank else None)
+    check_act(qa, qx, sx, xl1, rank)
+
+
+def test_act_quant_edge_values():
+    """Zero rows, tiny (fp16-subnormal scale) groups, huge groups (saturated
+    scale) and exact ties, against the oracle bit for bit."""
+    note("act_quant edge values")
+    M, K = 20, 256
+    rng = np.random.default_rng(8)
+    xf = rng.standard_normal((M, K)).astype(np.float32)
+    xf[0] = 0.0
+    xf[1, :64] = 0.0
+    xf[2] *= 1e-6
+    xf[3, 64:128] *= 1e-9
+    xf[4] *= 3e5
+    xf[5] = np.round(xf[5] * 4) / 4          # many exact halves after scaling
+    xf[6, :64] = np.arange(64) - 32.0
+    xbits = numfmt.f32_to_bf16_bits(xf)
+    qx, sx, _ = lib.quantize_act(dev_u16(xbits), None, None, 0)
+    torch.cuda.synchronize()
+    qa = osv.quantize_act(xbits, None, None)
+    check_act(qa, qx, sx, None, 0)
+
+
+def test_act_quant_empty():
+    note("act_quant M=0")
+    x = torch.empty((0, 128), dtype=torch.bfloat16, device="cuda")
+    qx, sx, _ = lib.quantize_act(x, None, None, 0)
+    torch.cuda.synchronize()
+    assert qx.shape == (0, 64)
+
+
+def partials_gpu(qx_d, qw_d, M, K, N, m0, mc, n0, nc):
+    p = torch.full((mc, nc, K // 64), -12345, dtype=torch.int32, device="cuda")
+    lib.svdq_gemm_w4a4_partials(qx_d, M, K, qw_d, N, m0, mc, n0, nc, p)
+    torch.cuda.synchronize()
+    return p.cpu().numpy()
+
+
+def test_partials_tiny_all():
+    note("partials tiny")
+    cfg, li, w = layer("tiny")
+    qa = osv.quantize_act(li.x, w.inv_lambda, w.l1)
+    M, K, N = cfg.M, cfg.K, cfg.N
+    p = partials_gpu(dev(qa.qx), dev(w.qw), M, K, N, 0, M, 0, N)
+    assert np.array_equal(p, osv.group_partials(qa.codes, w.qw_codes))
+
+
+@pytest.mark.parametrize("rect", [(0, 64, 0, 96), (4000, 96, 9100, 116), (1234, 77, 4321, 200),
+                                  (2048, 128, 0, 9216)])
+def test_partials_qkv_sampled(rect):
+    m0, mc, n0, nc = rect
+    note(f"partials qkv rect={rect}")
+    cfg, li, w = layer("qkv")
+    qa = osv.quantize_act(li.x, w.inv_lambda, w.l1)
+    p = partials_gpu(dev(qa.qx), dev(w.qw), cfg.M, cfg.K, cfg.N, m0, mc, n0, nc)
+    ref = osv.group_partials(qa.codes[m0:m0 + mc], w.qw_codes[n0:n0 + nc])
+    assert np.array_equal(p, ref)
+
+
+def gemm_gpu(qa, dw, rank, act="none", out=torch.bfloat16, bias=True):
+    return lib.w4a4_linear(dev(qa.qx), dev_f16(qa.sx), dev(qa.xl1) if rank else None, dw.qw, dw.sw,
+                           dw.l2t, dw.bias if bias else None, rank, act=act, out_dtype=out)
+
+
+@pytest.mark.parametrize("act,out,bias", [("none", torch.float32, True), ("none", torch.bfloat16, True),
+                                          ("gelu_tanh", torch.float32, True),
+                                          ("gelu_tanh", torch.bfloat16, False)])
+def test_gemm_tiny(act, out, bias):
+    note(f"gemm tiny act={act} out={out} bias={bias}")
+    cfg, li, w = layer("tiny")
+    dw = DevSvdq(w)
+    qa = osv.quantize_act(li.x, w.inv_lambda, w.l1)
+    y = gemm_gpu(qa, dw, cfg.rank, act, out, bias)
+    torch.cuda.synchronize()
+    y64 = osv.linear_output(qa.codes, qa.sx, w.qw_codes, w.sw, qa.xl1, w.l2,
+                            w.bias if bias else None, act)
+    yg = y.cpu().numpy().astype(np.float64) if out == torch.float32 else host_bf16_f64(y)
+    if out == torch.float32:
+        assert rel_fro(yg, y64) <= 1e-5
+    else:
+        assert rel_fro(yg, numfmt.bf16_bits_to_f32(osv.output_bf16(y64))) <= 1e-4
+        assert rel_fro(yg, y64) <= 2e-3
+
+
+def test_gemm_ragged_rank0_and_rank128():
+    """Ragged M and N against the 128 x 128 tile, rank 0 (plain W4A4) and
+    the maximum rank."""
+    for (M, K, N, r) in [(77, 192, 200, 0), (130, 320, 136, 128), (1, 64, 16, 16)]:
+        note(f"gemm ragged M={M} K={K} N={N} r={r}")
+        x = synth.make_matrix_bf16(M, K, seed=M, std=1.0)
+        wb = synth.make_matrix_bf16(K, N, seed=N, std=0.05)
+        b = synth.make_matrix_bf16(1, N, seed=3, std=0.02)[0]
+        w = osv.prepare_svdq(x, wb, b, r)
+        dw = DevSvdq(w)
+        qx, sx, xl1 = lib.quantize_act(dev_u16(x), dw.inv_lambda, dw.l1t, r)
+        y = lib.w4a4_linear(qx, sx, xl1, dw.qw, dw.sw, dw.l2t, dw.bias, r, out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        qa, y64 = osv.forward(w, x)
+        check_act(qa, qx, sx, xl1, r)
+        assert rel_fro(y.cpu().numpy(), y64) <= 1e-5, (M, K, N, r)
+
+
+def test_gemm_empty_and_strided_output():
+    note("gemm M=0 and ldy > N")
+    cfg, li, w = layer("tiny")
+    dw = DevSvdq(w)
+    qa = osv.quantize_act(li.x, w.inv_lambda, w.l1)
+    y0 = torch.empty((0, cfg.N), dtype=torch.bfloat16, device="cuda")
+    lib.svdq_gemm_w4a4(dev(qa.qx), dev_f16(qa.sx), 0, cfg.K, dw.qw, dw.sw, cfg.N, None, None, 0,
+                       None, 0, y0, 0, cfg.N)
+    big = torch.full((cfg.M, cfg.N + 64), 7.0, dtype=torch.float32, device="cuda")
+    lib.svdq_gemm_w4a4(dev(qa.qx), dev_f16(qa.sx), cfg.M, cfg.K, dw.qw, dw.sw, cfg.N, dev(qa.xl1),
+                       dw.l2t, cfg.rank, dw.bias, 0, big, 1, cfg.N + 64)
+    torch.cuda.synchronize()
+    yb = big.cpu().numpy()
+    assert np.all(yb[:, cfg.N:] == 7.0)                     # padding untouched
+    y64 = osv.linear_output(qa.codes, qa.sx, w.qw_codes, w.sw, qa.xl1, w.l2, w.bias)
+    assert rel_fro(yb[:, :cfg.N], y64) <= 1e-5
+
+
+def test_qkv_linear_full_size():
+    """The QKV workload end to end on the GPU (act + GEMM, the launch the
+    benchmark times); every code and scale compared, outputs compared on
+    sampled rows (the oracle computes them one row block at a time)."""
+    note("qkv linear full size")
+    cfg, li, w = layer("qkv")
+    dw = DevSvdq(w)
+    qx, sx, xl1 = run_act(li.x, dw, cfg.rank)
+    y = lib.w4a4_linear(qx, sx, xl1, dw.qw, dw.sw, dw.l2t, dw.bias, cfg.rank)
+    y2 = lib.w4a4_linear(qx, sx, xl1, dw.qw, dw.sw, dw.l2t, dw.bias, cfg.rank)
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16), y2.view(torch.int16)), "not deterministic"
+    qa = osv.quantize_act(li.x, w.inv_lambda, w.l1)
+    check_act(qa, qx, sx, xl1, cfg.rank)
+    rows = np.unique(np.concatenate([np.arange(0, 8), np.arange(cfg.M - 8, cfg.M),
+                                     np.random.default_rng(0).choice(cfg.M, 48, replace=False)]))
+    y64 = osv.linear_output(qa.codes[rows], qa.sx[rows], w.qw_codes, w.sw, qa.xl1[rows], w.l2, w.bias)
+    yg = host_bf16_f64(y)[rows]
+    assert rel_fro(yg, numfmt.bf16_bits_to_f32(osv.output_bf16(y64))) <= 1e-4
+    assert rel_fro(yg, y64) <= 2e-3
+    # the GPU's own fp32 low-rank input differs from the oracle's by ~1e-6
+    yf = lib.w4a4_linear(qx, sx, xl1, dw.qw, dw.sw, dw.l2t, dw.bias, cfg.rank, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert rel_fro(yf.cpu().numpy()[rows], y64) <= 1e-5
