@@ -55,3 +55,62 @@ class DevSvdq:
         self.qw = dev(w.qw)
         self.sw = dev_f16(w.sw)
         self.bias = dev_u16(w.bias) if w.bias is not None else None
+
+
+def bf16_ulp(y64: np.ndarray) -> np.ndarray:
+    """Spacing of bf16 numbers at |y| (8 significant bits; subnormal floor)."""
+    a = np.abs(np.asarray(y64, np.float64))
+    _, e = np.frexp(np.where(a > 0, a, 1.0))
+    return np.ldexp(1.0, np.maximum(e - 8, -133))
+
+
+def assert_bf16_output(yg: np.ndarray, y64: np.ndarray, delta_rel: float):
+    """Element-wise bar for a bf16 output against the fp64 definition: the GPU
+    rounds its fp32 result once, so |yg - y64| <= ulp/2 of y64 plus the fp32
+    accumulation error, bounded by delta_rel * rms(y64)."""
+    yg = np.asarray(yg, np.float64)
+    y64 = np.asarray(y64, np.float64)
+    rms = float(np.sqrt(np.mean(y64 * y64)))
+    bound = 0.5 * bf16_ulp(y64) * (1 + 2.0 ** -7) + delta_rel * rms
+    bad = np.abs(yg - y64) > bound
+    assert not bad.any(), (f"{bad.sum()} of {bad.size} elements outside ulp/2 + {delta_rel:g} rms; "
+                           f"worst excess {np.max(np.abs(yg - y64) - bound):.3g}")
+    assert rel_fro(yg, y64) <= 2e-3
+
+
+def magnitude_sum(qx_codes, sx, qw_codes, sw, xl1, l2_bits, bias_bits):
+    """T[m, n] = sum_g |sx sw P_g| + sum_j |xl1_j L2_jn| + |bias_n|: the scale of
+    every term the fp32 accumulation adds, for the rounding-error bound."""
+    from oracle import numfmt
+    a = np.asarray(qx_codes, np.float64)
+    b = np.asarray(qw_codes, np.float64)
+    G = a.shape[1] // 64
+    sxf = np.asarray(sx, np.float16).astype(np.float64)
+    swf = np.asarray(sw, np.float16).astype(np.float64)
+    t = np.zeros((a.shape[0], b.shape[0]))
+    for g in range(G):
+        p = a[:, 64 * g:64 * g + 64] @ b[:, 64 * g:64 * g + 64].T
+        t += np.abs(sxf[:, g][:, None] * swf[:, g][None, :] * p)
+    if xl1 is not None and np.asarray(xl1).shape[1]:
+        t += np.abs(np.asarray(xl1, np.float64)) @ np.abs(numfmt.bf16_bits_to_f32(l2_bits).astype(np.float64))
+    if bias_bits is not None:
+        t += np.abs(numfmt.bf16_bits_to_f32(bias_bits).astype(np.float64))[None, :]
+    return t
+
+
+def assert_fp32_output(y32, y64, tmag, n_terms: int):
+    """fp32 accumulation of n_terms terms: |y32 - y64| <= 2 (n_terms + 4) 2^-24 T
+    element-wise (T from magnitude_sum), and relative Frobenius <= 1e-5."""
+    y32 = np.asarray(y32, np.float64)
+    bound = 2.0 * (n_terms + 4) * 2.0 ** -24 * tmag + 1e-30
+    bad = np.abs(y32 - y64) > bound
+    assert not bad.any(), (f"{bad.sum()} of {bad.size} fp32 outputs outside the accumulation bound; "
+                           f"worst ratio {np.max(np.abs(y32 - y64) / bound):.3g}")
+    assert rel_fro(y32, y64) <= 1e-5
+
+
+def assert_bf16_is_rounded_fp32(ybf_bits: np.ndarray, y32: np.ndarray):
+    """The bf16 output is the RTNE rounding of the same kernel's fp32 result."""
+    from oracle import numfmt
+    exp = numfmt.f32_to_bf16_bits(np.asarray(y32, np.float32))
+    assert np.array_equal(np.asarray(ybf_bits, np.uint16), exp)
