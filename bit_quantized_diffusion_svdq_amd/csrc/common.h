@@ -29,9 +29,12 @@ DEV uint32_t pack_bf16x2(float lo, float hi) {
 
 DEV float f16_bits_to_f32(uint16_t h) { return (float)__builtin_bit_cast(_Float16, h); }
 
-// D = A(32x64 fp8) * B(64x32 fp8) + C, fp32 accumulate, unit block scales.
+// D = A(32x64 fp8) * B(64x32 fp8) + C, fp32 accumulate. Both operands carry
+// INT4 codes as E4M3 subnormals (value q * 2^-9, see int4sm_to_fp8); the
+// E8M0 block scale 2^9 (0x88) on each side turns the products back into
+// exact integer products, so the result is the exact integer dot product.
 DEV v16f mfma_f8_32x32x64(const v8i& a, const v8i& b, const v16f& c) {
-    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0x7F7F7F7F, 0, 0x7F7F7F7F);
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0x88888888, 0, 0x88888888);
 }
 
 // D = A(16x32 bf16) * B(32x16 bf16) + C
@@ -50,19 +53,15 @@ DEV v16f mfma_f16_32x32x16(const v8h& a, const v8h& b, const v16f& c) {
 }
 
 // Eight sign-magnitude INT4 codes (one dword, element 2i in the low nibble of
-// byte i) -> eight FP8 E4M3 bytes holding the same integers exactly.
+// byte i) -> eight FP8 E4M3 bytes. A code s|m (sign bit, magnitude 0..7)
+// becomes the E4M3 subnormal s|0000|m, whose value is (-1)^s * m * 2^-9, so
+// the byte is just the magnitude bits with the sign moved to bit 7.
 // lo: bytes = elements 0,2,4,6; hi: bytes = elements 1,3,5,7. Operands A and
 // B are expanded the same way, so the K order inside an MFMA is permuted
 // identically on both sides and every dot product is unchanged.
-// Magnitudes 0..7 map through a byte table {0, 1.0, 2.0, 3.0, 4.0, 5.0, 6.0,
-// 7.0} (E4M3 0x00 38 40 44 48 4A 4C 4E) with v_perm; the sign bit moves to
-// bit 7.
 DEV void int4sm_to_fp8(uint32_t x, uint32_t& lo, uint32_t& hi) {
-    const uint32_t t_lo = 0x44403800u, t_hi = 0x4E4C4A48u;
-    uint32_t mlo = __builtin_amdgcn_perm(t_hi, t_lo, x & 0x07070707u);
-    uint32_t mhi = __builtin_amdgcn_perm(t_hi, t_lo, (x >> 4) & 0x07070707u);
-    lo = mlo | ((x << 4) & 0x80808080u);
-    hi = mhi | (x & 0x80808080u);
+    lo = (x & 0x07070707u) | ((x << 4) & 0x80808080u);
+    hi = ((x >> 4) & 0x07070707u) | (x & 0x80808080u);
 }
 
 DEV float gelu_tanh_f32(float y) {

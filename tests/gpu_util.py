@@ -79,8 +79,10 @@ def assert_bf16_output(yg: np.ndarray, y64: np.ndarray, delta_rel: float):
 
 
 def magnitude_sum(qx_codes, sx, qw_codes, sw, xl1, l2_bits, bias_bits):
-    """T[m, n] = sum_g |sx sw P_g| + sum_j |xl1_j L2_jn| + |bias_n|: the scale of
-    every term the fp32 accumulation adds, for the rounding-error bound."""
+    """(T, T_lr): T[m, n] = sum_g |sx sw P_g| + sum_j |xl1_j L2_jn| + |bias_n|,
+    the scale of every term the fp32 accumulation adds, and T_lr the low-rank
+    part alone (its fp32 input is split into bf16 hi + lo on the GPU, which
+    keeps ~17 bits)."""
     from oracle import numfmt
     a = np.asarray(qx_codes, np.float64)
     b = np.asarray(qw_codes, np.float64)
@@ -88,21 +90,30 @@ def magnitude_sum(qx_codes, sx, qw_codes, sw, xl1, l2_bits, bias_bits):
     sxf = np.asarray(sx, np.float16).astype(np.float64)
     swf = np.asarray(sw, np.float16).astype(np.float64)
     t = np.zeros((a.shape[0], b.shape[0]))
+    t_lr = np.zeros_like(t)
     for g in range(G):
         p = a[:, 64 * g:64 * g + 64] @ b[:, 64 * g:64 * g + 64].T
         t += np.abs(sxf[:, g][:, None] * swf[:, g][None, :] * p)
     if xl1 is not None and np.asarray(xl1).shape[1]:
-        t += np.abs(np.asarray(xl1, np.float64)) @ np.abs(numfmt.bf16_bits_to_f32(l2_bits).astype(np.float64))
+        t_lr = np.abs(np.asarray(xl1, np.float64)) @ np.abs(numfmt.bf16_bits_to_f32(l2_bits).astype(np.float64))
+        t += t_lr
     if bias_bits is not None:
         t += np.abs(numfmt.bf16_bits_to_f32(bias_bits).astype(np.float64))[None, :]
-    return t
+    return t, t_lr
+
+
+def fp32_bound(tmag, n_terms: int):
+    """Element-wise error allowance of the fp32 result: accumulation of n_terms
+    terms, 2 (n_terms + 4) 2^-24 T, plus the hi/lo split residual of the
+    low-rank input, 2^-16 T_lr (bf16 hi + bf16 lo keep 16-17 bits)."""
+    t, t_lr = tmag
+    return 2.0 * (n_terms + 4) * 2.0 ** -24 * t + 2.0 ** -16 * t_lr + 1e-30
 
 
 def assert_fp32_output(y32, y64, tmag, n_terms: int):
-    """fp32 accumulation of n_terms terms: |y32 - y64| <= 2 (n_terms + 4) 2^-24 T
-    element-wise (T from magnitude_sum), and relative Frobenius <= 1e-5."""
+    """|y32 - y64| <= fp32_bound element-wise, relative Frobenius <= 1e-5."""
     y32 = np.asarray(y32, np.float64)
-    bound = 2.0 * (n_terms + 4) * 2.0 ** -24 * tmag + 1e-30
+    bound = fp32_bound(tmag, n_terms)
     bad = np.abs(y32 - y64) > bound
     assert not bad.any(), (f"{bad.sum()} of {bad.size} fp32 outputs outside the accumulation bound; "
                            f"worst ratio {np.max(np.abs(y32 - y64) / bound):.3g}")

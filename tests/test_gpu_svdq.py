@@ -15,8 +15,8 @@ import torch
 import synth
 from oracle import numfmt, svdq as osv
 from gpu_util import (DevSvdq, assert_bf16_is_rounded_fp32, assert_bf16_output,
-                      assert_fp32_output, dev, dev_f16, dev_u16, host_bf16_f64, host_u16,
-                      magnitude_sum, note, rel_fro)
+                      assert_fp32_output, dev, dev_f16, dev_u16, fp32_bound, host_bf16_f64,
+                      host_u16, magnitude_sum, note, rel_fro)
 
 pytestmark = pytest.mark.gpu
 
@@ -149,7 +149,7 @@ def test_gemm_tiny(act, bias):
     y32h = y32.cpu().numpy()
     if act == "gelu_tanh":
         # GELU is 1-Lipschitz-ish (|gelu'| <= 1.13) plus fp32 tanh error
-        assert np.all(np.abs(y32h - y64) <= 1.13 * 2.0 * (cfg.K // 64 + cfg.rank + 4) * 2.0 ** -24 * tmag
+        assert np.all(np.abs(y32h - y64) <= 1.13 * fp32_bound(tmag, cfg.K // 64 + cfg.rank)
                       + 4e-7 * np.abs(y64) + 1e-7)
         assert rel_fro(y32h, y64) <= 1e-5
     else:
