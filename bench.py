@@ -83,6 +83,31 @@ def time_events(fn, iters):
     return s.elapsed_time(e) / iters
 
 
+def time_graph(fn, per_graph, replays=20):
+    """Average duration (ms) of one fn() when per_graph launches are captured in
+    a HIP graph and replayed back to back (no host launch gaps between them),
+    timed by HIP events on the replay stream."""
+    import torch
+    g = torch.cuda.CUDAGraph()
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(st):
+        fn()                     # warm: any first-use host set-up happens outside capture
+        with torch.cuda.graph(g, stream=st):
+            for _ in range(per_graph):
+                fn()
+    torch.cuda.current_stream().wait_stream(st)
+    g.replay()
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(replays):
+        g.replay()
+    e.record()
+    e.synchronize()
+    return s.elapsed_time(e) / (replays * per_graph)
+
+
 def cpu_baseline(M, K, N, rank, budget_s=20.0):
     """The oracle (numpy, fp64) timed on the host on a bounded sample of the
     QKV workload: the online path (activation quantisation + W4A4 output) for
@@ -167,7 +192,11 @@ def main():
     iters = max(20, args.steps)
     gemm_ms = time_events(lambda: lib.w4a4_linear(qx, sx, xl1, ops["qw"], ops["sw"], ops["l2t"],
                                                   ops["bias"], R, y=y), iters)
-    act_ms = time_events(lambda: lib.quantize_act(ops["x"], ops["inv_lambda"], ops["l1t"], R), iters)
+    qx_b = torch.empty_like(qx)
+    sx_b = torch.empty_like(sx)
+    xl1_b = torch.empty_like(xl1)
+    act_ms = time_graph(lambda: lib.svdq_quantize_act(ops["x"], M, K, K, ops["inv_lambda"], ops["l1t"], R,
+                                                      qx_b, sx_b, xl1_b), 50)
     gemm_tflops = flops / (gemm_ms * 1e-3) / 1e12
     act_bytes = M * K * 2 + M * K // 2 + M * (K // 64) * 2 + M * R * 4 + K * 4 + R * K * 2
     log(f"step {ms:.4f} ms, gemm {gemm_ms * 1e3:.1f} us ({gemm_tflops:.0f} TFLOP/s), "
@@ -199,7 +228,7 @@ def main():
 
         for _ in range(nrot * 2):
             gemv()
-        gemv_ms = time_events(gemv, nrot * 20)
+        gemv_ms = time_graph(gemv, nrot * 8)
         gemv_bytes = Na * Ka // 2 + 2 * Na * (Ka // 64) * 2 + Ma * Ka * 2 + Ma * Na * 2 + Ka * 4 + Na * 2
         extra.update({"awq_gemv_us": round(gemv_ms * 1e3, 2),
                       "awq_gemv_GBps": round(gemv_bytes / (gemv_ms * 1e-3) / 1e9, 1),

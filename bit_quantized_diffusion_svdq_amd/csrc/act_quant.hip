@@ -6,7 +6,9 @@
 // "SVDQuant moves hard values out of 4-bit"); here it is re-derived for CDNA4:
 //  - one workgroup owns 16 token rows; its 8 waves take the 64-wide groups of
 //    K round-robin, so every row is read from HBM exactly once with 128-byte
-//    contiguous row segments per group;
+//    contiguous row segments per group; each wave issues the loads of six of
+//    its groups at once (and the L1 fragments one group ahead) before it
+//    quantises them, to keep enough bytes in flight for HBM;
 //  - a lane holds 16 consecutive channels of one row (two dwordx4 loads);
 //    the four lanes of a row (lanes l, l^16, l^32, l^48) reduce the group
 //    absmax with two cross-lane max steps;
@@ -40,6 +42,7 @@ __global__ __launch_bounds__(ROWS * 32) void act_quant_kernel(
     const float* __restrict__ inv_lambda, const uint16_t* __restrict__ l1t,
     uint8_t* __restrict__ qx, uint16_t* __restrict__ sx, float* __restrict__ xl1)
 {
+    constexpr int RTX = RT > 0 ? RT : 1;
     extern __shared__ float smem[];
     const int G = (int)(K / 64);
     float* s_inv = smem;                                   // [K]
@@ -50,27 +53,41 @@ __global__ __launch_bounds__(ROWS * 32) void act_quant_kernel(
     const int lane = tid & 63, wave = tid >> 6;
     const int64_t m0 = (int64_t)blockIdx.x * ROWS;
 
-    for (int64_t k = tid; k < K; k += ROWS * 32)
-        s_inv[k] = inv_lambda ? inv_lambda[k] : 1.0f;
-    __syncthreads();
-
     const int r = lane & 15, p = lane >> 4;
     const int64_t row = m0 + r;
     const bool valid = row < M;
-    const uint16_t* xrow = x + row * ldx;
+    // rows past the end read the last row; nothing of theirs is stored
+    const uint16_t* xrow = x + (valid ? row : M - 1) * ldx;
+    // this wave's groups are wave, wave + 8, ...; indices past the end are
+    // clamped to a real group so prefetches stay in bounds
+    const int n = (G > wave) ? (G - wave + WAVES - 1) / WAVES : 0;
+    auto gidx = [&](int i) { const int gi = wave + WAVES * i; return gi < G ? gi : G - 1; };
 
-    v4f acc[RT > 0 ? RT : 1];
+    v4f acc[RTX];
 #pragma unroll
-    for (int t = 0; t < (RT > 0 ? RT : 1); ++t) acc[t] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < RTX; ++t) acc[t] = v4f{0.f, 0.f, 0.f, 0.f};
 
-    for (int g = wave; g < G; g += WAVES) {
-        const int kb = g * 64 + 16 * p;
-        uint4 a0 = {0, 0, 0, 0}, a1 = {0, 0, 0, 0};
-        if (valid) {
-            a0 = *(const uint4*)(xrow + kb);
-            a1 = *(const uint4*)(xrow + kb + 8);
+    auto loadx = [&](uint4 (&d)[2], int i) {
+        const int kb = gidx(i) * 64 + 16 * p;
+        d[0] = *(const uint4*)(xrow + kb);
+        d[1] = *(const uint4*)(xrow + kb + 8);
+    };
+    auto loadl = [&](v8bf (&d)[RTX][2], int i) {
+        if constexpr (RT > 0) {
+            const int kb = gidx(i) * 64 + 16 * p;
+#pragma unroll
+            for (int t = 0; t < RT; ++t) {
+                const uint16_t* lrow = l1t + (int64_t)(16 * t + r) * K + kb;
+                d[t][0] = *(const v8bf*)(lrow);
+                d[t][1] = *(const v8bf*)(lrow + 8);
+            }
         }
-        const uint32_t w[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+    };
+    // quantise the lane's 16 values of group gidx(i) and feed the MFMA
+    auto process = [&](const uint4 (&xv)[2], const v8bf (&lv)[RTX][2], int i) {
+        const int g = gidx(i);
+        const int kb = g * 64 + 16 * p;
+        const uint32_t w[8] = {xv[0].x, xv[0].y, xv[0].z, xv[0].w, xv[1].x, xv[1].y, xv[1].z, xv[1].w};
         float v[16];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
@@ -103,8 +120,8 @@ __global__ __launch_bounds__(ROWS * 32) void act_quant_kernel(
             v8bf ah0, al0, ah1, al1;
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                __bf16 h0 = (__bf16)v[j];
-                __bf16 h1 = (__bf16)v[8 + j];
+                const __bf16 h0 = (__bf16)v[j];
+                const __bf16 h1 = (__bf16)v[8 + j];
                 ah0[j] = h0;
                 ah1[j] = h1;
                 al0[j] = (__bf16)(v[j] - (float)h0);
@@ -112,13 +129,40 @@ __global__ __launch_bounds__(ROWS * 32) void act_quant_kernel(
             }
 #pragma unroll
             for (int t = 0; t < RT; ++t) {
-                const uint16_t* lrow = l1t + (int64_t)(16 * t + r) * K + kb;
-                const v8bf b0 = *(const v8bf*)(lrow);
-                const v8bf b1 = *(const v8bf*)(lrow + 8);
-                acc[t] = mfma_bf16_16x16x32(ah0, b0, acc[t]);
-                acc[t] = mfma_bf16_16x16x32(al0, b0, acc[t]);
-                acc[t] = mfma_bf16_16x16x32(ah1, b1, acc[t]);
-                acc[t] = mfma_bf16_16x16x32(al1, b1, acc[t]);
+                acc[t] = mfma_bf16_16x16x32(ah0, lv[t][0], acc[t]);
+                acc[t] = mfma_bf16_16x16x32(al0, lv[t][0], acc[t]);
+                acc[t] = mfma_bf16_16x16x32(ah1, lv[t][1], acc[t]);
+                acc[t] = mfma_bf16_16x16x32(al1, lv[t][1], acc[t]);
+            }
+        }
+    };
+
+    // the X loads of up to CH groups are all issued before any is processed
+    // (with 2 waves per SIMD that keeps ~96 KB per CU in flight); L1 fragments
+    // run one group ahead
+    constexpr int CH = 6;
+    v8bf la[RTX][2], lb[RTX][2];
+    for (int c0 = 0; c0 < ((n + CH - 1) / CH) * CH || c0 == 0; c0 += CH) {
+        uint4 xs[CH][2];
+#pragma unroll
+        for (int u = 0; u < CH; ++u) loadx(xs[u], c0 + u);
+        loadl(la, c0);
+        if (c0 == 0) {
+            // the smoothing reciprocals go to LDS while the first X loads fly
+            for (int64_t k = 4 * tid; k < K; k += 4 * ROWS * 32)
+                *(float4*)(s_inv + k) = inv_lambda ? *(const float4*)(inv_lambda + k)
+                                                   : make_float4(1.f, 1.f, 1.f, 1.f);
+            __syncthreads();
+        }
+#pragma unroll
+        for (int u = 0; u < CH; u += 2) {
+            if (c0 + u < n) {
+                loadl(lb, c0 + u + 1);
+                process(xs[u], la, c0 + u);
+            }
+            if (c0 + u + 1 < n) {
+                loadl(la, c0 + u + 2);
+                process(xs[u + 1], lb, c0 + u + 1);
             }
         }
     }

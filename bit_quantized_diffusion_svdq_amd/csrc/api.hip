@@ -25,7 +25,7 @@ hipError_t launch_gemm_w4a4_partials(const uint8_t* qx, const uint8_t* qw, int64
 hipError_t launch_gemv_w4a16(const uint16_t* x, int M, int64_t K, const float* inv_s,
                              const uint8_t* qw, const uint16_t* scale, const uint16_t* zero,
                              int64_t N, const uint16_t* bias, uint16_t* y, hipStream_t stream);
-size_t gemv_smem_bytes(int M);
+size_t gemv_smem_bytes(int M, int64_t K);
 
 namespace {
 
@@ -147,9 +147,9 @@ svdq_status svdq_quantize_act(const void* x, int64_t M, int64_t K, int64_t ldx,
     if (!x || !qx || !sx_f16) return fail(SVDQ_ERR_NULL, "x, qx and sx_f16 are required");
     if (rank > 0 && (!l1t || !xl1)) return fail(SVDQ_ERR_NULL, "rank %d needs l1t and xl1", rank);
     if (!aligned(x, 16) || !aligned(qx, 16) || !aligned(sx_f16, 4) ||
-        (inv_lambda && !aligned(inv_lambda, 4)) ||
+        (inv_lambda && !aligned(inv_lambda, 16)) ||
         (rank > 0 && (!aligned(l1t, 16) || !aligned(xl1, 16))))
-        return fail(SVDQ_ERR_ALIGN, "x, l1t, qx, xl1 need 16-byte alignment, sx_f16 4 bytes");
+        return fail(SVDQ_ERR_ALIGN, "x, inv_lambda, l1t, qx, xl1 need 16-byte alignment, sx_f16 4 bytes");
     if ((s = check_current_device()) != SVDQ_OK) return s;
     return launched(launch_act_quant((const uint16_t*)x, M, K, ldx, inv_lambda,
                                      rank > 0 ? (const uint16_t*)l1t : nullptr, rank, qx,
@@ -219,9 +219,9 @@ svdq_status awq_gemv_w4a16(const void* x, int64_t M, int64_t K, const float* inv
     if (N / 16 > 0x7FFFFFFF) return fail(SVDQ_ERR_SHAPE, "N too large");
     if (!x || !qw || !scale_f16 || !zero_f16 || !y) return fail(SVDQ_ERR_NULL, "x, qw, scale, zero and y are required");
     if (!aligned(x, 16) || !aligned(qw, 16) || !aligned(y, 16) || !aligned(scale_f16, 4) ||
-        !aligned(zero_f16, 4) || (inv_s && !aligned(inv_s, 4)) || (bias && !aligned(bias, 2)))
-        return fail(SVDQ_ERR_ALIGN, "x, qw, y need 16-byte alignment, scale/zero 4 bytes");
-    if (gemv_smem_bytes((int)M) > kMaxLds) return fail(SVDQ_ERR_SHAPE, "M too large for the LDS budget");
+        !aligned(zero_f16, 4) || (inv_s && !aligned(inv_s, 16)) || (bias && !aligned(bias, 2)))
+        return fail(SVDQ_ERR_ALIGN, "x, inv_s, qw, y need 16-byte alignment, scale/zero 4 bytes");
+    if (gemv_smem_bytes((int)M, K) > kMaxLds) return fail(SVDQ_ERR_SHAPE, "M too large for the LDS budget");
     if ((s = check_current_device()) != SVDQ_OK) return s;
     return launched(launch_gemv_w4a16((const uint16_t*)x, (int)M, K, inv_s, qw,
                                       (const uint16_t*)scale_f16, (const uint16_t*)zero_f16, N,

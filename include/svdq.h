@@ -91,7 +91,7 @@ int svdq_version(void);
  * if s == 0 all codes are 0, else q = clamp(rtne(x_hat * fp32(1 / s)), -7, 7).
  * qx and sx are bit-exact with that definition. xl1 is accumulated in fp32
  * (relative error about 1e-6).
- * Alignment: x, l1t, qx, xl1 16-byte aligned; sx_f16 4-byte aligned.
+ * Alignment: x, inv_lambda, l1t, qx, xl1 16-byte aligned; sx_f16 4-byte aligned.
  */
 svdq_status svdq_quantize_act(const void* x, int64_t M, int64_t K, int64_t ldx,
                               const float* inv_lambda, const void* l1t, int32_t rank,
@@ -146,7 +146,7 @@ svdq_status svdq_gemm_w4a4_partials(const uint8_t* qx, int64_t M, int64_t K,
  *  y          out: bf16 [M][N]
  * N % 16 == 0. Accumulation is fp32; the result matches the fp64 definition
  * to about 1e-5 relative before the bf16 rounding.
- * Alignment: x, qw, y 16-byte aligned; scale/zero 4 bytes.
+ * Alignment: x, inv_s, qw, y 16-byte aligned; scale/zero 4 bytes.
  */
 svdq_status awq_gemv_w4a16(const void* x, int64_t M, int64_t K, const float* inv_s,
                            const uint8_t* qw, const void* scale_f16, const void* zero_f16,

@@ -44,6 +44,7 @@ def test_awq_full_size():
 
 
 @pytest.mark.parametrize("M,K,N,scaled,bias", [(1, 64, 16, False, False), (16, 192, 48, True, True),
+                                               (16, 3072, 80, True, True),
                                                (7, 2048 + 192, 32, True, False), (3, 4096, 64, True, True)])
 def test_awq_shapes(M, K, N, scaled, bias):
     note(f"awq gemv M={M} K={K} N={N}")
