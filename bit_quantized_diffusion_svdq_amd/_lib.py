@@ -149,10 +149,14 @@ def w4a4_linear(qx, sx, xl1, qw, sw, l2t, bias, rank: int, act: str = "none",
     return y
 
 
-def awq_gemv(x, inv_s, qw, scale, zero, bias, y=None, stream=None):
+def awq_gemv(x, inv_s, qwt, scale_t, zero_t, bias, N=None, y=None, stream=None):
+    """x bf16 [M, K]; qwt, scale_t, zero_t: codes, fp16 scales and zero points
+    in the GEMV tile layout (any shape: N * K / 2 bytes, N * K / 64 values)
+    -> y bf16 [M, N]."""
     M, K = x.shape
-    N = qw.shape[0]
+    if N is None:
+        N = scale_t.numel() // (K // 64)
     if y is None:
         y = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
-    awq_gemv_w4a16(x, M, K, inv_s, qw, scale, zero, N, bias, y, stream)
+    awq_gemv_w4a16(x, M, K, inv_s, qwt, scale_t, zero_t, N, bias, y, stream)
     return y

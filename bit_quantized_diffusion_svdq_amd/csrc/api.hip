@@ -23,8 +23,8 @@ hipError_t launch_gemm_w4a4_partials(const uint8_t* qx, const uint8_t* qw, int64
                                      int64_t K, int64_t m0, int64_t mc, int64_t n0, int64_t nc,
                                      int32_t* p, hipStream_t stream);
 hipError_t launch_gemv_w4a16(const uint16_t* x, int M, int64_t K, const float* inv_s,
-                             const uint8_t* qw, const uint16_t* scale, const uint16_t* zero,
-                             int64_t N, const uint16_t* bias, uint16_t* y, hipStream_t stream);
+                             const uint8_t* qwt, const uint16_t* scale, const uint16_t* zero,
+                             int64_t N, const uint16_t* bias, uint16_t* y, int cus, hipStream_t stream);
 size_t gemv_smem_bytes(int M, int64_t K);
 
 namespace {
@@ -45,9 +45,11 @@ svdq_status fail(svdq_status s, const char* fmt, ...) {
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
-// Per-device capability cache: 0 = unknown, 1 = gfx950, 2 = not supported.
+// Per-device capability cache: 0 = unknown, 1 = gfx950, 2 = not supported;
+// and the device's compute-unit count (persistent grids).
 constexpr int kMaxDev = 64;
 int g_dev_ok[kMaxDev];
+int g_dev_cus[kMaxDev];
 std::mutex g_dev_mu;
 
 svdq_status check_device_id(int dev) {
@@ -72,19 +74,25 @@ svdq_status check_device_id(int dev) {
     {
         std::lock_guard<std::mutex> lk(g_dev_mu);
         g_dev_ok[dev] = ok ? 1 : 2;
+        g_dev_cus[dev] = prop.multiProcessorCount > 0 ? prop.multiProcessorCount : 1;
     }
     if (!ok) return fail(SVDQ_ERR_DEVICE, "device %d is %s, these kernels are built for gfx950 only",
                          dev, prop.gcnArchName);
     return SVDQ_OK;
 }
 
-svdq_status check_current_device() {
+svdq_status check_current_device(int* cus = nullptr) {
     int dev = -1;
     if (hipGetDevice(&dev) != hipSuccess) {
         (void)hipGetLastError();
         return fail(SVDQ_ERR_DEVICE, "no current HIP device");
     }
-    return check_device_id(dev);
+    const svdq_status s = check_device_id(dev);
+    if (s == SVDQ_OK && cus) {
+        std::lock_guard<std::mutex> lk(g_dev_mu);
+        *cus = g_dev_cus[dev];
+    }
+    return s;
 }
 
 svdq_status launched(hipError_t e, const char* what) {
@@ -210,22 +218,29 @@ svdq_status svdq_gemm_w4a4_partials(const uint8_t* qx, int64_t M, int64_t K,
 }
 
 svdq_status awq_gemv_w4a16(const void* x, int64_t M, int64_t K, const float* inv_s,
-                           const uint8_t* qw, const void* scale_f16, const void* zero_f16,
+                           const uint8_t* qwt, const void* scale_f16, const void* zero_f16,
                            int64_t N, const void* bias, void* y, void* stream) {
+    const uint8_t* qw = qwt;
     svdq_status s;
     if (M < 1 || M > 16) return fail(SVDQ_ERR_SHAPE, "M = %lld must be in [1, 16]", (long long)M);
     if ((s = check_k(K)) != SVDQ_OK) return s;
+    if (K % 128) return fail(SVDQ_ERR_SHAPE, "K = %lld must be a multiple of 128 (group pairs)", (long long)K);
     if (N <= 0 || N % 16) return fail(SVDQ_ERR_SHAPE, "N = %lld must be a positive multiple of 16", (long long)N);
-    if (N / 16 > 0x7FFFFFFF) return fail(SVDQ_ERR_SHAPE, "N too large");
+    // the kernel addresses every array with 31-bit byte offsets
+    const int64_t lim = (int64_t)1 << 31;
+    if (N * (K / 2) >= lim || N * (K / 64) * 2 >= lim || M * K * 2 >= lim || K * 4 >= lim)
+        return fail(SVDQ_ERR_SHAPE, "N = %lld, K = %lld: packed weights or scales exceed 2 GiB",
+                    (long long)N, (long long)K);
     if (!x || !qw || !scale_f16 || !zero_f16 || !y) return fail(SVDQ_ERR_NULL, "x, qw, scale, zero and y are required");
-    if (!aligned(x, 16) || !aligned(qw, 16) || !aligned(y, 16) || !aligned(scale_f16, 4) ||
-        !aligned(zero_f16, 4) || (inv_s && !aligned(inv_s, 16)) || (bias && !aligned(bias, 2)))
-        return fail(SVDQ_ERR_ALIGN, "x, inv_s, qw, y need 16-byte alignment, scale/zero 4 bytes");
+    if (!aligned(x, 16) || !aligned(qw, 16) || !aligned(y, 16) || !aligned(scale_f16, 2) ||
+        !aligned(zero_f16, 2) || (inv_s && !aligned(inv_s, 16)) || (bias && !aligned(bias, 2)))
+        return fail(SVDQ_ERR_ALIGN, "x, inv_s, qw, y need 16-byte alignment, scale/zero 2 bytes");
     if (gemv_smem_bytes((int)M, K) > kMaxLds) return fail(SVDQ_ERR_SHAPE, "M too large for the LDS budget");
-    if ((s = check_current_device()) != SVDQ_OK) return s;
+    int cus = 0;
+    if ((s = check_current_device(&cus)) != SVDQ_OK) return s;
     return launched(launch_gemv_w4a16((const uint16_t*)x, (int)M, K, inv_s, qw,
                                       (const uint16_t*)scale_f16, (const uint16_t*)zero_f16, N,
-                                      (const uint16_t*)bias, (uint16_t*)y, (hipStream_t)stream),
+                                      (const uint16_t*)bias, (uint16_t*)y, cus, (hipStream_t)stream),
                     "awq_gemv_w4a16 launch");
 }
 

@@ -14,6 +14,13 @@ typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 
 #define DEV __device__ __forceinline__
 
+// Raw buffer resource over `bytes` bytes at `base` (gfx9 word 3: 32-bit data
+// format, no swizzle). Loads beyond `bytes` return 0.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+DEV rsrc_t make_rsrc(const void* base, int64_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)bytes, 0x00020000);
+}
+
 DEV float bf16_lo_to_f32(uint32_t w) { return __uint_as_float(w << 16); }
 DEV float bf16_hi_to_f32(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 

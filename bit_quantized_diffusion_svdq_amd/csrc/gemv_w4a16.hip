@@ -4,221 +4,402 @@
 // dequantised in registers.
 //
 // CDNA4 design:
+//  - Weights arrive in a tile layout, codes [N/16][K/128][16 columns][64 B]
+//    and scales / zero points [N/16][K/64][16]: the codes of one group pair
+//    of 16 columns are one contiguous 1 KB block and their scales 64 B, so
+//    every load instruction of a wave reads whole contiguous runs (16 lanes
+//    x 16 B per 256 B run streams at full rate; 16 rows x 32 B per
+//    instruction reaches less than half of it).
 //  - A nibble q becomes the bf16 value 128 + q exactly by OR-ing it into the
-//    bf16 pattern of 128.0 (0x4300): one shift + one and-or per two codes.
-//  - The bf16 MFMA (16x16x32) forms D_g = sum_k x~[m,k] (128 + q[n,k]) per
-//    64-wide group; the zero point and the offset fold out through the
-//    per-(row, group) sum of x~:  Y += s (D_g - (128 + z) sum_k x~).
-//  - x~ = fp32(x) * inv_s is split into bf16 hi + lo (two MFMAs) so the
-//    activations keep ~16 mantissa bits; hi/lo and the group sums are
-//    prepared once per workgroup in LDS, already in MFMA operand order.
-//  - A workgroup owns 64 output columns (4 waves x 16); each wave streams the
-//    whole K of its columns, keeping the next batch of 16 groups (codes,
-//    scales, zeros) in flight while it computes the current batch, so about
-//    70 KB per CU is in flight: enough to cover HBM latency at full rate.
+//    bf16 pattern of 128.0 (0x4300).
+//  - One v_mfma_f32_16x16x32_bf16 consumes 32 codes of each of 16 columns:
+//    lanes 0-31 hold codes of group A of the pair, lanes 32-63 of group B.
+//    The 16 rows of the A operand are used as [lo/hi][group][4 token rows]:
+//    rows 0-3 carry bf16(x~) of group A, rows 4-7 of group B, rows 8-15 the
+//    bf16 remainders x~ - hi, each zero where its group's codes are absent.
+//    So one MFMA chain yields D = sum x~ (128 + q) of both groups, hi and lo
+//    parts apart, and every lane of the result is a useful number.
+//  - The zero point and the offset fold out through the per-(row, group)
+//    sum of x~:  Y += s (D_hi - (128 + z) X) + s D_lo, where X = sum (hi + lo)
+//    comes from the same A fragments times a matrix of ones on the MFMA, so
+//    it is the sum the MFMA itself sees.
+//  - About one workgroup per CU: workgroup i owns TPW consecutive column
+//    tiles (TPW = 1, 2, 4, 5 or 8, template; 5 at 4 x 3072 -> 18432 on 256
+//    CUs) and prepares x~ = x inv_s (bf16 hi/lo in the A-operand order) and
+//    the scales and offsets of its tiles once in LDS. Its 8 waves split the
+//    group pairs into 8 parts; wave w streams part w of every tile of the workgroup, pair-major
+//    with the tile index a compile-time constant, so each tile keeps its own
+//    accumulator in registers and the task stream has no branch. The first
+//    loads are issued before the preparation so the weight stream starts at
+//    once. Lanes and parts are summed in LDS in a fixed order at the end
+//    (deterministic).
+//  - Token rows are processed in quads (NQ = 1, 2 or 4, template): every quad
+//    has its own A operand and accumulator; weights are loaded once.
 #include "common.h"
 
 namespace {
 
-constexpr int NT = 256;
-constexpr int WAVES = 4;
-constexpr int COLS = 16 * WAVES;
-constexpr int BATCH = 16;         // groups per prefetch batch
-constexpr int MAXM = 16;
-constexpr int LDS_ELEMS = 32768;  // x~ elements (rows x K chunk) held in LDS, hi + lo
+constexpr int NT = 512;
+constexpr int NW = NT / 64;       // waves = K parts
+constexpr int BTMAX = 16;         // (pair, tile) tasks per weight batch (rounded down to whole pairs)
+constexpr int ABLK = 528;         // A block per (quad, pair, step): 32 slots x 16 B + zero slot
+constexpr int MAXT = 8;           // largest tiles-per-workgroup instantiation
+constexpr int LDS_BUDGET = 147456;
 
-// K chunk held in LDS: a multiple of 2048 (32 groups, two prefetch batches),
-// so every chunk starts on an even batch
-__host__ __device__ inline int kchunk(int M, int64_t K) {
-    const int kc = (LDS_ELEMS / M) & ~2047;
-    return (int)(K < kc ? K : kc);
+__host__ __device__ inline int quads(int M) { return M <= 4 ? 1 : (M <= 8 ? 2 : 4); }
+
+// reduction buffer: [TPW tiles][NW parts][NQ][4 rows][16 columns] floats
+__host__ __device__ inline int red_bytes(int NQ, int TPW) { return TPW * NW * NQ * 4 * 16 * 4; }
+
+// group pairs held in LDS per chunk: A blocks 4 * ABLK per quad, and
+// (scale, offset) pairs 2 groups x 16 TPW columns x 8 B, beside the reduction buffer
+__host__ __device__ inline int chunk_pairs(int NQ, int TPW, int KP) {
+    const int cp = (LDS_BUDGET - red_bytes(NQ, TPW)) / (4 * ABLK * NQ + 2 * 16 * TPW * 8);
+    return KP < cp ? KP : cp;
 }
 
-// MFMA slot j of a step holds element perm[j] of the lane's 8 codes, because
+// MFMA slot j of a step holds element perm(j) of the lane's 8 codes, because
 // the 8 nibbles of a dword are expanded as pairs (t, t + 4).
 DEV int slot_of(int o) { return (o < 4) ? 2 * o : 2 * (o - 4) + 1; }
 
-DEV v8bf codes_to_bf16(uint32_t x) {
+DEV uint32_t and_or(uint32_t x, uint32_t m, uint32_t c) { return (x & m) | c; }
+
+DEV v8bf codes_to_bf16(uint32_t x, uint32_t magic) {
+    const uint32_t y = x >> 8;
     uint32_t d[4];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) d[t] = ((x >> (4 * t)) & 0x000F000Fu) | 0x43004300u;
+    d[0] = and_or(x, 0x000F000Fu, magic);
+    d[1] = and_or(x >> 4, 0x000F000Fu, magic);
+    d[2] = and_or(y, 0x000F000Fu, magic);
+    d[3] = and_or(y >> 4, 0x000F000Fu, magic);
     return __builtin_bit_cast(v8bf, make_uint4(d[0], d[1], d[2], d[3]));
 }
 
-struct Batch {
-    uint2 q[BATCH];
-    uint32_t sz[BATCH];     // scale (low 16 bits) and zero (high 16 bits), fp16
-};
+DEV uint4 ld128(rsrc_t r, int off, int soff) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, soff, 0);
+    return make_uint4(v[0], v[1], v[2], v[3]);
+}
 
-__global__ __launch_bounds__(NT) void gemv_w4a16_kernel(
-    const uint16_t* __restrict__ x, int M, int64_t K, const float* __restrict__ inv_s,
-    const uint8_t* __restrict__ qw, const uint16_t* __restrict__ scale,
-    const uint16_t* __restrict__ zero, int64_t N, const uint16_t* __restrict__ bias,
+DEV uint32_t pk(uint16_t a, uint16_t b) { return (uint32_t)a | ((uint32_t)b << 16); }
+
+template <int NQ, int TPW>
+__global__ __launch_bounds__(NT, 2) void gemv_w4a16_kernel(
+    const uint16_t* __restrict__ x, int M, int K, const float* __restrict__ inv_s,
+    const uint8_t* __restrict__ qwt, const uint16_t* __restrict__ scale_t,
+    const uint16_t* __restrict__ zero_t, int N, const uint16_t* __restrict__ bias,
     uint16_t* __restrict__ y)
 {
-    extern __shared__ uint32_t smem_u[];
-    const int KC = kchunk(M, K);
-    const int steps_c = KC / 32;
-    // [2 (hi, lo)][steps][4 p][M][8 bf16]  then  xsum [KC/64][MAXM]
-    uint16_t* s_a = (uint16_t*)smem_u;
-    float* s_xsum = (float*)(smem_u + (2 * steps_c * 4 * M * 8) / 2);
+    constexpr int LNQ = NQ == 1 ? 0 : (NQ == 2 ? 1 : 2);
+    constexpr int PB = ((BTMAX / NQ) / TPW > 0) ? (BTMAX / NQ) / TPW : 1;   // pairs per batch
+    constexpr int BT = PB * TPW;                                           // tasks per batch
+    constexpr int TC = TPW * 16;                                           // columns per workgroup
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    const int KP = K / 128, G = K / 64, T = N / 16;
+    const int CP = chunk_pairs(NQ, TPW, KP);
+    // LDS: A blocks [NQ][CP][4 steps][ABLK], (scale, 128 + zero) [2 CP][TC], reduction buffer
+    char* s_a = smem;
+    float2* s_so = (float2*)(smem + NQ * CP * 4 * ABLK);
+    float* s_red = (float*)(smem + LDS_BUDGET - red_bytes(NQ, TPW));
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (scalar)
     const int c = lane & 15, p = lane >> 4;
-    const int64_t n = (int64_t)blockIdx.x * COLS + wave * 16 + c;
-    const int64_t ncl = n < N ? n : N - 1;      // columns past N read the last one, never stored
-    const int G = (int)(K / 64);
-    const uint8_t* wrow = qw + ncl * (K / 2) + 8 * p;
-    const uint16_t* srow = scale + ncl * G;
-    const uint16_t* zrow = zero + ncl * G;
+    const int t0 = blockIdx.x * TPW;                            // this workgroup's tiles t0 .. t0 + TPW - 1
 
-    auto load_batch = [&](Batch& b, int g0) {
+    // buffer resources (the host checks every array fits 31-bit byte offsets)
+    const rsrc_t rw = make_rsrc(qwt, (int64_t)N * (K / 2));
+    const rsrc_t rx = make_rsrc(x, (int64_t)M * K * 2);
+    const rsrc_t rs = make_rsrc(inv_s, inv_s ? (int64_t)K * 4 : 0);
+    const rsrc_t rsc = make_rsrc(scale_t, (int64_t)N * G * 2);
+    const rsrc_t rzr = make_rsrc(zero_t, (int64_t)N * G * 2);
+
+    // opaque copy of the bf16 pattern of 128.0 in a VGPR, so the nibble
+    // expansion is one v_and_or_b32 per dword (mask from an SGPR)
+    uint32_t magic;
+    asm volatile("v_mov_b32 %0, 0x43004300" : "=v"(magic));
+    const v8bf ones = __builtin_bit_cast(v8bf, make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u));
+
+    // A operand: lane (row r, k-group p) reads slot p * 8 + (r >> 3) * 4 + (r & 3)
+    // when row r's group (bit 2 of r) matches the lane's codes (p >> 1), else the zero slot
+    const int aoff = (((c >> 2) & 1) == (p >> 1)) ? 16 * (p * 8 + (c >> 3) * 4 + (c & 3)) : 512;
+    // epilogue: lane (column c, p) holds result rows 4p..4p+3 = [lo/hi][group][row]
+    const int eg = p & 1;                      // group of the pair this lane's result belongs to
+    const float omask = (p < 2) ? 1.0f : 0.0f; // the zero-point fold applies to the hi part only
+    const int woff = c * 64 + 16 * p;          // + (tile * KP + pair) * 1024
+
+    v4f acc[TPW][NQ];
 #pragma unroll
-        for (int i = 0; i < BATCH; ++i) {
-            const int g = (g0 + i < G) ? g0 + i : G - 1;     // clamped: stays in bounds
-            b.q[i] = *(const uint2*)(wrow + (int64_t)g * 32);
-            b.sz[i] = (uint32_t)srow[g] | ((uint32_t)zrow[g] << 16);
-        }
-    };
-
-    v4f acc = {0.f, 0.f, 0.f, 0.f};
-    Batch b0, b1;
-    load_batch(b0, 0);
-
-    for (int64_t k0 = 0; k0 < K; k0 += KC) {
-        const int kc = (int)((K - k0) < KC ? (K - k0) : KC);
-        const int gc = kc / 64, gbase = (int)(k0 / 64);
-        __syncthreads();   // previous chunk's LDS reads are done
-        // x~ hi/lo in MFMA order; item = (row m, 8 consecutive k); the 8 items
-        // of one (row, group) are 8 consecutive threads, which sum their part.
-        // Items are taken 8 per thread at a time with all their loads issued
-        // first, so the prep costs one memory latency per 8 items.
-        const int nitems = M * (kc / 8);
-        constexpr int IB = 8;
-        for (int it0 = 0; it0 < nitems; it0 += IB * NT) {
-            uint4 raw[IB];
-            float4 sc0[IB], sc1[IB];
+    for (int t = 0; t < TPW; ++t)
 #pragma unroll
-            for (int u = 0; u < IB; ++u) {
-                const int itc = min(it0 + u * NT + tid, nitems - 1);      // clamped: in bounds
-                const int m = itc / (kc / 8), kk = (itc % (kc / 8)) * 8;
-                raw[u] = *(const uint4*)(x + (int64_t)m * K + k0 + kk);
-                if (inv_s) {
-                    sc0[u] = *(const float4*)(inv_s + k0 + kk);
-                    sc1[u] = *(const float4*)(inv_s + k0 + kk + 4);
-                } else {
-                    sc0[u] = make_float4(1.f, 1.f, 1.f, 1.f);
-                    sc1[u] = sc0[u];
-                }
+        for (int q = 0; q < NQ; ++q) acc[t][q] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    for (int pc0 = 0; pc0 < KP; pc0 += CP) {
+        const int np = (KP - pc0) < CP ? (KP - pc0) : CP;       // pairs in this chunk
+        const int gc = 2 * np, g0 = 2 * pc0;                    // groups in this chunk
+        // this wave's pairs [ps, pe) of the chunk
+        const int ps = (wave * np) / NW, pe = ((wave + 1) * np) / NW;
+        const int plast = pe > ps ? pe - 1 : ps;
+        const int xitems = gc * NQ * 8;                         // (group, quad, 8 channels)
+        const int sitems = TPW * gc * 2;                        // (tile, group, 8 columns) uint4
+
+        // ---- 1. preparation loads (x, inv_s; scales, zero points), issued first
+        auto xload = [&](int it, uint4 (&xr)[4], uint4& s0, uint4& s1) {
+            const int itc = it < xitems ? it : xitems - 1;      // clamped: stays in bounds
+            const int sub = itc & 7, q = (itc >> 3) & (NQ - 1), gl = itc >> (3 + LNQ);
+            const int k = (g0 + gl) * 64 + sub * 8;
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                const int m = 4 * q + rr;
+                const int mr = m < M ? m : M - 1;               // padded rows read a real row
+                xr[rr] = ld128(rx, (mr * K + k) * 2, 0);
             }
+            if (inv_s) {
+                s0 = ld128(rs, k * 4, 0);
+                s1 = ld128(rs, k * 4 + 16, 0);
+            } else {
+                s0 = make_uint4(0x3F800000u, 0x3F800000u, 0x3F800000u, 0x3F800000u);
+                s1 = s0;
+            }
+        };
+        // scale / zero item: 8 columns (half a tile row) of group gl of tile ti
+        auto sitem = [&](int it, int& ti, int& gl, int& h) {
+            const int itc = it < sitems ? it : sitems - 1;
+            h = itc & 1;
+            const int r = itc >> 1;                             // row (tile, group) of the block
+            ti = r / gc;
+            gl = r - ti * gc;
+        };
+        auto sload = [&](int it, uint4& sb, uint4& zb) {
+            int ti, gl, h;
+            sitem(it, ti, gl, h);
+            const int tt = t0 + ti < T ? t0 + ti : T - 1;
+            const int off = ((tt * G + g0 + gl) * 16 + 8 * h) * 2;
+            sb = ld128(rsc, off, 0);
+            zb = ld128(rzr, off, 0);
+        };
+        uint4 xr0[4], xs0, xs1, sb0, zb0, sb1, zb1;
+        xload(tid, xr0, xs0, xs1);
+        sload(tid, sb0, zb0);
+        sload(tid + NT, sb1, zb1);
+
+        // ---- 2. this wave's first batch of codes
+        uint4 qv[BT];
+        auto load_batch = [&](int j0) {                          // j0: first pair (chunk-local)
 #pragma unroll
-            for (int u = 0; u < IB; ++u) {
-                const int it = it0 + u * NT + tid;
-                if (it0 + u * NT >= nitems) break;        // uniform across the workgroup
-                const bool live = it < nitems;
-                const int itc = live ? it : nitems - 1;
-                const int m = itc / (kc / 8), kk = (itc % (kc / 8)) * 8;
-                const int gl = kk / 64, pp = (kk % 64) / 16, ss = (kk % 16) / 8;
-                const uint32_t w[4] = {raw[u].x, raw[u].y, raw[u].z, raw[u].w};
-                const float is[8] = {sc0[u].x, sc0[u].y, sc0[u].z, sc0[u].w,
-                                     sc1[u].x, sc1[u].y, sc1[u].z, sc1[u].w};
+            for (int i = 0; i < BT; ++i) {
+                // task i: pair j0 + i / TPW, tile t0 + i % TPW; pairs past the end and
+                // tiles past N re-read valid data (clamped)
+                const int pl = (j0 + i / TPW < pe) ? j0 + i / TPW : plast;
+                const int pcl = pc0 + (pl < np ? pl : np - 1);
+                const int tt = t0 + i % TPW;
+                const int tcl = tt < T ? tt : T - 1;
+                // wave-uniform offset: keep it in an SGPR (a VGPR offset would turn
+                // each buffer load into a waterfall loop)
+                const int wb = __builtin_amdgcn_readfirstlane((tcl * KP + pcl) * 1024);
+                qv[i] = ld128(rw, woff, wb);
+            }
+        };
+        load_batch(ps);
+
+        // ---- 3. preparation into LDS: x~ = x inv_s as bf16 hi/lo in A-operand
+        // order, and (scale, 128 + zero) per (group, column)
+        auto xprep = [&](const uint4 (&xr)[4], const uint4& s0, const uint4& s1, int it) {
+            if (it >= xitems) return;
+            const int sub = it & 7, q = (it >> 3) & (NQ - 1), gl = it >> (3 + LNQ);
+            // channels 8 sub .. 8 sub + 7 of group gl: lane p = 2 (gl & 1) + (sub >> 2), step sub & 3
+            const int pl = 2 * (gl & 1) + (sub >> 2), st = sub & 3;
+            char* blk = s_a + ((q * CP + (gl >> 1)) * 4 + st) * ABLK;
+            const uint32_t sr[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                const uint32_t w[4] = {xr[rr].x, xr[rr].y, xr[rr].z, xr[rr].w};
                 uint16_t hi[8], lo[8];
-                float part = 0.0f;
 #pragma unroll
                 for (int o = 0; o < 8; ++o) {
-                    const float xv = ((o & 1) ? bf16_hi_to_f32(w[o >> 1]) : bf16_lo_to_f32(w[o >> 1]));
-                    const float xt = xv * is[o];
+                    const float xf = (o & 1) ? bf16_hi_to_f32(w[o >> 1]) : bf16_lo_to_f32(w[o >> 1]);
+                    const float xt = xf * __uint_as_float(sr[o]);
                     const __bf16 h = (__bf16)xt;
                     const __bf16 l = (__bf16)(xt - (float)h);
                     hi[slot_of(o)] = __builtin_bit_cast(uint16_t, h);
                     lo[slot_of(o)] = __builtin_bit_cast(uint16_t, l);
-                    part += (float)h + (float)l;
                 }
-                // items it .. it+7 (aligned) are one (row, group): fixed-order tree sum
-                part += __shfl_xor(part, 1);
-                part += __shfl_xor(part, 2);
-                part += __shfl_xor(part, 4);
-                if (live) {
-                    const int base = (((gl * 2 + ss) * 4 + pp) * M + m) * 8;
-                    *(uint4*)(s_a + base) = make_uint4(hi[0] | ((uint32_t)hi[1] << 16), hi[2] | ((uint32_t)hi[3] << 16),
-                                                       hi[4] | ((uint32_t)hi[5] << 16), hi[6] | ((uint32_t)hi[7] << 16));
-                    *(uint4*)(s_a + steps_c * 4 * M * 8 + base) =
-                        make_uint4(lo[0] | ((uint32_t)lo[1] << 16), lo[2] | ((uint32_t)lo[3] << 16),
-                                   lo[4] | ((uint32_t)lo[5] << 16), lo[6] | ((uint32_t)lo[7] << 16));
-                    if ((it & 7) == 0) s_xsum[gl * MAXM + m] = part;
-                }
+                *(uint4*)(blk + 16 * (pl * 8 + rr)) =
+                    make_uint4(pk(hi[0], hi[1]), pk(hi[2], hi[3]), pk(hi[4], hi[5]), pk(hi[6], hi[7]));
+                *(uint4*)(blk + 16 * (pl * 8 + 4 + rr)) =
+                    make_uint4(pk(lo[0], lo[1]), pk(lo[2], lo[3]), pk(lo[4], lo[5]), pk(lo[6], lo[7]));
             }
+        };
+        auto sprep = [&](const uint4& sb, const uint4& zb, int it) {
+            if (it >= sitems) return;
+            int ti, gl, h;
+            sitem(it, ti, gl, h);
+            const uint32_t sw[4] = {sb.x, sb.y, sb.z, sb.w}, zw[4] = {zb.x, zb.y, zb.z, zb.w};
+            float2* dst = s_so + gl * TC + ti * 16 + 8 * h;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const float sv = f16_bits_to_f32((uint16_t)(sw[j >> 1] >> (16 * (j & 1))));
+                const float zv = f16_bits_to_f32((uint16_t)(zw[j >> 1] >> (16 * (j & 1))));
+                dst[j] = make_float2(sv, 128.0f + zv);
+            }
+        };
+        // zero slots of the A blocks
+        for (int b = tid; b < NQ * np * 4; b += NT) {
+            const int q = b / (np * 4), rest = b - q * np * 4;
+            *(uint4*)(s_a + (q * CP * 4 + rest) * ABLK + 512) = make_uint4(0u, 0u, 0u, 0u);
+        }
+        xprep(xr0, xs0, xs1, tid);
+        sprep(sb0, zb0, tid);
+        sprep(sb1, zb1, tid + NT);
+        // larger M * K or more tiles: items beyond the ones loaded ahead
+        // (these loads queue behind the weight batch)
+        for (int it0 = NT; it0 < xitems; it0 += NT) {
+            uint4 xr[4], s0, s1;
+            xload(it0 + tid, xr, s0, s1);
+            xprep(xr, s0, s1, it0 + tid);
+        }
+        for (int it0 = 2 * NT; it0 < sitems; it0 += NT) {
+            uint4 sb, zb;
+            sload(it0 + tid, sb, zb);
+            sprep(sb, zb, it0 + tid);
         }
         __syncthreads();
 
-        auto compute = [&](const Batch& cur, int g0) {
+        // ---- 4. stream the tasks, pair by pair: the pair's A fragments are
+        // read once and serve its TPW tiles; X (the per-row group sums of
+        // hi + lo) comes from the same fragments times ones. No branch: pairs
+        // past the end get a zero scale and re-use valid data.
+        auto compute = [&](int j0) {
 #pragma unroll
-            for (int i = 0; i < BATCH; ++i) {
-                const int gl = g0 + i;
-                if (gl >= gc) break;
-                v4f d = {0.f, 0.f, 0.f, 0.f};
+            for (int jj = 0; jj < PB; ++jj) {
+                const bool live = j0 + jj < pe;                  // wave-uniform
+                const int pl = live ? j0 + jj : plast;
+                const int g = 2 * pl + eg;
+                v8bf a[NQ][4];
+                v4f xsum[NQ];
 #pragma unroll
-                for (int st = 0; st < 2; ++st) {
-                    const v8bf bq = codes_to_bf16(st ? cur.q[i].y : cur.q[i].x);
-                    v8bf ah, al;
-                    if (c < M) {
-                        const int base = (((gl * 2 + st) * 4 + p) * M + c) * 8;
-                        ah = *(const v8bf*)(s_a + base);
-                        al = *(const v8bf*)(s_a + steps_c * 4 * M * 8 + base);
-                    } else {
+                for (int q = 0; q < NQ; ++q) {
+                    v4f d = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                        for (int j = 0; j < 8; ++j) { ah[j] = (__bf16)0.0f; al[j] = (__bf16)0.0f; }
+                    for (int st = 0; st < 4; ++st) {
+                        a[q][st] = *(const v8bf*)(s_a + ((q * CP + pl) * 4 + st) * ABLK + aoff);
+                        d = mfma_bf16_16x16x32(a[q][st], ones, d);
                     }
-                    // A rows are activation rows (lane & 15), B columns are outputs
-                    d = mfma_bf16_16x16x32(ah, bq, d);
-                    d = mfma_bf16_16x16x32(al, bq, d);
-                }
-                const float sc = f16_bits_to_f32((uint16_t)(cur.sz[i] & 0xFFFFu));
-                const float off = 128.0f + f16_bits_to_f32((uint16_t)(cur.sz[i] >> 16));
-                const float4 xs = *(const float4*)(s_xsum + gl * MAXM + 4 * p);
-                const float xsv[4] = {xs.x, xs.y, xs.z, xs.w};
+                    // rows 4p..4p+3: lanes p and p ^ 2 hold the hi and lo sums of one group
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float t = __builtin_fmaf(-off, xsv[e], d[e]);
-                    acc[e] = __builtin_fmaf(sc, t, acc[e]);
+                    for (int e = 0; e < 4; ++e) xsum[q][e] = d[e] + __shfl_xor(d[e], 32);
+                }
+#pragma unroll
+                for (int ti = 0; ti < TPW; ++ti) {
+                    const uint4 qw = qv[jj * TPW + ti];
+                    const uint32_t qd[4] = {qw.x, qw.y, qw.z, qw.w};
+                    v8bf b[4];
+#pragma unroll
+                    for (int st = 0; st < 4; ++st) b[st] = codes_to_bf16(qd[st], magic);
+                    const float2 so = s_so[g * TC + ti * 16 + c];
+                    const float sc = live ? so.x : 0.0f;
+                    const float oe = so.y * omask;
+#pragma unroll
+                    for (int q = 0; q < NQ; ++q) {
+                        v4f d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                        for (int st = 0; st < 4; ++st) d = mfma_bf16_16x16x32(a[q][st], b[st], d);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const float t = __builtin_fmaf(-oe, xsum[q][e], d[e]);
+                            acc[ti][q][e] = __builtin_fmaf(sc, t, acc[ti][q][e]);
+                        }
+                    }
                 }
             }
         };
-        // even batches live in b0, odd ones in b1; each load runs one batch ahead
-        for (int g0 = 0; g0 < gc; g0 += 2 * BATCH) {
-            load_batch(b1, gbase + g0 + BATCH);
-            compute(b0, g0);
-            load_batch(b0, gbase + g0 + 2 * BATCH);
-            if (g0 + BATCH < gc) compute(b1, g0 + BATCH);
+        // The first batch (issued before the preparation) is consumed by
+        // straight-line code; more pairs continue in a loop whose loads are
+        // issued and consumed inside one iteration, so no in-flight register
+        // meets another in a merge (which would force an early full wait).
+        if (pe > ps) {                    // wave-uniform; a wave without pairs has nothing to add
+            compute(ps);
+            for (int j0 = ps + PB; j0 < pe; j0 += PB) {
+                load_batch(j0);
+                compute(j0);
+            }
         }
+        __syncthreads();                  // LDS reuse by the next chunk
     }
 
-    // C layout (16x16): lane holds column c, rows 4p + e
-    const float bv = bias ? bf16_lo_to_f32(bias[ncl]) : 0.0f;
+    // ---- 5. sum the 4 lanes of every column (hi/lo, both groups), then the
+    // NW parts of every (tile, row, column), in a fixed order
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        const int m = 4 * p + e;
-        if (m < M && n < N) y[(int64_t)m * N + n] = f32_to_bf16_bits(acc[e] + bv);
+    for (int t = 0; t < TPW; ++t)
+#pragma unroll
+        for (int q = 0; q < NQ; ++q)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                float v = acc[t][q][e];
+                v += __shfl_xor(v, 16);
+                v += __shfl_xor(v, 32);
+                if (p == 0) s_red[(((t * NW + wave) * NQ + q) * 4 + e) * 16 + c] = v;
+            }
+    __syncthreads();
+    for (int e = tid; e < TPW * NQ * 4 * 16; e += NT) {
+        const int cc = e & 15, r4 = (e >> 4) & 3, q = (e >> 6) & (NQ - 1), ti = e >> (6 + LNQ);
+        const int m = 4 * q + r4, nn = (t0 + ti) * 16 + cc;
+        float v = 0.0f;
+        for (int w = 0; w < NW; ++w) v += s_red[(((ti * NW + w) * NQ + q) * 4 + r4) * 16 + cc];
+        if (m < M && nn < N) {
+            const float bv = bias ? bf16_lo_to_f32(bias[nn]) : 0.0f;
+            y[(int64_t)m * N + nn] = f32_to_bf16_bits(v + bv);
+        }
+    }
+}
+
+template <int NQ, int TPW>
+void launch(const uint16_t* x, int M, int K, const float* inv_s, const uint8_t* qwt,
+            const uint16_t* scale, const uint16_t* zero, int N, const uint16_t* bias, uint16_t* y,
+            hipStream_t stream) {
+    static bool attr = false;
+    if (!attr) {
+        (void)hipFuncSetAttribute((const void*)gemv_w4a16_kernel<NQ, TPW>,
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BUDGET);
+        attr = true;
+    }
+    const int T = N / 16;
+    hipLaunchKernelGGL((gemv_w4a16_kernel<NQ, TPW>), dim3((unsigned)((T + TPW - 1) / TPW)), dim3(NT),
+                       LDS_BUDGET, stream, x, M, K, inv_s, qwt, scale, zero, N, bias, y);
+}
+
+template <int NQ>
+void launch_tpw(int tpw, const uint16_t* x, int M, int K, const float* inv_s, const uint8_t* qwt,
+                const uint16_t* scale, const uint16_t* zero, int N, const uint16_t* bias, uint16_t* y,
+                hipStream_t stream) {
+    switch (tpw) {
+        case 1: launch<NQ, 1>(x, M, K, inv_s, qwt, scale, zero, N, bias, y, stream); break;
+        case 2: launch<NQ, 2>(x, M, K, inv_s, qwt, scale, zero, N, bias, y, stream); break;
+        case 4: launch<NQ, 4>(x, M, K, inv_s, qwt, scale, zero, N, bias, y, stream); break;
+        case 5: launch<NQ, 5>(x, M, K, inv_s, qwt, scale, zero, N, bias, y, stream); break;
+        default: launch<NQ, 8>(x, M, K, inv_s, qwt, scale, zero, N, bias, y, stream); break;
     }
 }
 
 }  // namespace
 
-size_t gemv_smem_bytes(int M, int64_t K) {
-    const int KC = kchunk(M, K);
-    return (size_t)2 * (KC / 32) * 4 * M * 8 * 2 + sizeof(float) * (KC / 64) * MAXM;
+size_t gemv_smem_bytes(int, int64_t) { return LDS_BUDGET; }
+
+// tiles per workgroup: the smallest instantiated count that covers the tiles
+// with one workgroup per CU (more workgroups than CUs only past 8 tiles each)
+int gemv_tiles_per_wg(int64_t N, int cus) {
+    const int64_t T = N / 16;
+    const int64_t need = (T + cus - 1) / cus;
+    return need <= 1 ? 1 : need <= 2 ? 2 : need <= 4 ? 4 : need <= 5 ? 5 : MAXT;
 }
 
 hipError_t launch_gemv_w4a16(const uint16_t* x, int M, int64_t K, const float* inv_s,
-                             const uint8_t* qw, const uint16_t* scale, const uint16_t* zero,
-                             int64_t N, const uint16_t* bias, uint16_t* y, hipStream_t stream)
+                             const uint8_t* qwt, const uint16_t* scale, const uint16_t* zero,
+                             int64_t N, const uint16_t* bias, uint16_t* y, int cus, hipStream_t stream)
 {
-    const dim3 grid((unsigned)((N + COLS - 1) / COLS)), block(NT);
-    const size_t smem = gemv_smem_bytes(M, K);
-    if (smem > 65536)
-        (void)hipFuncSetAttribute((const void*)gemv_w4a16_kernel,
-                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-    hipLaunchKernelGGL(gemv_w4a16_kernel, grid, block, smem, stream,
-                       x, M, K, inv_s, qw, scale, zero, N, bias, y);
+    const int tpw = gemv_tiles_per_wg(N, cus);
+    switch (quads(M)) {
+        case 1: launch_tpw<1>(tpw, x, M, (int)K, inv_s, qwt, scale, zero, (int)N, bias, y, stream); break;
+        case 2: launch_tpw<2>(tpw, x, M, (int)K, inv_s, qwt, scale, zero, (int)N, bias, y, stream); break;
+        default: launch_tpw<4>(tpw, x, M, (int)K, inv_s, qwt, scale, zero, (int)N, bias, y, stream); break;
+    }
     return hipGetLastError();
 }

@@ -140,16 +140,25 @@ svdq_status svdq_gemm_w4a4_partials(const uint8_t* qx, int64_t M, int64_t K,
  *
  *  x          bf16 [M][K] (1 <= M <= 16, dense rows)
  *  inv_s      fp32 [K] reciprocal activation-aware channel scales, or NULL
- *  qw         [N][K/2] unsigned 4-bit codes
- *  scale_f16  fp16 [N][K/64];  zero_f16 fp16 [N][K/64] (integers 0..15)
+ *  qwt        unsigned 4-bit codes in the GEMV tile layout (format v1 AWQ):
+ *             [N/16][K/128][16][64 bytes]. Block (t, j, c) holds bytes
+ *             64j .. 64j + 63 of the plain packed row of column n = 16t + c
+ *             (the codes of groups 2j and 2j + 1; byte i of a plain row holds
+ *             element 2i in bits 0-3 and 2i + 1 in bits 4-7), so the 16
+ *             columns of a tile and one group pair form one contiguous 1 KB
+ *             block. This is a byte permutation of the plain [N][K/2] layout.
+ *  scale_f16  fp16 scales and zero_f16 fp16 zero points (integers 0..15),
+ *             both in the GEMV tile layout [N/16][K/64][16]: entry (t, g, c)
+ *             belongs to column 16t + c and group g.
  *  bias       bf16 [N] or NULL
  *  y          out: bf16 [M][N]
- * N % 16 == 0. Accumulation is fp32; the result matches the fp64 definition
- * to about 1e-5 relative before the bf16 rounding.
- * Alignment: x, inv_s, qw, y 16-byte aligned; scale/zero 4 bytes.
+ * N % 16 == 0, K % 128 == 0; qwt, scale and zero must each stay below 2 GiB.
+ * Accumulation is fp32; the result matches the fp64 definition to about 1e-5
+ * relative before the bf16 rounding.
+ * Alignment: x, inv_s, qwt, y 16-byte aligned; scale/zero 2 bytes.
  */
 svdq_status awq_gemv_w4a16(const void* x, int64_t M, int64_t K, const float* inv_s,
-                           const uint8_t* qw, const void* scale_f16, const void* zero_f16,
+                           const uint8_t* qwt, const void* scale_f16, const void* zero_f16,
                            int64_t N, const void* bias, void* y, void* stream);
 
 #ifdef __cplusplus

@@ -15,7 +15,11 @@ per-input-channel scale s_c folded into the weight:
   Y[m, n] = sum_k (fp32(x[m, k]) * inv_s[k]) (q - z) s + bias[n]   (fp64)
 
 Codes are unsigned nibbles, stored [N][K/2] with element 2i in the low nibble
-of byte i; scale and zero are fp16 [N][K/64].
+of byte i; scale and zero are fp16 [N][K/64]. The GEMV reads the codes in a
+tile layout, [N/16][K/128][16][64 bytes] (``tile_for_gemv``): block (t, j, c)
+is bytes 64j .. 64j + 63 of the plain row of column 16t + c; and the scales
+and zero points as [N/16][K/64][16] (``tile_scales_for_gemv``). Both are
+permutations and change no value.
 """
 from __future__ import annotations
 
@@ -38,6 +42,9 @@ class AwqWeights:
     scale: np.ndarray        # fp16 [N, K/64]
     zero: np.ndarray         # fp16 [N, K/64] (integers 0..15)
     bias: np.ndarray | None  # bf16 bits [N]
+    qwt: np.ndarray | None = None      # packed codes in the GEMV tile layout (K % 128 == 0)
+    scale_t: np.ndarray | None = None  # scale in the GEMV tile layout [N/16][K/64][16]
+    zero_t: np.ndarray | None = None   # zero point in the GEMV tile layout
 
 
 def qasym64(v: np.ndarray):
@@ -70,6 +77,40 @@ def unpack_u4(packed: np.ndarray) -> np.ndarray:
     return out
 
 
+def tile_for_gemv(packed: np.ndarray) -> np.ndarray:
+    """Plain packed rows [N][K/2] -> the tile layout [N/16][K/128][16][64] as a
+    flat byte array: block (t, j, c) = packed[16 t + c, 64 j : 64 j + 64]."""
+    p = np.asarray(packed, np.uint8)
+    N, half_k = p.shape
+    if N % 16 or half_k % 64:
+        raise ValueError("tile layout needs N % 16 == 0 and K % 128 == 0")
+    out = np.empty(N * half_k, np.uint8)
+    pos = 0
+    for t in range(N // 16):
+        for j in range(half_k // 64):
+            for c in range(16):
+                out[pos:pos + 64] = p[16 * t + c, 64 * j:64 * j + 64]
+                pos += 64
+    return out
+
+
+def tile_scales_for_gemv(a: np.ndarray) -> np.ndarray:
+    """Per-(column, group) values [N][G] -> the tile layout [N/16][G][16] as a
+    flat array: entry (t, g, c) = a[16 t + c, g]."""
+    a = np.asarray(a)
+    N, G = a.shape
+    if N % 16:
+        raise ValueError("tile layout needs N % 16 == 0")
+    out = np.empty(N * G, a.dtype)
+    pos = 0
+    for t in range(N // 16):
+        for g in range(G):
+            for c in range(16):
+                out[pos] = a[16 * t + c, g]
+                pos += 1
+    return out
+
+
 def prepare_awq(w_bits: np.ndarray, chan_scale, bias_bits=None) -> AwqWeights:
     w = bf16_bits_to_f32(w_bits)
     K, N = w.shape
@@ -81,8 +122,13 @@ def prepare_awq(w_bits: np.ndarray, chan_scale, bias_bits=None) -> AwqWeights:
     groups = np.ascontiguousarray(wp.T).reshape(N, K // GROUP, GROUP)
     s, z, q = qasym64(groups)
     codes = q.reshape(N, K)
-    return AwqWeights(K, N, inv_s, codes, pack_u4(codes), s, z,
-                      None if bias_bits is None else np.asarray(bias_bits, np.uint16))
+    packed = pack_u4(codes)
+    tiled = N % 16 == 0 and K % 128 == 0
+    return AwqWeights(K, N, inv_s, codes, packed, s, z,
+                      None if bias_bits is None else np.asarray(bias_bits, np.uint16),
+                      tile_for_gemv(packed) if tiled else None,
+                      tile_scales_for_gemv(s) if tiled else None,
+                      tile_scales_for_gemv(z) if tiled else None)
 
 
 def gemv(x_bits: np.ndarray, wts: AwqWeights) -> np.ndarray:

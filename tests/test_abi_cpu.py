@@ -100,7 +100,9 @@ def test_partials_rejects(lib, kw, status):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(M=0), SHAPE), (dict(M=17), SHAPE), (dict(N=40), SHAPE), (dict(K=48), SHAPE),
-    (dict(zero=None), NULL), (dict(x=A + 4), ALIGN),
+    (dict(K=192), SHAPE),                      # group pairs: K must be a multiple of 128
+    (dict(zero=None), NULL), (dict(x=A + 4), ALIGN), (dict(scale=C + 1), ALIGN),
+    (dict(N=1 << 20, K=4096), SHAPE),          # packed weights of 2 GiB: beyond 31-bit offsets
 ])
 def test_gemv_rejects(lib, kw, status):
     a = dict(x=A, M=4, K=256, inv=None, qw=B, scale=C, zero=D, N=64, bias=None, y=E)

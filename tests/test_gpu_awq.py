@@ -15,8 +15,10 @@ import bit_quantized_diffusion_svdq_amd as lib
 
 
 def run(x_bits, w):
-    return lib.awq_gemv(dev_u16(x_bits), dev(w.inv_s), dev(w.qw), dev_f16(w.scale), dev_f16(w.zero),
-                        dev_u16(w.bias) if w.bias is not None else None)
+    # the kernel reads codes, scales and zero points in the GEMV tile layout written by
+    # the oracle's packer
+    return lib.awq_gemv(dev_u16(x_bits), dev(w.inv_s), dev(w.qwt), dev_f16(w.scale_t), dev_f16(w.zero_t),
+                        dev_u16(w.bias) if w.bias is not None else None, N=w.N)
 
 
 def check(y, x_bits, w):
@@ -43,9 +45,13 @@ def test_awq_full_size():
     check(y, li.x, w)
 
 
-@pytest.mark.parametrize("M,K,N,scaled,bias", [(1, 64, 16, False, False), (16, 192, 48, True, True),
-                                               (16, 3072, 80, True, True),
-                                               (7, 2048 + 192, 32, True, False), (3, 4096, 64, True, True)])
+# row quads 1, 2 and 4; an odd number of group pairs (uneven K halves); more
+# than 24 pairs per K half (the batch loop); two LDS chunks (16 rows, K 3072);
+# partial workgroups (N not a multiple of 64)
+@pytest.mark.parametrize("M,K,N,scaled,bias", [(1, 128, 16, False, False), (16, 256, 48, True, True),
+                                               (16, 3072, 80, True, True), (5, 1024, 32, True, True),
+                                               (7, 2176, 32, True, False), (3, 8192, 64, True, True),
+                                               (2, 3072, 18432 - 64 * 3 + 16, True, True)])
 def test_awq_shapes(M, K, N, scaled, bias):
     note(f"awq gemv M={M} K={K} N={N}")
     rng = np.random.default_rng(M * 1000 + K)

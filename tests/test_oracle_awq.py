@@ -2,6 +2,7 @@
 import os
 
 import numpy as np
+import pytest
 
 import synth
 from oracle import awq, numfmt
@@ -115,3 +116,48 @@ def test_channel_scale_moves_into_weight():
     x = synth.make_matrix_bf16(2, K, seed=4)
     ref = numfmt.bf16_bits_to_f32(x).astype(np.float64) @ w.astype(np.float64)
     assert np.allclose(awq.gemv(x, wts), ref, rtol=0, atol=1e-12 * np.abs(ref).max())
+
+
+def test_tile_layout_spot_checks():
+    """The GEMV tile layout [N/16][K/128][16][64]: flat offset of block
+    (t, j, c), byte b is ((t * K/128 + j) * 16 + c) * 64 + b, and it holds byte
+    64 j + b of plain row 16 t + c. Each plain byte is made unique so a wrong
+    index shows; offsets below are worked out by hand for N = 32, K = 256."""
+    N, K = 32, 256
+    plain = np.arange(N * K // 2, dtype=np.int64).reshape(N, K // 2)
+    plain = (plain * 7 + plain // 251) % 256          # distinct neighbours, all bytes used
+    plain = plain.astype(np.uint8)
+    flat = awq.tile_for_gemv(plain)
+    assert flat.shape == (N * K // 2,)
+    # (t=0, j=0, c=0, b=0) -> offset 0, plain[0][0]
+    assert flat[0] == plain[0, 0]
+    # (t=0, j=0, c=1, b=0) -> offset 64, plain[1][0]
+    assert flat[64] == plain[1, 0]
+    # (t=0, j=1, c=0, b=0) -> offset (1 * 16) * 64 = 1024, plain[0][64]
+    assert flat[1024] == plain[0, 64]
+    # (t=1, j=1, c=3, b=5) -> ((1 * 2 + 1) * 16 + 3) * 64 + 5 = 3269, plain[19][69]
+    assert flat[3269] == plain[19, 69]
+    # last byte: (t=1, j=1, c=15, b=63) -> 4095, plain[31][127]
+    assert flat[4095] == plain[31, 127]
+    # a permutation: every plain byte appears exactly once
+    assert np.array_equal(np.sort(flat), np.sort(plain.ravel()))
+
+
+def test_tile_layout_rejects_ragged():
+    with pytest.raises(ValueError):
+        awq.tile_for_gemv(np.zeros((24, 64), np.uint8))
+    with pytest.raises(ValueError):
+        awq.tile_for_gemv(np.zeros((16, 96), np.uint8))
+
+
+def test_tile_scales_spot_checks():
+    """[N/16][G][16]: flat offset of (t, g, c) is (t * G + g) * 16 + c and holds
+    a[16 t + c, g]; offsets worked out by hand for N = 32, G = 3."""
+    a = (np.arange(32 * 3).reshape(32, 3) * 5 % 97).astype(np.float16)
+    f = awq.tile_scales_for_gemv(a)
+    assert f[0] == a[0, 0]                 # (0, 0, 0)
+    assert f[1] == a[1, 0]                 # (0, 0, 1)
+    assert f[16] == a[0, 1]                # (0, 1, 0)
+    assert f[(1 * 3 + 2) * 16 + 7] == a[23, 2]   # (1, 2, 7) -> 87
+    assert f[95] == a[31, 2]
+    assert np.array_equal(np.sort(f), np.sort(a.ravel()))
