@@ -20,9 +20,10 @@
 //    So one MFMA chain yields D = sum x~ (128 + q) of both groups, hi and lo
 //    parts apart, and every lane of the result is a useful number.
 //  - The zero point and the offset fold out through the per-(row, group)
-//    sum of x~:  Y += s (D_hi - (128 + z) X) + s D_lo, where X = sum (hi + lo)
-//    comes from the same A fragments times a matrix of ones on the MFMA, so
-//    it is the sum the MFMA itself sees.
+//    sums of x~: Y += s (D_hi - (128 + z) X_hi) + s (D_lo - (128 + z) X_lo),
+//    where X_hi, X_lo come from the same A fragments times a matrix of ones
+//    on the MFMA, so they are the sums the MFMA itself sees and each lane
+//    folds its own rows.
 //  - About one workgroup per CU: workgroup i owns TPW consecutive column
 //    tiles (TPW = 1, 2, 4, 5 or 8, template; 5 at 4 x 3072 -> 18432 on 256
 //    CUs) and prepares x~ = x inv_s (bf16 hi/lo in the A-operand order) and
@@ -123,7 +124,6 @@ __global__ __launch_bounds__(NT, 2) void gemv_w4a16_kernel(
     const int aoff = (((c >> 2) & 1) == (p >> 1)) ? 16 * (p * 8 + (c >> 3) * 4 + (c & 3)) : 512;
     // epilogue: lane (column c, p) holds result rows 4p..4p+3 = [lo/hi][group][row]
     const int eg = p & 1;                      // group of the pair this lane's result belongs to
-    const float omask = (p < 2) ? 1.0f : 0.0f; // the zero-point fold applies to the hi part only
     const int woff = c * 64 + 16 * p;          // + (tile * KP + pair) * 1024
 
     v4f acc[TPW][NQ];
@@ -180,27 +180,11 @@ __global__ __launch_bounds__(NT, 2) void gemv_w4a16_kernel(
         xload(tid, xr0, xs0, xs1);
         sload(tid, sb0, zb0);
         sload(tid + NT, sb1, zb1);
+        // keep these ahead of the weight loads: loads complete in issue order,
+        // so waiting for a preparation load must not wait for the weights
+        __builtin_amdgcn_sched_barrier(0);
 
-        // ---- 2. this wave's first batch of codes
-        uint4 qv[BT];
-        auto load_batch = [&](int j0) {                          // j0: first pair (chunk-local)
-#pragma unroll
-            for (int i = 0; i < BT; ++i) {
-                // task i: pair j0 + i / TPW, tile t0 + i % TPW; pairs past the end and
-                // tiles past N re-read valid data (clamped)
-                const int pl = (j0 + i / TPW < pe) ? j0 + i / TPW : plast;
-                const int pcl = pc0 + (pl < np ? pl : np - 1);
-                const int tt = t0 + i % TPW;
-                const int tcl = tt < T ? tt : T - 1;
-                // wave-uniform offset: keep it in an SGPR (a VGPR offset would turn
-                // each buffer load into a waterfall loop)
-                const int wb = __builtin_amdgcn_readfirstlane((tcl * KP + pcl) * 1024);
-                qv[i] = ld128(rw, woff, wb);
-            }
-        };
-        load_batch(ps);
-
-        // ---- 3. preparation into LDS: x~ = x inv_s as bf16 hi/lo in A-operand
+        // preparation into LDS: x~ = x inv_s as bf16 hi/lo in A-operand
         // order, and (scale, 128 + zero) per (group, column)
         auto xprep = [&](const uint4 (&xr)[4], const uint4& s0, const uint4& s1, int it) {
             if (it >= xitems) return;
@@ -241,16 +225,10 @@ __global__ __launch_bounds__(NT, 2) void gemv_w4a16_kernel(
                 dst[j] = make_float2(sv, 128.0f + zv);
             }
         };
-        // zero slots of the A blocks
-        for (int b = tid; b < NQ * np * 4; b += NT) {
-            const int q = b / (np * 4), rest = b - q * np * 4;
-            *(uint4*)(s_a + (q * CP * 4 + rest) * ABLK + 512) = make_uint4(0u, 0u, 0u, 0u);
-        }
-        xprep(xr0, xs0, xs1, tid);
-        sprep(sb0, zb0, tid);
-        sprep(sb1, zb1, tid + NT);
-        // larger M * K or more tiles: items beyond the ones loaded ahead
-        // (these loads queue behind the weight batch)
+        // larger M * K or more tiles: items beyond the ones loaded ahead,
+        // prepared before any weight load is issued (waiting for them then
+        // never waits for the weight stream, and no control-flow merge
+        // happens while weights are in flight)
         for (int it0 = NT; it0 < xitems; it0 += NT) {
             uint4 xr[4], s0, s1;
             xload(it0 + tid, xr, s0, s1);
@@ -261,6 +239,37 @@ __global__ __launch_bounds__(NT, 2) void gemv_w4a16_kernel(
             sload(it0 + tid, sb, zb);
             sprep(sb, zb, it0 + tid);
         }
+
+        // ---- 2. this wave's first batch of codes
+        uint4 qv[BT];
+        auto load_batch = [&](int j0) {                          // j0: first pair (chunk-local)
+#pragma unroll
+            for (int i = 0; i < BT; ++i) {
+                // task i: pair j0 + i / TPW, tile t0 + i % TPW; pairs past the end and
+                // tiles past N re-read valid data (clamped)
+                const int pl = (j0 + i / TPW < pe) ? j0 + i / TPW : plast;
+                const int pcl = pc0 + (pl < np ? pl : np - 1);
+                const int tt = t0 + i % TPW;
+                const int tcl = tt < T ? tt : T - 1;
+                // wave-uniform offset: keep it in an SGPR (a VGPR offset would turn
+                // each buffer load into a waterfall loop)
+                const int wb = __builtin_amdgcn_readfirstlane((tcl * KP + pcl) * 1024);
+                qv[i] = ld128(rw, woff, wb);
+                __builtin_amdgcn_sched_barrier(0);     // issue in task order (= consumption order)
+            }
+        };
+        load_batch(ps);
+        __builtin_amdgcn_sched_barrier(0);
+
+        // ---- 3. preparation into LDS (first items)
+        // zero slots of the A blocks
+        for (int b = tid; b < NQ * np * 4; b += NT) {
+            const int q = b / (np * 4), rest = b - q * np * 4;
+            *(uint4*)(s_a + (q * CP * 4 + rest) * ABLK + 512) = make_uint4(0u, 0u, 0u, 0u);
+        }
+        xprep(xr0, xs0, xs1, tid);
+        sprep(sb0, zb0, tid);
+        sprep(sb1, zb1, tid + NT);
         __syncthreads();
 
         // ---- 4. stream the tasks, pair by pair: the pair's A fragments are
@@ -283,9 +292,9 @@ __global__ __launch_bounds__(NT, 2) void gemv_w4a16_kernel(
                         a[q][st] = *(const v8bf*)(s_a + ((q * CP + pl) * 4 + st) * ABLK + aoff);
                         d = mfma_bf16_16x16x32(a[q][st], ones, d);
                     }
-                    // rows 4p..4p+3: lanes p and p ^ 2 hold the hi and lo sums of one group
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) xsum[q][e] = d[e] + __shfl_xor(d[e], 32);
+                    // rows 4p..4p+3 of this lane: the hi (p < 2) or lo (p >= 2) part
+                    // of its group's row sums, folded against the same part of D
+                    xsum[q] = d;
                 }
 #pragma unroll
                 for (int ti = 0; ti < TPW; ++ti) {
@@ -296,7 +305,7 @@ __global__ __launch_bounds__(NT, 2) void gemv_w4a16_kernel(
                     for (int st = 0; st < 4; ++st) b[st] = codes_to_bf16(qd[st], magic);
                     const float2 so = s_so[g * TC + ti * 16 + c];
                     const float sc = live ? so.x : 0.0f;
-                    const float oe = so.y * omask;
+                    const float oe = so.y;
 #pragma unroll
                     for (int q = 0; q < NQ; ++q) {
                         v4f d = {0.f, 0.f, 0.f, 0.f};
@@ -309,6 +318,9 @@ __global__ __launch_bounds__(NT, 2) void gemv_w4a16_kernel(
                         }
                     }
                 }
+                // consume pairs in load order (the tiles of one pair interleave freely):
+                // the scheduler does not know that later loads arrive later
+                __builtin_amdgcn_sched_barrier(0);
             }
         };
         // The first batch (issued before the preparation) is consumed by
