@@ -25,15 +25,27 @@ namespace {
 constexpr int ROWS = 16;
 constexpr int WAVES = 8;
 
-// Quantise one lane's 16 values of a group: returns packed nibbles (8 bytes)
-// given the group's fp32 reciprocal `inv` (0 when the scale is 0).
-DEV uint32_t code_nibble(float v, float inv) {
+// Quantise one value given the group's fp32 reciprocal `inv` (0 when the
+// scale is 0) and return its FP6 E2M3 field: magnitude in bits 0-2, zero
+// exponent, sign in bit 5 (zero is stored with sign 0).
+DEV uint32_t code_field(float v, float inv) {
     float t = v * inv;                         // one fp32 multiply (no contraction)
     t = __builtin_rintf(t);                    // round half to even
     t = fminf(fmaxf(t, -7.0f), 7.0f);
     uint32_t mag = (uint32_t)(int)fabsf(t);
-    uint32_t sgn = (__float_as_uint(t) >> 28) & 8u;   // sign bit -> bit 3
+    uint32_t sgn = (__float_as_uint(t) >> 26) & 32u;  // sign bit -> bit 5
     return (t != 0.0f) ? (mag | sgn) : 0u;
+}
+
+// Sixteen E2M3 fields (code e at bits 6e..6e+5 of a 96-bit stream T) -> the
+// 64-bit storage word: T[0:32) and T[64:96) keep their places, and the bits of
+// T[32:64) go into the zero exponent positions of those two thirds
+// (0x18618618 in the low word, 0x61861861 in the high word).
+DEV uint2 fold_fields(const uint32_t (&f)[16]) {
+    const uint32_t d0 = f[0] | (f[1] << 6) | (f[2] << 12) | (f[3] << 18) | (f[4] << 24) | (f[5] << 30);
+    const uint32_t d1 = (f[5] >> 2) | (f[6] << 4) | (f[7] << 10) | (f[8] << 16) | (f[9] << 22) | (f[10] << 28);
+    const uint32_t d2 = (f[10] >> 4) | (f[11] << 2) | (f[12] << 8) | (f[13] << 14) | (f[14] << 20) | (f[15] << 26);
+    return make_uint2(d0 | (d1 & 0x18618618u), d2 | (d1 & 0x61861861u));
 }
 
 template <int RT>   // RT = rank / 16 (0..8)
@@ -104,14 +116,12 @@ __global__ __launch_bounds__(ROWS * 32) void act_quant_kernel(
         const float sf = (float)s16;
         const float inv = (sf > 0.0f) ? 1.0f / sf : 0.0f;
 
-        uint32_t pk0 = 0, pk1 = 0;
+        uint32_t f[16];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            pk0 |= code_nibble(v[j], inv) << (4 * j);
-            pk1 |= code_nibble(v[8 + j], inv) << (4 * j);
-        }
+        for (int j = 0; j < 16; ++j) f[j] = code_field(v[j], inv);
+        const uint2 word = fold_fields(f);
         if (valid) {
-            *(uint2*)(qx + row * (K / 2) + g * 32 + 8 * p) = make_uint2(pk0, pk1);
+            *(uint2*)(qx + row * (K / 2) + g * 32 + 8 * p) = word;
             if (p == 0) s_sx[r * G + g] = __builtin_bit_cast(uint16_t, s16);
         }
 

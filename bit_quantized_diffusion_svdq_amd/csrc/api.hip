@@ -113,6 +113,14 @@ svdq_status check_k(int64_t K) {
     return SVDQ_OK;
 }
 
+// the GEMM addresses the packed codes and scales with 31-bit byte offsets
+svdq_status check_gemm_bytes(int64_t M, int64_t N, int64_t K) {
+    const int64_t lim = (int64_t)1 << 31;
+    if (M * (K / 2) >= lim || N * (K / 2) >= lim)
+        return fail(SVDQ_ERR_SHAPE, "M * K / 2 and N * K / 2 must stay below 2^31 bytes");
+    return SVDQ_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -132,7 +140,7 @@ const char* svdq_status_string(svdq_status s) {
 
 const char* svdq_last_error(void) { return g_last_error.c_str(); }
 
-int svdq_version(void) { return 100; }
+int svdq_version(void) { return 200; }
 
 svdq_status svdq_check_device(int device) {
     svdq_status s = check_device_id(device);
@@ -177,6 +185,7 @@ svdq_status svdq_gemm_w4a4(const uint8_t* qx, const void* sx_f16, int64_t M, int
     if ((s = check_rank(rank)) != SVDQ_OK) return s;
     if (N <= 0 || N % 8) return fail(SVDQ_ERR_SHAPE, "N = %lld must be a positive multiple of 8", (long long)N);
     if (M > ((int64_t)1 << 31) || N > ((int64_t)1 << 31)) return fail(SVDQ_ERR_SHAPE, "M or N too large");
+    if ((s = check_gemm_bytes(M, N, K)) != SVDQ_OK) return s;
     if (ldy < N) return fail(SVDQ_ERR_SHAPE, "ldy = %lld < N = %lld", (long long)ldy, (long long)N);
     if (ldy % 8) return fail(SVDQ_ERR_ALIGN, "ldy = %lld must be a multiple of 8", (long long)ldy);
     if (act != SVDQ_ACT_NONE && act != SVDQ_ACT_GELU_TANH)
@@ -205,6 +214,7 @@ svdq_status svdq_gemm_w4a4_partials(const uint8_t* qx, int64_t M, int64_t K,
     svdq_status s;
     if ((s = check_k(K)) != SVDQ_OK) return s;
     if (M < 0 || N <= 0 || N % 8) return fail(SVDQ_ERR_SHAPE, "bad M or N");
+    if ((s = check_gemm_bytes(M, N, K)) != SVDQ_OK) return s;
     if (m0 < 0 || mcount < 0 || m0 + mcount > M || n0 < 0 || ncount < 0 || n0 + ncount > N)
         return fail(SVDQ_ERR_SHAPE, "rectangle outside the M x N output");
     if (mcount == 0 || ncount == 0) { g_last_error.clear(); return SVDQ_OK; }

@@ -6,10 +6,12 @@
 
 typedef int v2i __attribute__((ext_vector_type(2)));
 typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v6i __attribute__((ext_vector_type(6)));
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef _Float16 v4h __attribute__((ext_vector_type(4)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 
 #define DEV __device__ __forceinline__
@@ -36,13 +38,30 @@ DEV uint32_t pack_bf16x2(float lo, float hi) {
 
 DEV float f16_bits_to_f32(uint16_t h) { return (float)__builtin_bit_cast(_Float16, h); }
 
-// D = A(32x64 fp8) * B(64x32 fp8) + C, fp32 accumulate. Both operands carry
-// INT4 codes as E4M3 subnormals (value q * 2^-9, see int4sm_to_fp8); the
-// E8M0 block scale 2^9 (0x88) on each side turns the products back into
-// exact integer products, so the result is the exact integer dot product.
-DEV v16f mfma_f8_32x32x64(const v8i& a, const v8i& b, const v16f& c) {
-    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0x88888888, 0, 0x88888888);
+// D = A(32x64) * B(64x32) + C with both operands FP6 E2M3 (cbsz = blgp = 2):
+// 32 six-bit fields per lane packed at 6-bit strides in 6 dwords. A 4-bit code q is the E2M3 subnormal q / 8
+// (zero exponent) and the E8M0 block scale 2^3 (0x82) on each side restores
+// q_a * q_w, so the fp32 result is the exact integer dot product (|sum| <= 3136).
+DEV v16f mfma_fp6_32x32x64(const v6i& a, const v6i& b, const v16f& c) {
+    const v8i a8 = __builtin_shufflevector(a, a, 0, 1, 2, 3, 4, 5, -1, -1);
+    const v8i b8 = __builtin_shufflevector(b, b, 0, 1, 2, 3, 4, 5, -1, -1);
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, b8, c, 2, 2, 0, 0x82828282, 0, 0x82828282);
 }
+
+// Empty register ties: they emit no instruction, but code that uses the
+// value afterwards cannot be scheduled above them, which keeps independent
+// MFMAs in program order instead of being hoisted (and their results kept
+// live) by the compiler.
+template <class T>
+DEV void order_point(T& x) { asm volatile("" : "+v"(x)); }
+template <class T, class U>
+DEV void order_point(T& x, U& y) { asm volatile("" : "+v"(x), "+v"(y)); }
+
+// Workgroup barrier for LDS traffic only: waits for this wave's LDS accesses
+// (lgkmcnt) but, unlike __syncthreads(), not for its outstanding global
+// loads, so prefetches stay in flight across it. The memory clobber keeps
+// the compiler from moving memory accesses across the barrier.
+DEV void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // D = A(16x32 bf16) * B(32x16 bf16) + C
 DEV v4f mfma_bf16_16x16x32(const v8bf& a, const v8bf& b, const v4f& c) {
@@ -54,21 +73,20 @@ DEV v16f mfma_bf16_32x32x16(const v8bf& a, const v8bf& b, const v16f& c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// D = A(32x16 f16) * B(16x32 f16) + C
-DEV v16f mfma_f16_32x32x16(const v8h& a, const v8h& b, const v16f& c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+// D = A(32x8 f16) * B(8x32 f16) + C (same issue cost as the 32x32x16 form
+// on gfx950, half the operand registers)
+DEV v16f mfma_f16_32x32x8(const v4h& a, const v4h& b, const v16f& c) {
+    return __builtin_amdgcn_mfma_f32_32x32x8f16(a, b, c, 0, 0, 0);
 }
 
-// Eight sign-magnitude INT4 codes (one dword, element 2i in the low nibble of
-// byte i) -> eight FP8 E4M3 bytes. A code s|m (sign bit, magnitude 0..7)
-// becomes the E4M3 subnormal s|0000|m, whose value is (-1)^s * m * 2^-9, so
-// the byte is just the magnitude bits with the sign moved to bit 7.
-// lo: bytes = elements 0,2,4,6; hi: bytes = elements 1,3,5,7. Operands A and
-// B are expanded the same way, so the K order inside an MFMA is permuted
-// identically on both sides and every dot product is unchanged.
-DEV void int4sm_to_fp8(uint32_t x, uint32_t& lo, uint32_t& hi) {
-    lo = (x & 0x07070707u) | ((x << 4) & 0x80808080u);
-    hi = ((x >> 4) & 0x07070707u) | (x & 0x80808080u);
+// One stored 64-bit word of 16 codes (x0 = bits 0-31, x1 = bits 32-63) -> the
+// three dwords of its E2M3 operand stream. The word keeps stream dwords 0 and
+// 2 in place and carries stream dword 1 in their zero exponent fields, at
+// 0x18618618 (low word) and 0x61861861 (high word).
+DEV void unfold_fp6(uint32_t x0, uint32_t x1, uint32_t& d0, uint32_t& d1, uint32_t& d2) {
+    d0 = x0 & ~0x18618618u;
+    d1 = (x0 & 0x18618618u) | (x1 & 0x61861861u);
+    d2 = x1 & ~0x61861861u;
 }
 
 DEV float gelu_tanh_f32(float y) {

@@ -4,20 +4,26 @@
 // The pages attribute to the original engine a fusion of the low-rank
 // up-projection with the 4-bit matmul (remio.ai page, section "SVDQuant moves
 // hard values out of 4-bit"). The CDNA4 design:
-//  - INT4 codes in [-7, 7] are exact FP8 E4M3 subnormals (q * 2^-9), and the
-//    E8M0 block scales of v_mfma_scale_f32_32x32x64_f8f6f4 undo the 2^-9 on
-//    both sides, so one MFMA forms one 64-wide group's integer partial P_g
-//    exactly in fp32 (no int->float conversion);
-//  - the two-sided scale S = sx (x) sw of a 32x32 block is an outer product;
-//    a v_mfma_f32_32x32x16_f16 with a single non-zero k forms it exactly
-//    (fp16 x fp16 fits fp32), so the matrix pipe, not the VALU, builds it and
-//    the VALU does one FMA per output element per group: acc += P_g * S_g;
-//  - packed nibbles are expanded to FP8 once per workgroup while a group is
-//    staged into LDS, in MFMA lane order, so each wave reads a 32x64 operand
-//    fragment as contiguous 1 KB runs; raw packed data is prefetched three
-//    groups ahead in registers;
-//  - the tile shape is a template parameter; tiles are swizzled so each XCD
-//    (own L2) works on compact groups of tiles;
+//  - INT4 codes in [-7, 7] are exact FP6 E2M3 subnormals (q / 8); with the
+//    E8M0 block scale 2^3 on both sides one v_mfma_scale_f32_32x32x64_f8f6f4
+//    (FP6 operands run at twice the FP8 rate) forms one 64-wide group's
+//    integer partial P_g exactly in fp32;
+//  - the stored 4-bit word is the E2M3 operand stream with its zero exponent
+//    fields folded out, so a wave turns 16 codes into FP6 with four bit
+//    operations right before its MFMAs;
+//  - packed rows travel from global memory straight into LDS (buffer loads
+//    with an LDS destination), two groups = 64 contiguous bytes per row at a
+//    time, into a ring of three pair slots filled two steps ahead, with no
+//    registers held; every lane's 16 bytes land where the lane that consumes
+//    them in the MFMA reads them;
+//  - the two-sided scale S = sx (x) sw of a 32x32 block is an outer product
+//    that a v_mfma_f32_32x32x8_f16 with one non-zero k forms exactly; the
+//    scales arrive in LDS as the zero-extended first register of that
+//    operand (lanes 32..63 read zero), and the VALU does one FMA per output
+//    element and group, acc += P_g * S_g;
+//  - products and scale products of consecutive blocks alternate between two
+//    register sets, so a block's FMAs run while the next block's MFMAs do;
+//  - tiles are swizzled so each XCD (own L2) works on compact groups of tiles;
 //  - the accumulator starts from X_hat L1 L2 (bf16 MFMA on the hi/lo split of
 //    the fp32 xl1); bias and GELU run in fp32 before the single rounding of
 //    the output, which leaves through LDS as row-contiguous 16-byte stores.
@@ -25,133 +31,55 @@
 
 namespace {
 
-constexpr int FRAG_DW = 8;                   // a 32x64 fp8 fragment: 8 dwords per lane
-
-template <int BM_, int BN_, int WGM_, int WGN_, int MINB_>
+template <int BM_, int BN_, int WGM_, int WGN_>
 struct Cfg {
-    static constexpr int BM = BM_, BN = BN_, WGM = WGM_, WGN = WGN_, MINB = MINB_;
+    static constexpr int BM = BM_, BN = BN_, WGM = WGM_, WGN = WGN_;
     static constexpr int NW = WGM * WGN, NT = 64 * NW;
     static constexpr int TM = BM / 32 / WGM, TN = BN / 32 / WGN;     // 32x32 blocks per wave
-    static constexpr int ABLK = BM / 32, BBLK = BN / 32;
-    static constexpr int NA = (ABLK + NW - 1) / NW, NB = (BBLK + NW - 1) / NW;  // blocks staged per wave
-    static constexpr int A_DW = ABLK * 64 * FRAG_DW, B_DW = BBLK * 64 * FRAG_DW;
-    static constexpr int STAGE_BYTES = 4 * (A_DW + B_DW) + 2 * 64 * (ABLK + BBLK);  // scales [blk][64]
-    static constexpr int OUT_LD = BN + 8;
-    static constexpr int OUT_BYTES = BM * OUT_LD * 2;
-    static constexpr int SMEM_BYTES = (2 * STAGE_BYTES > OUT_BYTES) ? 2 * STAGE_BYTES : OUT_BYTES;
+    static constexpr int ABLK = BM / 32, BBLK = BN / 32, SBLK = ABLK + NW;
+    // One pair slot (two groups): codes [group][block][lane][16 B], then
+    // scale operands [group][block][lane][4 B]; blocks are the ABLK A blocks,
+    // then one B slot per wave (waves w >= BBLK fill theirs with a copy that
+    // nobody reads, so every wave issues the same loads).
+    static constexpr int CODES = 2 * SBLK * 1024, SLOT = CODES + 2 * SBLK * 256;
+    // bf16 output staging for the epilogue: OUT_ROWS rows at a time in slot 0
+    static constexpr int OUT_LD = BN + 8, OUT_ROWS = 32 * TM;
     static_assert(TM * 32 * WGM == BM && TN * 32 * WGN == BN, "tile shape");
+    static_assert(ABLK <= NW && BBLK <= NW, "one loaded block per wave and operand");
+    static_assert((TM * TN) % 2 == 0, "blocks per wave must be even for the register rotation");
+    static_assert(OUT_ROWS * OUT_LD * 2 <= SLOT, "epilogue staging fits one slot");
+    static_assert(3 * SLOT <= 160 * 1024, "LDS budget");
 };
 
 // the QKV-sized configuration: 256 x 192 tiles, 8 waves (4 x 2) of 64 x 96,
-// one workgroup per CU; 4096 x 9216 is 768 tiles = 3 per CU. (Two 4-wave
-// workgroups of 128 x 192 per CU measured 1.5x slower: the smaller tile
-// stages more bytes per MAC and needs two B staging slots per wave.)
-using MainCfg = Cfg<256, 192, 4, 2, 1>;
+// one workgroup per CU; 4096 x 9216 is 768 tiles = 3 per CU.
+using MainCfg = Cfg<256, 192, 4, 2>;
 
 DEV int out_row(int i, int lane) { return 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3); }
 
-template <class C>
-struct Raw {
-    uint4 a[C::NA], b[C::NB];
-    uint32_t sa[C::NA], sb[C::NB];
-};
+typedef __attribute__((address_space(3))) void lds_void;
 
-struct Stage {
-    uint32_t* A;
-    uint32_t* B;
-    uint16_t* SA;
-    uint16_t* SB;
-};
-
-template <class C>
-DEV Stage stage_ptr(char* smem, int s) {
-    char* base = smem + s * C::STAGE_BYTES;
-    Stage st;
-    st.A = (uint32_t*)base;
-    st.B = st.A + C::A_DW;
-    st.SA = (uint16_t*)(st.B + C::B_DW);
-    st.SB = st.SA + 64 * C::ABLK;
-    return st;
+// 16 bytes per lane from global memory into LDS at lds + 16 * lane
+DEV void dma16(rsrc_t r, char* lds, int voff, int soff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, voff, soff, 0, 0);
 }
 
-// Per-thread staging sources. Wave w stages the 32-row blocks w, w + NW, ...
-// of the A tile and of the B tile; lane l takes row l % 32 of a block and half
-// l / 32 of that row's 32 packed bytes, which is exactly the lane that
-// consumes those codes in the MFMA, so fragments are written and read as
-// contiguous 1 KB runs (no LDS bank conflicts). Rows past the end are clamped
-// to the last row: what they load only reaches output rows or columns that
-// are never stored.
-template <class C>
-struct Src {
-    const uint8_t* a[C::NA];
-    const uint8_t* b[C::NB];
-    const uint16_t* sa[C::NA];
-    const uint16_t* sb[C::NB];
-};
-
-template <class C, bool SCALES>
-DEV void load_raw(Raw<C>& r, const Src<C>& src, int g) {
-#pragma unroll
-    for (int t = 0; t < C::NA; ++t) {
-        r.a[t] = *(const uint4*)(src.a[t] + (int64_t)g * 32);
-        r.sa[t] = SCALES ? src.sa[t][g] : 0u;
-    }
-#pragma unroll
-    for (int t = 0; t < C::NB; ++t) {
-        r.b[t] = *(const uint4*)(src.b[t] + (int64_t)g * 32);
-        r.sb[t] = SCALES ? src.sb[t][g] : 0u;
-    }
+// 2 bytes per lane into the low half of the dword at lds + 4 * lane (the
+// high half is zeroed; lanes whose offset is out of range get 0)
+DEV void dma2(rsrc_t r, char* lds, int voff, int soff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 2, voff, soff, 0, 0);
 }
 
-// Fragment layout in LDS: [block][half j][lane][16 bytes]; lane l of block b
-// holds the 32 fp8 codes of row 32b + l % 32, k half l / 32.
-DEV void expand_store(const uint4& raw, uint32_t* __restrict__ tile, int blk, int lane) {
-    uint32_t o[8];
-    int4sm_to_fp8(raw.x, o[0], o[1]);
-    int4sm_to_fp8(raw.y, o[2], o[3]);
-    int4sm_to_fp8(raw.z, o[4], o[5]);
-    int4sm_to_fp8(raw.w, o[6], o[7]);
-    *(uint4*)(tile + ((blk * 2 + 0) * 64 + lane) * 4) = make_uint4(o[0], o[1], o[2], o[3]);
-    *(uint4*)(tile + ((blk * 2 + 1) * 64 + lane) * 4) = make_uint4(o[4], o[5], o[6], o[7]);
-}
-
-template <class C>
-DEV void store_raw(const Raw<C>& r, const Stage& st, int wave, int lane) {
-#pragma unroll
-    for (int t = 0; t < C::NA; ++t) {
-        const int blk = wave + t * C::NW;
-        if (C::NA * C::NW == C::ABLK || blk < C::ABLK) {
-            expand_store(r.a[t], st.A, blk, lane);
-            if (lane < 32) st.SA[blk * 64 + lane] = (uint16_t)r.sa[t];
-        }
-    }
-#pragma unroll
-    for (int t = 0; t < C::NB; ++t) {
-        const int blk = wave + t * C::NW;
-        if (C::NB * C::NW == C::BBLK || blk < C::BBLK) {
-            expand_store(r.b[t], st.B, blk, lane);
-            if (lane < 32) st.SB[blk * 64 + lane] = (uint16_t)r.sb[t];
-        }
-    }
-}
-
-DEV v8i read_frag(const uint32_t* __restrict__ tile, int blk, int lane) {
-    const uint4 a = *(const uint4*)(tile + ((blk * 2 + 0) * 64 + lane) * 4);
-    const uint4 b = *(const uint4*)(tile + ((blk * 2 + 1) * 64 + lane) * 4);
-    return v8i{(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)b.x, (int)b.y, (int)b.z, (int)b.w};
-}
-
-// Operand of the outer-product MFMA: only k = 0 (element 0 of lanes 0..31) is
-// non-zero (lanes 32..63 read the zero half of the scale row); A and B share
-// the k layout, so the product is s_row * s_col. The zero registers of the
-// tuple stay in place across groups.
-DEV v8h scale_operand(v4i& t, const uint16_t* __restrict__ srow, int lane) {
-    t[0] = (int)srow[lane];
-    return __builtin_bit_cast(v8h, t);
+// 16 raw bytes (two stored words) -> the lane's FP6 fragment (6 dwords)
+DEV v6i unfold_frag(const uint4& raw) {
+    uint32_t d[6];
+    unfold_fp6(raw.x, raw.y, d[0], d[1], d[2]);
+    unfold_fp6(raw.z, raw.w, d[3], d[4], d[5]);
+    return v6i{(int)d[0], (int)d[1], (int)d[2], (int)d[3], (int)d[4], (int)d[5]};
 }
 
 template <class C, int MODE, int ACT>   // MODE 0: bf16 out, 1: fp32 out, 2: integer partials dump
-__global__ __launch_bounds__(C::NT, C::MINB) void gemm_w4a4_kernel(
+__global__ __launch_bounds__(C::NT, 1) void gemm_w4a4_kernel(
     const uint8_t* __restrict__ qx, const uint16_t* __restrict__ sx,
     const uint8_t* __restrict__ qw, const uint16_t* __restrict__ sw,
     const float* __restrict__ xl1, const uint16_t* __restrict__ l2t, int rank,
@@ -160,8 +88,14 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_w4a4_kernel(
     int64_t pm0, int64_t pmc, int64_t pn0, int64_t pnc, int32_t* __restrict__ part)
 {
     constexpr int BM = C::BM, BN = C::BN, TM = C::TM, TN = C::TN, NT = C::NT;
-    extern __shared__ __attribute__((aligned(16))) char smem[];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // three pair slots as separate objects: the compiler then tracks each
+    // slot's outstanding LDS-destination loads on its own and makes reads of
+    // one slot wait only for loads into that slot
+    __shared__ __attribute__((aligned(16))) char slot0[C::SLOT];
+    __shared__ __attribute__((aligned(16))) char slot1[C::SLOT];
+    __shared__ __attribute__((aligned(16))) char slot2[C::SLOT];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / C::WGN, wn = wave % C::WGN;
 
     // tile index: blocks are dealt round-robin to the 8 XCDs; consecutive
@@ -185,28 +119,55 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_w4a4_kernel(
     const int64_t n0 = (MODE == 2 ? pn0 : 0) + (int64_t)tn * BN;
     const int64_t mlim = (MODE == 2) ? pm0 + pmc : M;
     const int64_t nlim = (MODE == 2) ? pn0 + pnc : N;
-    const int G = (int)(K / 64);
+    const int G = (int)(K / 64), NP = (G + 1) / 2;   // groups, group pairs
 
-    Src<C> src;
-    {
-        const int half = lane >> 5;
-#pragma unroll
-        for (int u = 0; u < C::NA; ++u) {
-            const int blk = (wave + u * C::NW) % C::ABLK;
-            const int64_t r = m0 + blk * 32 + (lane & 31);
-            const int64_t ra = r < mlim ? r : mlim - 1;
-            src.a[u] = qx + ra * (K / 2) + 16 * half;
-            src.sa[u] = (MODE != 2) ? sx + ra * G : nullptr;
+    // Loading: wave w loads block w of the A tile and block w % BBLK of the
+    // B tile; lane l takes row l % 32 and half l / 32 of each group of
+    // that row, which is where the lane that consumes those codes in the MFMA
+    // reads them. Scale loads go to lanes 0..31 (lanes 32..63 get an out-of-
+    // range offset, hence 0). Rows past the end are clamped to the last row:
+    // what they load only reaches output rows or columns that are never
+    // stored. Byte offsets fit in 31 bits (checked on the host).
+    const int half = lane >> 5;
+    int64_t ra = m0 + (int64_t)(wave % C::ABLK) * 32 + (lane & 31);
+    int64_t rb = n0 + (int64_t)(wave % C::BBLK) * 32 + (lane & 31);
+    ra = ra < mlim ? ra : mlim - 1;
+    rb = rb < nlim ? rb : nlim - 1;
+    const rsrc_t rqa = make_rsrc(qx, M * (K / 2));
+    const rsrc_t rqb = make_rsrc(qw, N * (K / 2));
+    const rsrc_t rsa = make_rsrc(sx, (MODE != 2) ? M * G * 2 : 0);
+    const rsrc_t rsb = make_rsrc(sw, (MODE != 2) ? N * G * 2 : 0);
+    const int va = (int)(ra * (K / 2)) + 16 * half, vb = (int)(rb * (K / 2)) + 16 * half;
+    constexpr int OUT_OF_RANGE = 0x7FFFFFF0;
+    const int vsa = half ? OUT_OF_RANGE : (int)(ra * G * 2);
+    const int vsb = half ? OUT_OF_RANGE : (int)(rb * G * 2);
+
+    // pair q into a slot (pair indices past the end are clamped; groups past
+    // the end get a zero scale operand where they are read).
+    auto load_pair = [&](char* sl, int q) {
+        q = q < NP ? q : NP - 1;
+        const int so = q * 64, ss = q * 4;
+        dma16(rqa, sl + (0 * C::SBLK + wave) * 1024, va, so);
+        dma16(rqa, sl + (1 * C::SBLK + wave) * 1024, va + 32, so);
+        if constexpr (MODE != 2) {
+            dma2(rsa, sl + C::CODES + (0 * C::SBLK + wave) * 256, vsa, ss);
+            dma2(rsa, sl + C::CODES + (1 * C::SBLK + wave) * 256, vsa + 2, ss);
         }
-#pragma unroll
-        for (int u = 0; u < C::NB; ++u) {
-            const int blk = (wave + u * C::NW) % C::BBLK;
-            const int64_t r = n0 + blk * 32 + (lane & 31);
-            const int64_t rb = r < nlim ? r : nlim - 1;
-            src.b[u] = qw + rb * (K / 2) + 16 * half;
-            src.sb[u] = (MODE != 2) ? sw + rb * G : nullptr;
+        dma16(rqb, sl + (0 * C::SBLK + C::ABLK + wave) * 1024, vb, so);
+        dma16(rqb, sl + (1 * C::SBLK + C::ABLK + wave) * 1024, vb + 32, so);
+        if constexpr (MODE != 2) {
+            dma2(rsb, sl + C::CODES + (0 * C::SBLK + C::ABLK + wave) * 256, vsb, ss);
+            dma2(rsb, sl + C::CODES + (1 * C::SBLK + C::ABLK + wave) * 256, vsb + 2, ss);
         }
-    }
+    };
+    // Wait until this wave's loads of the pair issued two loads back have
+    // landed (one pair's loads may stay in flight), then publish with a
+    // barrier. The partials dump also stores in the loop, so it waits for all.
+    auto publish = [&]() {
+        if constexpr (MODE == 2) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        else asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+        lds_barrier();
+    };
 
     v16f acc[TM][TN];
 #pragma unroll
@@ -216,15 +177,11 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_w4a4_kernel(
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-    constexpr bool SC = (MODE != 2);
-    Raw<C> r0, r1, r2;
-    // group indices past the end are clamped to the last group: the extra
-    // loads are harmless and keep the pipeline free of branches
-    load_raw<C, SC>(r0, src, 0);
-    load_raw<C, SC>(r1, src, G > 1 ? 1 : G - 1);
-    load_raw<C, SC>(r2, src, G > 2 ? 2 : G - 1);
+    load_pair(slot0, 0);
+    load_pair(slot1, 1);
+    load_pair(slot2, 2);
 
-    // low-rank branch while the first groups are in flight: acc = xl1 L2
+    // low-rank branch while the first pairs are in flight: acc = xl1 L2
     if (MODE != 2 && rank > 0) {
         const int h = lane >> 5;
         for (int ks = 0; ks < rank / 16; ++ks) {
@@ -259,91 +216,157 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_w4a4_kernel(
         }
     }
 
-    // zero upper halves of the per-block scale rows of both stages (staging
-    // never writes them; lanes 32..63 of the scale operands read them)
-    constexpr int SBLK = C::ABLK + C::BBLK;
-    for (int e = tid; e < 2 * SBLK * 32; e += NT) {
-        const int stg = e / (SBLK * 32), blk = (e / 32) % SBLK, l = e % 32;
-        const Stage zs = stage_ptr<C>(smem, stg);
-        if (blk < C::ABLK) zs.SA[blk * 64 + 32 + l] = 0;
-        else zs.SB[(blk - C::ABLK) * 64 + 32 + l] = 0;
-    }
-    store_raw<C>(r0, stage_ptr<C>(smem, 0), wave, lane);
-    __syncthreads();
-    v4i so_t[TM], wo_t[TN];
+    // Operands of the group being computed: FP6 fragments and the scale
+    // operands {s, 0} (the zero register stays in place). Right after the
+    // last MFMA of a group that reads an operand, its raw codes and scale for
+    // the next group are read; the codes are turned into FP6 just before
+    // their first MFMA there, so in between only the raw registers are live.
+    const int l16 = lane * 16, l4 = lane * 4;
+    const int ablk = wm * TM, bblk = C::ABLK + wn * TN;
+    v6i fa[TM], fb[TN];
+    v2i so[TM], wo[TN];
+    uint4 ra_n[TM], rb_n[TN];
 #pragma unroll
-    for (int i = 0; i < TM; ++i) so_t[i] = v4i{0, 0, 0, 0};
+    for (int i = 0; i < TM; ++i) so[i] = v2i{0, 0};
 #pragma unroll
-    for (int j = 0; j < TN; ++j) wo_t[j] = v4i{0, 0, 0, 0};
-
-    const v16f zero = {};
-    // One group: stage g+1 from its registers, refill them with group g+3,
-    // then run the MFMAs of group g from LDS stage g%2.
-    auto step = [&](int g, Raw<C>& rn, Raw<C>& rfill) {
-        store_raw<C>(rn, stage_ptr<C>(smem, (g + 1) & 1), wave, lane);
-        load_raw<C, SC>(rfill, src, (g + 3 < G) ? g + 3 : G - 1);
-        const Stage st = stage_ptr<C>(smem, g & 1);
-        v8i a[TM], b[TN];
-#pragma unroll
-        for (int i = 0; i < TM; ++i) a[i] = read_frag(st.A, wm * TM + i, lane);
-#pragma unroll
-        for (int j = 0; j < TN; ++j) b[j] = read_frag(st.B, wn * TN + j, lane);
-#pragma unroll
-        for (int i = 0; i < TM; ++i) {
-            const v8h so = scale_operand(so_t[i], st.SA + (wm * TM + i) * 64, lane);
-#pragma unroll
-            for (int j = 0; j < TN; ++j) {
-                const v16f p = mfma_f8_32x32x64(a[i], b[j], zero);
-                if constexpr (MODE == 2) {
-                    const int64_t col = n0 + wn * 32 * TN + j * 32 + (lane & 31);
-#pragma unroll
-                    for (int e = 0; e < 16; ++e) {
-                        const int64_t row = m0 + wm * 32 * TM + i * 32 + out_row(e, lane);
-                        if (row < mlim && col < nlim)
-                            part[((row - pm0) * pnc + (col - pn0)) * G + g] = (int32_t)p[e];
-                    }
-                } else {
-                    const v8h wo = scale_operand(wo_t[j], st.SB + (wn * TN + j) * 64, lane);
-                    const v16f s = mfma_f16_32x32x16(so, wo, zero);
-#pragma unroll
-                    for (int e = 0; e < 16; ++e) acc[i][j][e] = __builtin_fmaf(p[e], s[e], acc[i][j][e]);
-                }
-            }
+    for (int j = 0; j < TN; ++j) wo[j] = v2i{0, 0};
+    // operand i / j of group gi (0 / 1) of the pair in slot sl; `phantom`:
+    // that group lies past the end of K
+    auto read_a = [&](const char* sl, int gi, int i, bool phantom) {
+        ra_n[i] = *(const uint4*)(sl + (gi * C::SBLK + ablk + i) * 1024 + l16);
+        if constexpr (MODE != 2) {
+            const int s = *(const int*)(sl + C::CODES + (gi * C::SBLK + ablk + i) * 256 + l4);
+            so[i][0] = phantom ? 0 : s;
         }
-        __syncthreads();
+    };
+    auto read_b = [&](const char* sl, int gi, int j) {
+        rb_n[j] = *(const uint4*)(sl + (gi * C::SBLK + bblk + j) * 1024 + l16);
+        if constexpr (MODE != 2)
+            wo[j][0] = *(const int*)(sl + C::CODES + (gi * C::SBLK + bblk + j) * 256 + l4);
     };
 
-    for (int g = 0; g < G; g += 3) {
-        step(g, r1, r0);
-        if (g + 1 < G) step(g + 1, r2, r1);
-        if (g + 2 < G) step(g + 2, r0, r2);
+    const v16f zero = {};
+    // products and scale products of consecutive blocks, by parity
+    v16f P0 = zero, P1 = zero, S0 = zero, S1 = zero;
+
+    // One group g (raw operands read). For block b = (i, j): operands used
+    // for the first time are turned into FP6; the two MFMAs of b, then the
+    // FMAs of block b - 1 (for b = 0: the last block of the previous group,
+    // parity 1); operands used for the last time are read for the next group
+    // (group gi of slot nsl; nph = that group is a phantom).
+    auto group = [&](int g, const char* nsl, int gi, bool nph) {
+#pragma unroll
+        for (int bl = 0; bl < TM * TN; ++bl) {
+            const int i = bl / TN, j = bl % TN;
+            if (j == 0) fa[i] = unfold_frag(ra_n[i]);
+            if (i == 0) fb[j] = unfold_frag(rb_n[j]);
+            if constexpr (MODE == 2) {
+                order_point(fa[i], fb[j]);
+                const v16f p = mfma_fp6_32x32x64(fa[i], fb[j], zero);
+                const int64_t col = n0 + wn * 32 * TN + j * 32 + (lane & 31);
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int64_t row = m0 + wm * 32 * TM + i * 32 + out_row(e, lane);
+                    if (g < G && row < mlim && col < nlim)
+                        part[((row - pm0) * pnc + (col - pn0)) * G + g] = (int32_t)p[e];
+                }
+            } else {
+                const int pb = (bl + TM * TN - 1) % (TM * TN), pi = pb / TN, pj = pb % TN;
+                v16f& Pn = (bl & 1) ? P1 : P0;
+                v16f& Sn = (bl & 1) ? S1 : S0;
+                const v16f& Pp = (bl & 1) ? P0 : P1;
+                const v16f& Sp = (bl & 1) ? S0 : S1;
+                order_point(fa[i], fb[j]);
+                Pn = mfma_fp6_32x32x64(fa[i], fb[j], zero);
+                order_point(so[i], wo[j]);
+                Sn = mfma_f16_32x32x8(__builtin_bit_cast(v4h, so[i]), __builtin_bit_cast(v4h, wo[j]), zero);
+#pragma unroll
+                for (int e = 0; e < 16; ++e) acc[pi][pj][e] = __builtin_fmaf(Pp[e], Sp[e], acc[pi][pj][e]);
+                order_point(acc[pi][pj]);
+            }
+            if (j == TN - 1) read_a(nsl, gi, i, nph);
+            if (i == TM - 1) read_b(nsl, gi, j);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
+    // prologue: pair 0 published (pairs 1 and 2 may stay in flight), group
+    // 0's operands read
+    if constexpr (MODE == 2) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+    lds_barrier();
+#pragma unroll
+    for (int i = 0; i < TM; ++i) read_a(slot0, 0, i, false);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) read_b(slot0, 0, j);
+
+    // Step q (pair q in slot q % 3): group 2q, during which group 2q + 1's
+    // operands are read; publish pair q + 1 (loaded two steps ago); load
+    // pair q + 3 into pair q's slot, which nobody reads any more; group
+    // 2q + 1, during which group 2q + 2's operands are read from pair q + 1.
+    // The step count is rounded up to a multiple of three so the loop body
+    // has no branches (which would blur the compiler's per-slot tracking of
+    // loads into LDS); the extra groups carry zero scales.
+    auto step = [&](int q, char* cur, char* nxt) {
+        group(2 * q, cur, 1, 2 * q + 1 >= G);
+        publish();
+        load_pair(cur, q + 3);
+        group(2 * q + 1, nxt, 0, 2 * q + 2 >= G);
+    };
+    for (int q = 0; q < NP; q += 3) {
+        step(q, slot0, slot1);
+        step(q + 1, slot1, slot2);
+        step(q + 2, slot2, slot0);
     }
+    if constexpr (MODE != 2) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[TM - 1][TN - 1][e] = __builtin_fmaf(P1[e], S1[e], acc[TM - 1][TN - 1][e]);
+    }
+    // every load into LDS has landed and every wave is done with the slots
+    __syncthreads();
 
     if constexpr (MODE == 0) {
-        // bias, GELU, bf16 rounding; transpose through LDS for row-contiguous stores
-        uint16_t* out = (uint16_t*)smem;
+        // bias, GELU and bf16 rounding in registers, then transposed through
+        // LDS (slot 0), one wave row (OUT_ROWS rows) at a time, for
+        // row-contiguous stores
+        uint32_t ob[TM][TN][8];
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
-            const int lc = wn * 32 * TN + j * 32 + (lane & 31);
-            const int64_t col = n0 + lc;
+            const int64_t col = n0 + wn * 32 * TN + j * 32 + (lane & 31);
             const float bv = (bias && col < N) ? bf16_lo_to_f32(bias[col]) : 0.0f;
 #pragma unroll
             for (int i = 0; i < TM; ++i)
 #pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    float v = acc[i][j][e] + bv;
-                    if constexpr (ACT == 1) v = gelu_tanh_f32(v);
-                    const int lr = wm * 32 * TM + i * 32 + out_row(e, lane);
-                    out[lr * C::OUT_LD + lc] = f32_to_bf16_bits(v);
+                for (int e = 0; e < 16; e += 2) {
+                    float v0 = acc[i][j][e] + bv, v1 = acc[i][j][e + 1] + bv;
+                    if constexpr (ACT == 1) { v0 = gelu_tanh_f32(v0); v1 = gelu_tanh_f32(v1); }
+                    ob[i][j][e / 2] = pack_bf16x2(v0, v1);
                 }
         }
-        __syncthreads();
+        uint16_t* out = (uint16_t*)slot0;
         constexpr int CHUNKS = BN / 8;              // 16-byte chunks per tile row
-        for (int c = tid; c < BM * CHUNKS; c += NT) {
-            const int lr = c / CHUNKS, lc = (c % CHUNKS) * 8;
-            const int64_t row = m0 + lr, col = n0 + lc;
-            if (row < M && col < N)
-                *(uint4*)((uint16_t*)y + row * ldy + col) = *(const uint4*)(out + lr * C::OUT_LD + lc);
+        for (int r = 0; r < C::WGM; ++r) {
+            if (wm == r) {
+#pragma unroll
+                for (int j = 0; j < TN; ++j) {
+                    const int lc = wn * 32 * TN + j * 32 + (lane & 31);
+#pragma unroll
+                    for (int i = 0; i < TM; ++i)
+#pragma unroll
+                        for (int e = 0; e < 16; ++e) {
+                            const int lr = i * 32 + out_row(e, lane);
+                            out[lr * C::OUT_LD + lc] = (uint16_t)(ob[i][j][e / 2] >> (16 * (e & 1)));
+                        }
+                }
+            }
+            __syncthreads();
+            for (int c = tid; c < C::OUT_ROWS * CHUNKS; c += NT) {
+                const int lr = c / CHUNKS, lc = (c % CHUNKS) * 8;
+                const int64_t row = m0 + r * C::OUT_ROWS + lr, col = n0 + lc;
+                if (row < M && col < N)
+                    *(uint4*)((uint16_t*)y + row * ldy + col) = *(const uint4*)(out + lr * C::OUT_LD + lc);
+            }
+            __syncthreads();
         }
     } else if constexpr (MODE == 1) {
 #pragma unroll
@@ -370,16 +393,10 @@ void launch_mode(hipStream_t stream, const uint8_t* qx, const uint16_t* sx,
                  const uint8_t* qw, const uint16_t* sw, const float* xl1, const uint16_t* l2t,
                  int rank, const uint16_t* bias, void* y, int64_t ldy, int64_t M, int64_t N,
                  int64_t K, int64_t pm0, int64_t pmc, int64_t pn0, int64_t pnc, int32_t* p) {
-    static bool attr = false;
-    if (!attr) {
-        (void)hipFuncSetAttribute((const void*)gemm_w4a4_kernel<C, MODE, ACT>,
-                                  hipFuncAttributeMaxDynamicSharedMemorySize, C::SMEM_BYTES);
-        attr = true;
-    }
     const int64_t mext = (MODE == 2) ? pmc : M, next = (MODE == 2) ? pnc : N;
     const int64_t tiles = ((next + C::BN - 1) / C::BN) * ((mext + C::BM - 1) / C::BM);
     hipLaunchKernelGGL((gemm_w4a4_kernel<C, MODE, ACT>), dim3((unsigned)tiles), dim3(C::NT),
-                       C::SMEM_BYTES, stream, qx, sx, qw, sw, xl1, l2t, rank, bias, y, ldy, M, N, K,
+                       0, stream, qx, sx, qw, sw, xl1, l2t, rank, bias, y, ldy, M, N, K,
                        pm0, pmc, pn0, pnc, p);
 }
 

@@ -29,10 +29,19 @@
  *  - M == 0 is valid: after the shape checks the call returns SVDQ_OK
  *    without reading any pointer or touching the device.
  *  - Group size is 64 along K; K must be a multiple of 64.
- *  - 4-bit codes (format v1): rows are K-contiguous, byte i of a row holds
- *    element 2i in bits 0-3 and element 2i+1 in bits 4-7. SVDQ codes are
- *    sign-magnitude nibbles (bit 3 sign, bits 0-2 magnitude) in [-7, 7];
- *    AWQ codes are unsigned nibbles 0..15.
+ *  - SVDQ 4-bit codes (format v2): codes in [-7, 7], rows K-contiguous, every
+ *    16 consecutive codes of a row form one little-endian 64-bit word (so a
+ *    64-wide group is 32 bytes). Put the 16 codes into a 96-bit stream T as
+ *    FP6 E2M3 fields (code e at bits 6e..6e+5: |q| in bits 6e..6e+2, zero
+ *    exponent bits 6e+3 and 6e+4, sign in bit 6e+5; zero has sign 0). The
+ *    word's low dword is T[0:32) | (T[32:64) & 0x18618618) and its high dword
+ *    is T[64:96) | (T[32:64) & 0x61861861): the middle third of T rides in the
+ *    exponent fields of the outer two, so every bit of the word is a
+ *    magnitude or sign bit and any 64-bit pattern is valid. (The layout
+ *    follows gfx950's FP6 MFMA operand stream; the pages fix only that codes
+ *    are 4-bit.)
+ *  - AWQ 4-bit codes (format v1): unsigned nibbles 0..15, byte i of a row
+ *    holds element 2i in bits 0-3 and element 2i+1 in bits 4-7.
  *  - bf16 and fp16 values are passed as their 16-bit patterns.
  */
 #ifndef SVDQ_H
@@ -110,8 +119,9 @@ svdq_status svdq_quantize_act(const void* x, int64_t M, int64_t K, int64_t ldx,
  *  act         SVDQ_ACT_NONE or SVDQ_ACT_GELU_TANH (applied in fp32)
  *  y           out: [M][ldy] of y_dtype (bf16 RTNE of the fp32 result, or fp32)
  *
- * N % 8 == 0, ldy >= N, ldy % 8 == 0. The group partials P_g are exact; the
- * fp32 result matches the fp64 definition to about 1e-6 relative.
+ * N % 8 == 0, ldy >= N, ldy % 8 == 0; M * K / 2 and N * K / 2 (code bytes)
+ * must stay below 2^31. The group partials P_g are exact; the fp32 result
+ * matches the fp64 definition to about 1e-6 relative.
  * Alignment: every pointer 16-byte aligned except sx_f16 / sw_f16 (4 bytes).
  */
 svdq_status svdq_gemm_w4a4(const uint8_t* qx, const void* sx_f16, int64_t M, int64_t K,
@@ -126,6 +136,7 @@ svdq_status svdq_gemm_w4a4(const uint8_t* qx, const void* sx_f16, int64_t M, int
  * by a dump of the exact integer group partials P_g[m, n] for the rectangle
  * rows [m0, m0 + mcount) x columns [n0, n0 + ncount).
  *  p   out: int32 [mcount][ncount][K/64]
+ * Same shape limits as svdq_gemm_w4a4.
  */
 svdq_status svdq_gemm_w4a4_partials(const uint8_t* qx, int64_t M, int64_t K,
                                     const uint8_t* qw, int64_t N,

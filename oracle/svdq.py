@@ -22,10 +22,19 @@ Readings taken where the pages are silent (all listed in the design notes):
   * Y = X_hat L1 L2 + sum_g sx sw P_g + bias, with P_g the exact integer dot
     product of the codes of group g, then optional GELU (tanh form).
 
-Storage format of the 4-bit codes (shared with the library only as a
-documented layout, not as code): rows are K-contiguous, byte i of a row holds
-element 2i in bits 0-3 and element 2i+1 in bits 4-7; a nibble is
-sign-magnitude (bit 3 = sign, bits 0-2 = |q|). Weights are stored transposed,
+Storage format of the 4-bit codes (format v2; shared with the library only as
+a documented layout, not as code): rows are K-contiguous and every run of 16
+consecutive codes of a row is one little-endian 64-bit word. The word is
+defined through the 96-bit stream T that holds the 16 codes as FP6 E2M3
+values q / 8 (OCP microscaling formats: sign bit 5, exponent bits 3-4,
+mantissa bits 0-2 of each 6-bit field; a code's field sits at bits 6e..6e+5
+of T, its exponent bits are zero). The word keeps T[0:32) in bits 0-31 and
+T[64:96) in bits 32-63; the 32 bits of T[32:64) are stored in the exponent
+positions of those two parts (each bit of T[32:64) at the same offset in
+the low half when that offset is an exponent position of T[0:32), else in
+the high half, where it is an exponent position of T[64:96)). So the
+word is a bit permutation of 16 sign-magnitude codes and the three 32-bit
+thirds of T come back with masks alone. Weights are stored transposed,
 [N][K/2]; scales are fp16 [rows][K/64].
 """
 from __future__ import annotations
@@ -136,24 +145,71 @@ def dequantize_rows(codes: np.ndarray, scales_f16: np.ndarray) -> np.ndarray:
     return (q * np.asarray(scales_f16, np.float16).astype(np.float64)[..., None]).reshape(codes.shape)
 
 
+def _e2m3_word_positions() -> np.ndarray:
+    """Bit position in the 64-bit storage word of (code e, bit b) for e < 16,
+    b = 0, 1, 2 (magnitude bits) and b = 3 (sign), following the format-v2
+    definition above: the E2M3 field of code e sits at stream bits 6e..6e+5
+    (mantissa 6e..6e+2, exponent 6e+3..6e+4, sign 6e+5)."""
+    exp_pos = {6 * e + 3 for e in range(16)} | {6 * e + 4 for e in range(16)}
+    lo_holes = {t for t in exp_pos if t < 32}                # exponent bits of T[0:32)
+    hi_holes = {t - 64 for t in exp_pos if t >= 64}          # exponent bits of T[64:96)
+    pos = np.empty((16, 4), np.int64)
+    for e in range(16):
+        for b, off in enumerate((0, 1, 2, 5)):
+            t = 6 * e + off
+            if t < 32:
+                pos[e, b] = t
+            elif t >= 64:
+                pos[e, b] = t - 32
+            else:
+                u = t - 32
+                if u in lo_holes:
+                    pos[e, b] = u
+                elif u in hi_holes:
+                    pos[e, b] = 32 + u
+                else:
+                    raise AssertionError("stream bit has no storage position")
+    return pos
+
+
+_WORD_POS = _e2m3_word_positions()
+
+
 def pack_int4(codes: np.ndarray) -> np.ndarray:
-    """int8 codes in [-7, 7], [rows, K] -> bytes [rows, K/2] (sign-magnitude
-    nibbles; element 2i in the low nibble of byte i)."""
+    """int8 codes in [-7, 7], [rows, K] (K % 16 == 0) -> bytes [rows, K/2] in
+    format v2 (see the module docstring). Zero is stored with sign 0."""
     c = np.asarray(codes, np.int16)
     if c.min(initial=0) < -QMAX or c.max(initial=0) > QMAX:
         raise ValueError("codes out of [-7, 7]")
-    nib = (np.abs(c) | np.where(c < 0, 8, 0)).astype(np.uint8)
-    return (nib[:, 0::2] | (nib[:, 1::2] << 4)).astype(np.uint8)
+    rows, k = c.shape
+    if k % 16:
+        raise ValueError("K must be a multiple of 16")
+    c = c.reshape(rows, k // 16, 16)
+    mag = np.abs(c).astype(np.uint64)
+    sgn = (c < 0).astype(np.uint64)
+    word = np.zeros((rows, k // 16), np.uint64)
+    for e in range(16):
+        for b in range(3):
+            word |= ((mag[:, :, e] >> np.uint64(b)) & np.uint64(1)) << np.uint64(_WORD_POS[e, b])
+        word |= sgn[:, :, e] << np.uint64(_WORD_POS[e, 3])
+    return word.astype("<u8").view(np.uint8).reshape(rows, k // 2)
 
 
 def unpack_int4(packed: np.ndarray) -> np.ndarray:
     """Inverse of pack_int4 -> int8 codes [rows, 2 * bytes]."""
-    p = np.asarray(packed, np.uint8)
-    nib = np.empty((p.shape[0], p.shape[1] * 2), np.uint8)
-    nib[:, 0::2] = p & 0xF
-    nib[:, 1::2] = p >> 4
-    mag = (nib & 7).astype(np.int8)
-    return np.where(nib & 8, -mag, mag).astype(np.int8)
+    p = np.ascontiguousarray(np.asarray(packed, np.uint8))
+    rows, nb = p.shape
+    if nb % 8:
+        raise ValueError("row length must be a multiple of 8 bytes")
+    word = p.view("<u8").astype(np.uint64)
+    out = np.empty((rows, nb // 8, 16), np.int8)
+    for e in range(16):
+        mag = np.zeros(word.shape, np.int64)
+        for b in range(3):
+            mag |= (((word >> np.uint64(_WORD_POS[e, b])) & np.uint64(1)).astype(np.int64) << b)
+        neg = ((word >> np.uint64(_WORD_POS[e, 3])) & np.uint64(1)).astype(bool)
+        out[:, :, e] = np.where(neg, -mag, mag)
+    return out.reshape(rows, nb * 2)
 
 
 @dataclass

@@ -46,7 +46,7 @@ def test_status_strings(lib):
     for s in range(7):
         assert lib.svdq_status_string(s)
     assert lib.svdq_status_string(99) == b"unknown status"
-    assert lib.svdq_version() == 100
+    assert lib.svdq_version() == 200
 
 
 def _act(lib, **kw):
@@ -81,7 +81,7 @@ def _gemm(lib, **kw):
     (dict(N=100), SHAPE), (dict(N=0), SHAPE), (dict(K=96), SHAPE), (dict(ldy=64), SHAPE),
     (dict(ldy=132), ALIGN), (dict(act=2), UNSUP), (dict(ydt=3), UNSUP), (dict(qw=None), NULL),
     (dict(y=None), NULL), (dict(xl1=None), NULL), (dict(rank=20), SHAPE), (dict(qw=C + 4), ALIGN),
-    (dict(y=E + 65536 + 8), ALIGN),
+    (dict(y=E + 65536 + 8), ALIGN), (dict(M=1 << 20, K=4096), SHAPE), (dict(N=1 << 20, K=4096), SHAPE),
 ])
 def test_gemm_rejects(lib, kw, status):
     assert _gemm(lib, **kw) == status
@@ -89,7 +89,7 @@ def test_gemm_rejects(lib, kw, status):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(m0=-1), SHAPE), (dict(mcount=100), SHAPE), (dict(n0=64, ncount=100), SHAPE),
-    (dict(p=None), NULL), (dict(K=65), SHAPE),
+    (dict(p=None), NULL), (dict(K=65), SHAPE), (dict(M=1 << 20, K=4096), SHAPE),
 ])
 def test_partials_rejects(lib, kw, status):
     a = dict(qx=A, M=64, K=256, qw=C, N=128, m0=0, mcount=64, n0=0, ncount=128, p=E)

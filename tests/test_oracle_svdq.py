@@ -59,6 +59,36 @@ def test_pack_roundtrip_and_range():
         svdq.pack_int4(np.full((1, 2), -8, np.int8))
 
 
+def _e2m3_value(f: int) -> float:
+    """OCP E2M3 decode of one 6-bit field (bias 1; exponent 0 is subnormal)."""
+    sign, exp, man = (f >> 5) & 1, (f >> 3) & 3, f & 7
+    v = man / 8.0 if exp == 0 else (1.0 + man / 8.0) * 2.0 ** (exp - 1)
+    return -v if sign else v
+
+
+def test_pack_word_is_folded_e2m3_stream():
+    """Unfold each stored word into the 96-bit stream of 16 E2M3 fields and
+    decode every field as an FP6 value: it must be the code / 8 with a zero
+    exponent, which is what the 4-bit MFMA operand expects."""
+    exp_bits = [6 * e + 3 for e in range(16)] + [6 * e + 4 for e in range(16)]
+    lo_mask = sum(1 << t for t in exp_bits if t < 32)
+    hi_mask = sum(1 << (t - 64) for t in exp_bits if t >= 64)
+    assert lo_mask & hi_mask == 0
+    rng = np.random.default_rng(5)
+    c = rng.integers(-7, 8, size=(3, 64)).astype(np.int8)
+    words = svdq.pack_int4(c).view("<u8")
+    for r in range(3):
+        for w in range(4):
+            x = int(words[r, w])
+            x0, x1 = x & 0xFFFFFFFF, x >> 32
+            t = (x0 & ~lo_mask & 0xFFFFFFFF) | (((x0 & lo_mask) | (x1 & hi_mask)) << 32) \
+                | ((x1 & ~hi_mask & 0xFFFFFFFF) << 64)
+            for e in range(16):
+                f = (t >> (6 * e)) & 63
+                assert (f >> 3) & 3 == 0
+                assert _e2m3_value(f) * 8 == c[r, 16 * w + e]
+
+
 def test_qsym64_error_bound_and_idempotence():
     rng = np.random.default_rng(1)
     v = (rng.standard_normal((4000, 64)) * np.exp(rng.uniform(-8, 8, (4000, 1)))).astype(np.float32)
