@@ -113,11 +113,12 @@ svdq_status check_k(int64_t K) {
     return SVDQ_OK;
 }
 
-// the GEMM addresses the packed codes and scales with 31-bit byte offsets
+// the GEMM addresses the packed codes and scales with 31-bit byte offsets,
+// including rows up to one tile past the end of the matrix
 svdq_status check_gemm_bytes(int64_t M, int64_t N, int64_t K) {
     const int64_t lim = (int64_t)1 << 31;
-    if (M * (K / 2) >= lim || N * (K / 2) >= lim)
-        return fail(SVDQ_ERR_SHAPE, "M * K / 2 and N * K / 2 must stay below 2^31 bytes");
+    if ((M + 256) * (K / 2) >= lim || (N + 256) * (K / 2) >= lim)
+        return fail(SVDQ_ERR_SHAPE, "(M + 256) * K / 2 and (N + 256) * K / 2 must stay below 2^31 bytes");
     return SVDQ_OK;
 }
 

@@ -12,17 +12,18 @@
 //    fields folded out, so a wave turns 16 codes into FP6 with four bit
 //    operations right before its MFMAs;
 //  - packed rows travel from global memory straight into LDS (buffer loads
-//    with an LDS destination), two groups = 64 contiguous bytes per row at a
-//    time, into a ring of three pair slots filled two steps ahead, with no
-//    registers held; every lane's 16 bytes land where the lane that consumes
-//    them in the MFMA reads them;
+//    with an LDS destination) four groups at a time: one load instruction
+//    covers whole 128-byte lines of 8 rows (the vector memory pipeline's cost
+//    follows the number of lines an instruction touches), and the chunk a
+//    lane fetches is XOR-swizzled so the lanes that consume a group in the
+//    MFMA read LDS without bank conflicts; the scales of the same four groups
+//    come as a 32-byte window per row that absorbs any row misalignment;
 //  - the two-sided scale S = sx (x) sw of a 32x32 block is an outer product
-//    that a v_mfma_f32_32x32x8_f16 with one non-zero k forms exactly; the
-//    scales arrive in LDS as the zero-extended first register of that
-//    operand (lanes 32..63 read zero), and the VALU does one FMA per output
-//    element and group, acc += P_g * S_g;
+//    that a v_mfma_f32_32x32x8_f16 with one non-zero k forms exactly, and the
+//    VALU does one FMA per output element and group, acc += P_g * S_g;
 //  - products and scale products of consecutive blocks alternate between two
-//    register sets, so a block's FMAs run while the next block's MFMAs do;
+//    register sets, so one wave's FMAs for a block run while the matrix pipe
+//    works on its next block;
 //  - tiles are swizzled so each XCD (own L2) works on compact groups of tiles;
 //  - the accumulator starts from X_hat L1 L2 (bf16 MFMA on the hi/lo split of
 //    the fp32 xl1); bias and GELU run in fp32 before the single rounding of
@@ -31,29 +32,35 @@
 
 namespace {
 
-template <int BM_, int BN_, int WGM_, int WGN_>
+template <int BM_, int BN_, int WGM_, int WGN_, int MINB_>
 struct Cfg {
-    static constexpr int BM = BM_, BN = BN_, WGM = WGM_, WGN = WGN_;
+    static constexpr int BM = BM_, BN = BN_, WGM = WGM_, WGN = WGN_, MINB = MINB_;
     static constexpr int NW = WGM * WGN, NT = 64 * NW;
     static constexpr int TM = BM / 32 / WGM, TN = BN / 32 / WGN;     // 32x32 blocks per wave
-    static constexpr int ABLK = BM / 32, BBLK = BN / 32, SBLK = ABLK + NW;
-    // One pair slot (two groups): codes [group][block][lane][16 B], then
-    // scale operands [group][block][lane][4 B]; blocks are the ABLK A blocks,
-    // then one B slot per wave (waves w >= BBLK fill theirs with a copy that
-    // nobody reads, so every wave issues the same loads).
-    static constexpr int CODES = 2 * SBLK * 1024, SLOT = CODES + 2 * SBLK * 256;
-    // bf16 output staging for the epilogue: OUT_ROWS rows at a time in slot 0
+    static constexpr int ABLK = BM / 32, BBLK = BN / 32, SBLK = ABLK + BBLK;
+    // wave w loads the 32-row blocks w, w + NW, ... of A and of B
+    static constexpr int APW = ABLK / NW, BPW = BBLK / NW;
+    // One quad slot (four groups): codes [block][8-row part][lane][16 B]
+    // (A blocks, then B blocks; see the swizzle at the loads) and, in a slot
+    // of its own, the scale windows [tile row][32 B] (A rows, then B rows).
+    static constexpr int CODE_SLOT = SBLK * 4096, SC_SLOT = (BM + BN) * 32;
+    // bf16 output staging for the epilogue: OUT_ROWS rows at a time in code slot 0
     static constexpr int OUT_LD = BN + 8, OUT_ROWS = 32 * TM;
     static_assert(TM * 32 * WGM == BM && TN * 32 * WGN == BN, "tile shape");
-    static_assert(ABLK <= NW && BBLK <= NW, "one loaded block per wave and operand");
+    static_assert(APW * NW == ABLK && BPW * NW == BBLK && APW >= 1 && BPW >= 1,
+                  "blocks split evenly over the waves");
     static_assert((TM * TN) % 2 == 0, "blocks per wave must be even for the register rotation");
-    static_assert(OUT_ROWS * OUT_LD * 2 <= SLOT, "epilogue staging fits one slot");
-    static_assert(3 * SLOT <= 160 * 1024, "LDS budget");
+    static_assert(OUT_ROWS * OUT_LD * 2 <= CODE_SLOT, "epilogue staging fits one slot");
+    static_assert(2 * (CODE_SLOT + SC_SLOT) * MINB <= 160 * 1024, "LDS budget");
 };
 
-// the QKV-sized configuration: 256 x 192 tiles, 8 waves (4 x 2) of 64 x 96,
-// one workgroup per CU; 4096 x 9216 is 768 tiles = 3 per CU.
-using MainCfg = Cfg<256, 192, 4, 2>;
+// 128 x 128 tiles, 4 waves (2 x 2) of 64 x 64, two workgroups per CU. The
+// 64 x 64 wave tile leaves room in 256 VGPRs for the accumulators, two sets
+// of products and scale products and the operands; with one wave per SIMD
+// per workgroup, the two waves that share a SIMD belong to different
+// workgroups, never wait for each other at a barrier and so interleave their
+// MFMA and VALU work.
+using MainCfg = Cfg<128, 128, 2, 2, 2>;
 
 DEV int out_row(int i, int lane) { return 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3); }
 
@@ -62,12 +69,6 @@ typedef __attribute__((address_space(3))) void lds_void;
 // 16 bytes per lane from global memory into LDS at lds + 16 * lane
 DEV void dma16(rsrc_t r, char* lds, int voff, int soff) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, voff, soff, 0, 0);
-}
-
-// 2 bytes per lane into the low half of the dword at lds + 4 * lane (the
-// high half is zeroed; lanes whose offset is out of range get 0)
-DEV void dma2(rsrc_t r, char* lds, int voff, int soff) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 2, voff, soff, 0, 0);
 }
 
 // 16 raw bytes (two stored words) -> the lane's FP6 fragment (6 dwords)
@@ -79,7 +80,7 @@ DEV v6i unfold_frag(const uint4& raw) {
 }
 
 template <class C, int MODE, int ACT>   // MODE 0: bf16 out, 1: fp32 out, 2: integer partials dump
-__global__ __launch_bounds__(C::NT, 1) void gemm_w4a4_kernel(
+__global__ __launch_bounds__(C::NT, C::MINB) void gemm_w4a4_kernel(
     const uint8_t* __restrict__ qx, const uint16_t* __restrict__ sx,
     const uint8_t* __restrict__ qw, const uint16_t* __restrict__ sw,
     const float* __restrict__ xl1, const uint16_t* __restrict__ l2t, int rank,
@@ -88,12 +89,13 @@ __global__ __launch_bounds__(C::NT, 1) void gemm_w4a4_kernel(
     int64_t pm0, int64_t pmc, int64_t pn0, int64_t pnc, int32_t* __restrict__ part)
 {
     constexpr int BM = C::BM, BN = C::BN, TM = C::TM, TN = C::TN, NT = C::NT;
-    // three pair slots as separate objects: the compiler then tracks each
-    // slot's outstanding LDS-destination loads on its own and makes reads of
-    // one slot wait only for loads into that slot
-    __shared__ __attribute__((aligned(16))) char slot0[C::SLOT];
-    __shared__ __attribute__((aligned(16))) char slot1[C::SLOT];
-    __shared__ __attribute__((aligned(16))) char slot2[C::SLOT];
+    // two quad slots of codes and two of scales, all separate objects: the
+    // compiler then tracks each one's outstanding LDS-destination loads on
+    // its own and makes reads of a slot wait only for loads into that slot
+    __shared__ __attribute__((aligned(16))) char cs0[C::CODE_SLOT];
+    __shared__ __attribute__((aligned(16))) char cs1[C::CODE_SLOT];
+    __shared__ __attribute__((aligned(16))) char ss0[C::SC_SLOT];
+    __shared__ __attribute__((aligned(16))) char ss1[C::SC_SLOT];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / C::WGN, wn = wave % C::WGN;
@@ -119,53 +121,85 @@ __global__ __launch_bounds__(C::NT, 1) void gemm_w4a4_kernel(
     const int64_t n0 = (MODE == 2 ? pn0 : 0) + (int64_t)tn * BN;
     const int64_t mlim = (MODE == 2) ? pm0 + pmc : M;
     const int64_t nlim = (MODE == 2) ? pn0 + pnc : N;
-    const int G = (int)(K / 64), NP = (G + 1) / 2;   // groups, group pairs
+    const int G = (int)(K / 64), NQ = (G + 3) / 4;   // groups, quads of groups
 
-    // Loading: wave w loads block w of the A tile and block w % BBLK of the
-    // B tile; lane l takes row l % 32 and half l / 32 of each group of
-    // that row, which is where the lane that consumes those codes in the MFMA
-    // reads them. Scale loads go to lanes 0..31 (lanes 32..63 get an out-of-
-    // range offset, hence 0). Rows past the end are clamped to the last row:
-    // what they load only reaches output rows or columns that are never
-    // stored. Byte offsets fit in 31 bits (checked on the host).
-    const int half = lane >> 5;
-    int64_t ra = m0 + (int64_t)(wave % C::ABLK) * 32 + (lane & 31);
-    int64_t rb = n0 + (int64_t)(wave % C::BBLK) * 32 + (lane & 31);
-    ra = ra < mlim ? ra : mlim - 1;
-    rb = rb < nlim ? rb : nlim - 1;
+    // ---- loads into LDS ------------------------------------------------
+    // Codes: a quad of a row is 128 contiguous bytes. Part i (0..3) of a
+    // 32-row block is one load: lane l takes row 8 i + l / 8 of the block and
+    // its 16-byte chunk c = (l % 8) ^ f(row), f(row) = (row / 2) % 8, so chunk
+    // c of block row r lands at byte 128 r + 16 (c ^ f(r)) of the block's 4 KB.
+    // Rows past the end of the matrix fall outside the buffer and read 0
+    // (their outputs are never stored). Stepping by 8 rows and by quads goes
+    // into the scalar offset. Byte offsets fit in 31 bits (checked on the host).
     const rsrc_t rqa = make_rsrc(qx, M * (K / 2));
     const rsrc_t rqb = make_rsrc(qw, N * (K / 2));
-    const rsrc_t rsa = make_rsrc(sx, (MODE != 2) ? M * G * 2 : 0);
-    const rsrc_t rsb = make_rsrc(sw, (MODE != 2) ? N * G * 2 : 0);
-    const int va = (int)(ra * (K / 2)) + 16 * half, vb = (int)(rb * (K / 2)) + 16 * half;
-    constexpr int OUT_OF_RANGE = 0x7FFFFFF0;
-    const int vsa = half ? OUT_OF_RANGE : (int)(ra * G * 2);
-    const int vsb = half ? OUT_OF_RANGE : (int)(rb * G * 2);
-
-    // pair q into a slot (pair indices past the end are clamped; groups past
-    // the end get a zero scale operand where they are read).
-    auto load_pair = [&](char* sl, int q) {
-        q = q < NP ? q : NP - 1;
-        const int so = q * 64, ss = q * 4;
-        dma16(rqa, sl + (0 * C::SBLK + wave) * 1024, va, so);
-        dma16(rqa, sl + (1 * C::SBLK + wave) * 1024, va + 32, so);
-        if constexpr (MODE != 2) {
-            dma2(rsa, sl + C::CODES + (0 * C::SBLK + wave) * 256, vsa, ss);
-            dma2(rsa, sl + C::CODES + (1 * C::SBLK + wave) * 256, vsa + 2, ss);
+    // the buffer range check zeroes any dword that is partly out of range, so
+    // the scale ranges are rounded up to whole dwords (the extra two bytes
+    // share the last dword of the array, so the read stays on its page)
+    const rsrc_t rsa = make_rsrc(sx, (MODE != 2) ? (M * G * 2 + 3) / 4 * 4 : 0);
+    const rsrc_t rsb = make_rsrc(sw, (MODE != 2) ? (N * G * 2 + 3) / 4 * 4 : 0);
+    const int lr8 = lane >> 3;                       // row within an 8-row part
+    const int cpe = (lane & 7) ^ (lr8 >> 1);          // chunk for even parts (f = lr8 / 2)
+    const int cpo = cpe ^ 4;                          // odd parts (f = 4 + lr8 / 2)
+    int vca_e[C::APW], vca_o[C::APW], vcb_e[C::BPW], vcb_o[C::BPW];
+#pragma unroll
+    for (int k = 0; k < C::APW; ++k) {
+        const int64_t r = m0 + (int64_t)(wave + k * C::NW) * 32 + lr8;
+        vca_e[k] = (int)(r * (K / 2)) + 16 * cpe;
+        vca_o[k] = (int)(r * (K / 2)) + 16 * cpo;
+    }
+#pragma unroll
+    for (int k = 0; k < C::BPW; ++k) {
+        const int64_t r = n0 + (int64_t)(wave + k * C::NW) * 32 + lr8;
+        vcb_e[k] = (int)(r * (K / 2)) + 16 * cpe;
+        vcb_o[k] = (int)(r * (K / 2)) + 16 * cpo;
+    }
+    // Scales: the quad's four fp16 scales of a row are 8 bytes at
+    // 2 (row G + 4 q), inside the 32-byte window that starts at the 16-byte
+    // boundary below 2 row G + 8 q (2 row G mod 16 is the row's offset in
+    // the window). One load covers 32 rows: lane l takes 16 bytes of row l / 2.
+    int vsa[C::APW], vsb[C::BPW];
+#pragma unroll
+    for (int k = 0; k < C::APW; ++k) {
+        const int64_t r = m0 + (int64_t)(wave + k * C::NW) * 32 + (lane >> 1);
+        vsa[k] = (int)((r * G * 2) & ~(int64_t)15) + 16 * (lane & 1);
+    }
+#pragma unroll
+    for (int k = 0; k < C::BPW; ++k) {
+        const int64_t r = n0 + (int64_t)(wave + k * C::NW) * 32 + (lane >> 1);
+        vsb[k] = (int)((r * G * 2) & ~(int64_t)15) + 16 * (lane & 1);
+    }
+    // quad q into a code slot and a scale slot (quads past the end read the
+    // next row's bytes or 0; their groups get a zero scale where read)
+    auto load_quad = [&](char* cs, char* ss, int q) __attribute__((always_inline)) {
+        const int so = q * 128;
+#pragma unroll
+        for (int k = 0; k < C::APW; ++k) {
+            char* dst = cs + (wave + k * C::NW) * 4096;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                dma16(rqa, dst + i * 1024, (i & 1) ? vca_o[k] : vca_e[k], so + 8 * i * (int)(K / 2));
         }
-        dma16(rqb, sl + (0 * C::SBLK + C::ABLK + wave) * 1024, vb, so);
-        dma16(rqb, sl + (1 * C::SBLK + C::ABLK + wave) * 1024, vb + 32, so);
+#pragma unroll
+        for (int k = 0; k < C::BPW; ++k) {
+            char* dst = cs + (C::ABLK + wave + k * C::NW) * 4096;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                dma16(rqb, dst + i * 1024, (i & 1) ? vcb_o[k] : vcb_e[k], so + 8 * i * (int)(K / 2));
+        }
         if constexpr (MODE != 2) {
-            dma2(rsb, sl + C::CODES + (0 * C::SBLK + C::ABLK + wave) * 256, vsb, ss);
-            dma2(rsb, sl + C::CODES + (1 * C::SBLK + C::ABLK + wave) * 256, vsb + 2, ss);
+#pragma unroll
+            for (int k = 0; k < C::APW; ++k)
+                dma16(rsa, ss + (wave + k * C::NW) * 32 * 32, vsa[k], q * 8);
+#pragma unroll
+            for (int k = 0; k < C::BPW; ++k)
+                dma16(rsb, ss + (BM + (wave + k * C::NW) * 32) * 32, vsb[k], q * 8);
         }
     };
-    // Wait until this wave's loads of the pair issued two loads back have
-    // landed (one pair's loads may stay in flight), then publish with a
-    // barrier. The partials dump also stores in the loop, so it waits for all.
-    auto publish = [&]() {
-        if constexpr (MODE == 2) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        else asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    // Wait for this wave's loads (the quad loaded one step ago) and publish
+    // them with a barrier.
+    auto publish = [&]() __attribute__((always_inline)) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         lds_barrier();
     };
 
@@ -177,11 +211,9 @@ __global__ __launch_bounds__(C::NT, 1) void gemm_w4a4_kernel(
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-    load_pair(slot0, 0);
-    load_pair(slot1, 1);
-    load_pair(slot2, 2);
+    load_quad(cs0, ss0, 0);
 
-    // low-rank branch while the first pairs are in flight: acc = xl1 L2
+    // low-rank branch while the first quad is in flight: acc = xl1 L2
     if (MODE != 2 && rank > 0) {
         const int h = lane >> 5;
         for (int ks = 0; ks < rank / 16; ++ks) {
@@ -216,12 +248,27 @@ __global__ __launch_bounds__(C::NT, 1) void gemm_w4a4_kernel(
         }
     }
 
-    // Operands of the group being computed: FP6 fragments and the scale
-    // operands {s, 0} (the zero register stays in place). Right after the
-    // last MFMA of a group that reads an operand, its raw codes and scale for
-    // the next group are read; the codes are turned into FP6 just before
-    // their first MFMA there, so in between only the raw registers are live.
-    const int l16 = lane * 16, l4 = lane * 4;
+    // ---- operands ---------------------------------------------------------
+    // Codes of group gq (0..3) of a quad, for this lane (row r = lane % 32 of
+    // a block, half h = lane / 32): chunk 2 gq + h of the row. The scale of
+    // group gq of row r sits in its window at byte (2 r_glob G mod 16) + 2 gq.
+    // A's scale operand is {s, 0} with s = 0 in lanes 32..63 and for groups
+    // past the end of K; B's is {s, 0} (its lanes 32..63 meet A's zeros).
+    const int r32 = lane & 31, hh = lane >> 5;
+    int xo[4];
+#pragma unroll
+    for (int gq = 0; gq < 4; ++gq) xo[gq] = 128 * r32 + 16 * ((2 * gq + hh) ^ ((r32 >> 1) & 7));
+    int soa[TM], sob[TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+        const int tr = (wm * TM + i) * 32 + r32;
+        soa[i] = tr * 32 + (int)(((m0 + tr) * G * 2) & 15);
+    }
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+        const int tr = (wn * TN + j) * 32 + r32;
+        sob[j] = (BM + tr) * 32 + (int)(((n0 + tr) * G * 2) & 15);
+    }
     const int ablk = wm * TM, bblk = C::ABLK + wn * TN;
     v6i fa[TM], fb[TN];
     v2i so[TM], wo[TN];
@@ -230,19 +277,19 @@ __global__ __launch_bounds__(C::NT, 1) void gemm_w4a4_kernel(
     for (int i = 0; i < TM; ++i) so[i] = v2i{0, 0};
 #pragma unroll
     for (int j = 0; j < TN; ++j) wo[j] = v2i{0, 0};
-    // operand i / j of group gi (0 / 1) of the pair in slot sl; `phantom`:
-    // that group lies past the end of K
-    auto read_a = [&](const char* sl, int gi, int i, bool phantom) {
-        ra_n[i] = *(const uint4*)(sl + (gi * C::SBLK + ablk + i) * 1024 + l16);
+    // operand i / j of group gq of the quad in (cs, ss); `real`: the group
+    // lies inside K
+    auto read_a = [&](const char* cs, const char* ss, int gq, int i, bool real) __attribute__((always_inline)) {
+        ra_n[i] = *(const uint4*)(cs + (ablk + i) * 4096 + xo[gq]);
         if constexpr (MODE != 2) {
-            const int s = *(const int*)(sl + C::CODES + (gi * C::SBLK + ablk + i) * 256 + l4);
-            so[i][0] = phantom ? 0 : s;
+            const int s = (int)*(const uint16_t*)(ss + soa[i] + 2 * gq);
+            so[i][0] = (real && hh == 0) ? s : 0;
         }
     };
-    auto read_b = [&](const char* sl, int gi, int j) {
-        rb_n[j] = *(const uint4*)(sl + (gi * C::SBLK + bblk + j) * 1024 + l16);
+    auto read_b = [&](const char* cs, const char* ss, int gq, int j) __attribute__((always_inline)) {
+        rb_n[j] = *(const uint4*)(cs + (bblk + j) * 4096 + xo[gq]);
         if constexpr (MODE != 2)
-            wo[j][0] = *(const int*)(sl + C::CODES + (gi * C::SBLK + bblk + j) * 256 + l4);
+            wo[j][0] = (int)*(const uint16_t*)(ss + sob[j] + 2 * gq);
     };
 
     const v16f zero = {};
@@ -253,8 +300,8 @@ __global__ __launch_bounds__(C::NT, 1) void gemm_w4a4_kernel(
     // for the first time are turned into FP6; the two MFMAs of b, then the
     // FMAs of block b - 1 (for b = 0: the last block of the previous group,
     // parity 1); operands used for the last time are read for the next group
-    // (group gi of slot nsl; nph = that group is a phantom).
-    auto group = [&](int g, const char* nsl, int gi, bool nph) {
+    // (group ngq of the quad in (ncs, nss); nreal = it lies inside K).
+    auto group = [&](int g, const char* ncs, const char* nss, int ngq, bool nreal) __attribute__((always_inline)) {
 #pragma unroll
         for (int bl = 0; bl < TM * TN; ++bl) {
             const int i = bl / TN, j = bl % TN;
@@ -280,43 +327,47 @@ __global__ __launch_bounds__(C::NT, 1) void gemm_w4a4_kernel(
                 Pn = mfma_fp6_32x32x64(fa[i], fb[j], zero);
                 order_point(so[i], wo[j]);
                 Sn = mfma_f16_32x32x8(__builtin_bit_cast(v4h, so[i]), __builtin_bit_cast(v4h, wo[j]), zero);
+                // both MFMAs issue before the FMAs of the previous block,
+                // whose inputs are long complete, so one wave keeps the
+                // matrix pipe and the VALU busy at the same time
+                __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int e = 0; e < 16; ++e) acc[pi][pj][e] = __builtin_fmaf(Pp[e], Sp[e], acc[pi][pj][e]);
                 order_point(acc[pi][pj]);
             }
-            if (j == TN - 1) read_a(nsl, gi, i, nph);
-            if (i == TM - 1) read_b(nsl, gi, j);
+            if (j == TN - 1) read_a(ncs, nss, ngq, i, nreal);
+            if (i == TM - 1) read_b(ncs, nss, ngq, j);
             __builtin_amdgcn_sched_barrier(0);
         }
     };
 
-    // prologue: pair 0 published (pairs 1 and 2 may stay in flight), group
-    // 0's operands read
-    if constexpr (MODE == 2) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    else asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
-    lds_barrier();
+    // prologue: quad 0 published, quad 1 in flight, group 0's operands read
+    publish();
+    load_quad(cs1, ss1, 1);
 #pragma unroll
-    for (int i = 0; i < TM; ++i) read_a(slot0, 0, i, false);
+    for (int i = 0; i < TM; ++i) read_a(cs0, ss0, 0, i, true);
 #pragma unroll
-    for (int j = 0; j < TN; ++j) read_b(slot0, 0, j);
+    for (int j = 0; j < TN; ++j) read_b(cs0, ss0, 0, j);
 
-    // Step q (pair q in slot q % 3): group 2q, during which group 2q + 1's
-    // operands are read; publish pair q + 1 (loaded two steps ago); load
-    // pair q + 3 into pair q's slot, which nobody reads any more; group
-    // 2q + 1, during which group 2q + 2's operands are read from pair q + 1.
-    // The step count is rounded up to a multiple of three so the loop body
-    // has no branches (which would blur the compiler's per-slot tracking of
-    // loads into LDS); the extra groups carry zero scales.
-    auto step = [&](int q, char* cur, char* nxt) {
-        group(2 * q, cur, 1, 2 * q + 1 >= G);
+    // Step q (quad q in slots cur): groups 4q .. 4q + 2, each reading the
+    // next one's operands; publish quad q + 1 (loaded one step ago); load
+    // quad q + 2 into quad q's slots, which nobody reads any more; group
+    // 4q + 3, reading group 4q + 4's operands from quad q + 1. The step count
+    // is rounded up to an even number so the loop body has no branches
+    // (which would blur the compiler's per-slot tracking of loads into LDS);
+    // the extra groups carry zero scales.
+    auto step = [&](int q, char* cs, char* ss, char* ncs, char* nss) __attribute__((always_inline)) {
+        const int g0 = 4 * q;
+        group(g0, cs, ss, 1, g0 + 1 < G);
+        group(g0 + 1, cs, ss, 2, g0 + 2 < G);
+        group(g0 + 2, cs, ss, 3, g0 + 3 < G);
         publish();
-        load_pair(cur, q + 3);
-        group(2 * q + 1, nxt, 0, 2 * q + 2 >= G);
+        load_quad(cs, ss, q + 2);
+        group(g0 + 3, ncs, nss, 0, g0 + 4 < G);
     };
-    for (int q = 0; q < NP; q += 3) {
-        step(q, slot0, slot1);
-        step(q + 1, slot1, slot2);
-        step(q + 2, slot2, slot0);
+    for (int q = 0; q < NQ; q += 2) {
+        step(q, cs0, ss0, cs1, ss1);
+        step(q + 1, cs1, ss1, cs0, ss0);
     }
     if constexpr (MODE != 2) {
 #pragma unroll
@@ -327,7 +378,7 @@ __global__ __launch_bounds__(C::NT, 1) void gemm_w4a4_kernel(
 
     if constexpr (MODE == 0) {
         // bias, GELU and bf16 rounding in registers, then transposed through
-        // LDS (slot 0), one wave row (OUT_ROWS rows) at a time, for
+        // LDS (code slot 0), one wave row (OUT_ROWS rows) at a time, for
         // row-contiguous stores
         uint32_t ob[TM][TN][8];
 #pragma unroll
@@ -343,7 +394,7 @@ __global__ __launch_bounds__(C::NT, 1) void gemm_w4a4_kernel(
                     ob[i][j][e / 2] = pack_bf16x2(v0, v1);
                 }
         }
-        uint16_t* out = (uint16_t*)slot0;
+        uint16_t* out = (uint16_t*)cs0;
         constexpr int CHUNKS = BN / 8;              // 16-byte chunks per tile row
         for (int r = 0; r < C::WGM; ++r) {
             if (wm == r) {

@@ -119,8 +119,8 @@ svdq_status svdq_quantize_act(const void* x, int64_t M, int64_t K, int64_t ldx,
  *  act         SVDQ_ACT_NONE or SVDQ_ACT_GELU_TANH (applied in fp32)
  *  y           out: [M][ldy] of y_dtype (bf16 RTNE of the fp32 result, or fp32)
  *
- * N % 8 == 0, ldy >= N, ldy % 8 == 0; M * K / 2 and N * K / 2 (code bytes)
- * must stay below 2^31. The group partials P_g are exact; the fp32 result
+ * N % 8 == 0, ldy >= N, ldy % 8 == 0; (M + 256) * K / 2 and
+ * (N + 256) * K / 2 must stay below 2^31 (code bytes plus a tile of slack). The group partials P_g are exact; the fp32 result
  * matches the fp64 definition to about 1e-6 relative.
  * Alignment: every pointer 16-byte aligned except sx_f16 / sw_f16 (4 bytes).
  */
