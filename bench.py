@@ -29,8 +29,17 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
-PEAK_FP8_TFLOPS = 5000.0      # MI355X dense FP8 MFMA (the GEMM's MFMA type)
+PEAK_FP6_TFLOPS = 10100.0     # MI355X dense FP6/FP4 MFMA: the instruction the GEMM runs on
+PEAK_INT8_TOPS = 5000.0       # MI355X dense INT8 MFMA: the integer peak INT4 x INT4 is quoted against
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+
+# HBM traffic of one GEMM launch on the QKV shape, from two rocprofv3 counter
+# passes over this script (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch),
+# each scaled by the factor that makes the same counter read the known size of
+# the plain device copy this script also runs.  The figures hold only for the
+# kernel sources they were taken on (their sha256 below); otherwise the
+# traffic is reported as null.
+GEMM_TRAFFIC = None
 
 
 def log(msg):
@@ -58,7 +67,7 @@ def synth_linear(M, K, N, rank, seed, device):
         l1t=(torch.randn((rank, K), generator=g) * 0.05).to(torch.bfloat16).to(device),
         l2t=(torch.randn((N, rank), generator=g) * 0.1).to(torch.bfloat16).to(device),
         qw=torch.randint(0, 256, (N, K // 2), generator=g, dtype=torch.uint8).to(device),
-        sw=(torch.rand((N, K // 64), generator=g) * 0.02 + 0.01).to(torch.float16).to(device),
+        sw=(torch.rand(((K // 64 + 3) // 4, N, 4), generator=g) * 0.02 + 0.01).to(torch.float16).to(device),
         bias=bf16(li.bias),
     )
     return ops
@@ -106,6 +115,24 @@ def time_graph(fn, per_graph, replays=20):
     e.record()
     e.synchronize()
     return s.elapsed_time(e) / (replays * per_graph)
+
+
+def gemm_source_digest():
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("gemm_w4a4.hip", "common.h"):
+        with open(os.path.join(ROOT, "bit_quantized_diffusion_svdq_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def gemm_traffic_bytes():
+    """HBM bytes per GEMM launch from the recorded counter passes, or None when
+    the kernel sources have changed since they were taken."""
+    t = GEMM_TRAFFIC
+    if t is None or t["source_sha256"] != gemm_source_digest():
+        return None
+    return int(round(1024 * (t["fetch_kib"] * t["fetch_factor"] + t["write_kib"] * t["write_factor"])))
 
 
 def cpu_baseline(M, K, N, rank, budget_s=20.0):
@@ -172,39 +199,56 @@ def main():
     y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
     qx, sx, xl1 = lib.quantize_act(ops["x"], ops["inv_lambda"], ops["l1t"], R)
 
-    def step():
-        run_linear(lib, ops, R, y=y)
+    # the GEMM of every timed step is bracketed by HIP events on the stream it
+    # is launched on (torch's current stream, which the binding passes down)
+    marks = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+             for _ in range(args.steps)]
+
+    def step(i=None):
+        qa, sa, xa = lib.quantize_act(ops["x"], ops["inv_lambda"], ops["l1t"], R)
+        if i is not None:
+            marks[i][0].record()
+        lib.w4a4_linear(qa, sa, xa, ops["qw"], ops["sw"], ops["l2t"], ops["bias"], R, y=y)
+        if i is not None:
+            marks[i][1].record()
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     log(f"timing {args.steps} steps")
     t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
+    for i in range(args.steps):
+        step(i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms = wall * 1e3 / args.steps
     flops = 2.0 * M * N * K
     value = flops / (ms * 1e-3) / 1e12
+    gemm_ms = sum(a.elapsed_time(b) for a, b in marks) / args.steps
 
-    # per-kernel durations with HIP events on the launch stream
-    iters = max(20, args.steps)
-    gemm_ms = time_events(lambda: lib.w4a4_linear(qx, sx, xl1, ops["qw"], ops["sw"], ops["l2t"],
-                                                  ops["bias"], R, y=y), iters)
     qx_b = torch.empty_like(qx)
     sx_b = torch.empty_like(sx)
     xl1_b = torch.empty_like(xl1)
     act_ms = time_graph(lambda: lib.svdq_quantize_act(ops["x"], M, K, K, ops["inv_lambda"], ops["l1t"], R,
                                                       qx_b, sx_b, xl1_b), 50)
     gemm_tflops = flops / (gemm_ms * 1e-3) / 1e12
+    # HBM reference: a plain device-to-device copy of known size (its counter
+    # readings calibrate the GEMM's FETCH_SIZE / WRITE_SIZE figures)
+    copy_bytes = 1 << 28
+    csrc_buf = torch.ones(copy_bytes, dtype=torch.uint8, device=dev)
+    cdst_buf = torch.empty_like(csrc_buf)
+    copy_ms = time_events(lambda: cdst_buf.copy_(csrc_buf), 10)
+    del csrc_buf, cdst_buf
+    gemm_bytes = (M + N) * (K // 2 + (K // 64) * 2) + M * R * 4 + N * R * 2 + N * 2 + M * N * 2
     act_bytes = M * K * 2 + M * K // 2 + M * (K // 64) * 2 + M * R * 4 + K * 4 + R * K * 2
     log(f"step {ms:.4f} ms, gemm {gemm_ms * 1e3:.1f} us ({gemm_tflops:.0f} TFLOP/s), "
         f"act {act_ms * 1e3:.1f} us")
 
     extra = {"gemm_us": round(gemm_ms * 1e3, 2), "act_quant_us": round(act_ms * 1e3, 2),
              "act_quant_GBps": round(act_bytes / (act_ms * 1e-3) / 1e9, 1),
-             "act_quant_hbm_frac": round(act_bytes / (act_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+             "act_quant_hbm_frac": round(act_bytes / (act_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+             "gemm_frac_of_int8_peak": round(gemm_tflops / PEAK_INT8_TOPS, 4),
+             "copy_256MiB_GBps": round(2 * copy_bytes / (copy_ms * 1e-3) / 1e9, 1)}
 
     if not args.no_extra:
         # AWQ W4A16 GEMV, weights rotated through > 256 MB
@@ -258,15 +302,16 @@ def main():
         "metric": "W4A4 linear effective TOPS (M4096 K3072 N9216 r32) + % of MI355X MFMA peak",
         "value": round(value, 2), "unit": "TOPS", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "int4 codes, fp8 MFMA, fp32 accumulate",
+        "scaling": "weak", "vs_baseline": None, "dtype": "int4 x int4 (exact on fp6 MFMA), fp32 accumulate",
         "data": "synthetic",
         "config": {"workload": "DiT attention QKV projection as an SVDQuant W4A4 linear: act quant + "
                                "INT4 g64 GEMM + rank-32 low-rank + bias, bf16 out",
                    "M": M, "K": K, "N": N, "rank": R, "group": 64, "parallelism": "none (1 GPU)"},
-        "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 1), "peak": PEAK_FP8_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(gemm_tflops / PEAK_FP8_TFLOPS, 4),
-                     "traffic": None, "kernel": "gemm_w4a4_kernel"},
-        "frac_of_peak_step": round(value / PEAK_FP8_TFLOPS, 4),
+        "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 1), "peak": PEAK_FP6_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(gemm_tflops / PEAK_FP6_TFLOPS, 4),
+                     "traffic": gemm_traffic_bytes(), "traffic_unit": "HBM bytes per launch",
+                     "algorithmic_bytes": gemm_bytes, "kernel": "gemm_w4a4_kernel"},
+        "frac_of_int8_peak_step": round(value / PEAK_INT8_TOPS, 4),
         "extra": extra,
     }
     if not args.no_cpu_baseline:

@@ -124,11 +124,12 @@ def awq_gemv_w4a16(x, M, K, inv_s, qw, scale, zero, N, bias, y, stream=None):
 # (allocate outputs with torch, then call the entry points above)
 
 def quantize_act(x: torch.Tensor, inv_lambda, l1t, rank: int, stream=None):
-    """x: bf16 [M, K] on the GPU -> (qx uint8 [M, K/2], sx fp16 [M, K/64], xl1 fp32 [M, r])."""
+    """x: bf16 [M, K] on the GPU -> (qx uint8 [M, K/2], sx fp16 [ceil(K/256), M, 4]
+    (quad-major group scales), xl1 fp32 [M, r])."""
     M, K = x.shape
     dev = x.device
     qx = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
-    sx = torch.empty((M, K // 64), dtype=torch.float16, device=dev)
+    sx = torch.empty(((K // 64 + 3) // 4, M, 4), dtype=torch.float16, device=dev)
     xl1 = torch.empty((M, rank), dtype=torch.float32, device=dev) if rank else None
     svdq_quantize_act(x, M, K, x.stride(0), inv_lambda, l1t if rank else None, rank, qx, sx, xl1,
                       stream)

@@ -188,10 +188,13 @@ __global__ __launch_bounds__(ROWS * 32) void act_quant_kernel(
     }
     __syncthreads();
 
-    // scales: one contiguous row segment per token row
-    for (int e = tid; e < ROWS * G; e += ROWS * 32) {
-        const int rr = e / G, gg = e % G;
-        if (m0 + rr < M) sx[(m0 + rr) * G + gg] = s_sx[e];
+    // scales, quad-major [G4][M][4]: quad q of the block's rows is one
+    // contiguous 8 * ROWS-byte segment; groups past the last one are 0
+    const int G4 = (G + 3) / 4;
+    for (int e = tid; e < ROWS * G4 * 4; e += ROWS * 32) {
+        const int q = e / (ROWS * 4), rr = (e / 4) % ROWS, gg = 4 * q + (e & 3);
+        if (m0 + rr < M)
+            sx[((int64_t)q * M + m0 + rr) * 4 + (e & 3)] = gg < G ? s_sx[rr * G + gg] : (uint16_t)0;
     }
     if constexpr (RT > 0) {
         const int RK = 16 * RT;

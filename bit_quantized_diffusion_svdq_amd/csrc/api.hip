@@ -141,7 +141,7 @@ const char* svdq_status_string(svdq_status s) {
 
 const char* svdq_last_error(void) { return g_last_error.c_str(); }
 
-int svdq_version(void) { return 200; }
+int svdq_version(void) { return 300; }
 
 svdq_status svdq_check_device(int device) {
     svdq_status s = check_device_id(device);
@@ -163,10 +163,10 @@ svdq_status svdq_quantize_act(const void* x, int64_t M, int64_t K, int64_t ldx,
     if (M == 0) { g_last_error.clear(); return SVDQ_OK; }   // empty batch: nothing to read or write
     if (!x || !qx || !sx_f16) return fail(SVDQ_ERR_NULL, "x, qx and sx_f16 are required");
     if (rank > 0 && (!l1t || !xl1)) return fail(SVDQ_ERR_NULL, "rank %d needs l1t and xl1", rank);
-    if (!aligned(x, 16) || !aligned(qx, 16) || !aligned(sx_f16, 4) ||
+    if (!aligned(x, 16) || !aligned(qx, 16) || !aligned(sx_f16, 16) ||
         (inv_lambda && !aligned(inv_lambda, 16)) ||
         (rank > 0 && (!aligned(l1t, 16) || !aligned(xl1, 16))))
-        return fail(SVDQ_ERR_ALIGN, "x, inv_lambda, l1t, qx, xl1 need 16-byte alignment, sx_f16 4 bytes");
+        return fail(SVDQ_ERR_ALIGN, "x, inv_lambda, l1t, qx, sx_f16, xl1 need 16-byte alignment");
     if ((s = check_current_device()) != SVDQ_OK) return s;
     return launched(launch_act_quant((const uint16_t*)x, M, K, ldx, inv_lambda,
                                      rank > 0 ? (const uint16_t*)l1t : nullptr, rank, qx,
@@ -187,6 +187,8 @@ svdq_status svdq_gemm_w4a4(const uint8_t* qx, const void* sx_f16, int64_t M, int
     if (N <= 0 || N % 8) return fail(SVDQ_ERR_SHAPE, "N = %lld must be a positive multiple of 8", (long long)N);
     if (M > ((int64_t)1 << 31) || N > ((int64_t)1 << 31)) return fail(SVDQ_ERR_SHAPE, "M or N too large");
     if ((s = check_gemm_bytes(M, N, K)) != SVDQ_OK) return s;
+    if ((M + 256) * rank * 4 >= ((int64_t)1 << 31) || (N + 256) * rank * 2 >= ((int64_t)1 << 31))
+        return fail(SVDQ_ERR_SHAPE, "(M + 256) * rank * 4 and (N + 256) * rank * 2 must stay below 2^31 bytes");
     if (ldy < N) return fail(SVDQ_ERR_SHAPE, "ldy = %lld < N = %lld", (long long)ldy, (long long)N);
     if (ldy % 8) return fail(SVDQ_ERR_ALIGN, "ldy = %lld must be a multiple of 8", (long long)ldy);
     if (act != SVDQ_ACT_NONE && act != SVDQ_ACT_GELU_TANH)
@@ -196,10 +198,10 @@ svdq_status svdq_gemm_w4a4(const uint8_t* qx, const void* sx_f16, int64_t M, int
     if (M == 0) { g_last_error.clear(); return SVDQ_OK; }   // empty batch
     if (!qx || !sx_f16 || !qw || !sw_f16 || !y) return fail(SVDQ_ERR_NULL, "qx, sx, qw, sw and y are required");
     if (rank > 0 && (!xl1 || !l2t)) return fail(SVDQ_ERR_NULL, "rank %d needs xl1 and l2t", rank);
-    if (!aligned(qx, 16) || !aligned(qw, 16) || !aligned(y, 16) || !aligned(sx_f16, 4) ||
-        !aligned(sw_f16, 4) || (bias && !aligned(bias, 2)) ||
+    if (!aligned(qx, 16) || !aligned(qw, 16) || !aligned(y, 16) || !aligned(sx_f16, 16) ||
+        !aligned(sw_f16, 16) || (bias && !aligned(bias, 2)) ||
         (rank > 0 && (!aligned(xl1, 16) || !aligned(l2t, 16))))
-        return fail(SVDQ_ERR_ALIGN, "qx, qw, xl1, l2t, y need 16-byte alignment, scales 4 bytes");
+        return fail(SVDQ_ERR_ALIGN, "qx, sx, qw, sw, xl1, l2t, y need 16-byte alignment");
     if ((s = check_current_device()) != SVDQ_OK) return s;
     return launched(launch_gemm_w4a4(qx, (const uint16_t*)sx_f16, qw, (const uint16_t*)sw_f16,
                                      rank > 0 ? xl1 : nullptr, rank > 0 ? (const uint16_t*)l2t : nullptr,

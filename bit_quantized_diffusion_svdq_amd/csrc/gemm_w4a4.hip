@@ -16,11 +16,15 @@
 //    covers whole 128-byte lines of 8 rows (the vector memory pipeline's cost
 //    follows the number of lines an instruction touches), and the chunk a
 //    lane fetches is XOR-swizzled so the lanes that consume a group in the
-//    MFMA read LDS without bank conflicts; the scales of the same four groups
-//    come as a 32-byte window per row that absorbs any row misalignment;
+//    MFMA read LDS without bank conflicts; the scales are stored quad-major
+//    (the four scales of a row's quad are 8 bytes, the rows of one quad are
+//    contiguous), so one 1 KB load brings a quad's scales for 128 rows and
+//    one 8-byte LDS read gives a lane all four;
 //  - the two-sided scale S = sx (x) sw of a 32x32 block is an outer product
-//    that a v_mfma_f32_32x32x8_f16 with one non-zero k forms exactly, and the
-//    VALU does one FMA per output element and group, acc += P_g * S_g;
+//    that a v_mfma_f32_32x32x8_f16 forms exactly: A holds a row's four
+//    scales of the quad in k = 0..3, B the column's scale of group g in
+//    k = g mod 4 and zeros elsewhere; the VALU does one FMA per output
+//    element and group, acc += P_g * S_g;
 //  - products and scale products of consecutive blocks alternate between two
 //    register sets, so one wave's FMAs for a block run while the matrix pipe
 //    works on its next block;
@@ -42,14 +46,16 @@ struct Cfg {
     static constexpr int APW = ABLK / NW, BPW = BBLK / NW;
     // One quad slot (four groups): codes [block][8-row part][lane][16 B]
     // (A blocks, then B blocks; see the swizzle at the loads) and, in a slot
-    // of its own, the scale windows [tile row][32 B] (A rows, then B rows).
-    static constexpr int CODE_SLOT = SBLK * 4096, SC_SLOT = (BM + BN) * 32;
+    // of its own, the scales [tile row][4] fp16 (A rows, then B rows).
+    static constexpr int CODE_SLOT = SBLK * 4096, SC_SLOT = (BM + BN) * 8;
     // bf16 output staging for the epilogue: OUT_ROWS rows at a time in code slot 0
     static constexpr int OUT_LD = BN + 8, OUT_ROWS = 32 * TM;
     static_assert(TM * 32 * WGM == BM && TN * 32 * WGN == BN, "tile shape");
     static_assert(APW * NW == ABLK && BPW * NW == BBLK && APW >= 1 && BPW >= 1,
                   "blocks split evenly over the waves");
     static_assert((TM * TN) % 2 == 0, "blocks per wave must be even for the register rotation");
+    static_assert(BM * 8 == 1024 && BN * 8 == 1024 && NW % 2 == 0,
+                  "a quad's scales of the tile rows are one 64-lane load per side");
     static_assert(OUT_ROWS * OUT_LD * 2 <= CODE_SLOT, "epilogue staging fits one slot");
     static_assert(2 * (CODE_SLOT + SC_SLOT) * MINB <= 160 * 1024, "LDS budget");
 };
@@ -133,11 +139,9 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_w4a4_kernel(
     // into the scalar offset. Byte offsets fit in 31 bits (checked on the host).
     const rsrc_t rqa = make_rsrc(qx, M * (K / 2));
     const rsrc_t rqb = make_rsrc(qw, N * (K / 2));
-    // the buffer range check zeroes any dword that is partly out of range, so
-    // the scale ranges are rounded up to whole dwords (the extra two bytes
-    // share the last dword of the array, so the read stays on its page)
-    const rsrc_t rsa = make_rsrc(sx, (MODE != 2) ? (M * G * 2 + 3) / 4 * 4 : 0);
-    const rsrc_t rsb = make_rsrc(sw, (MODE != 2) ? (N * G * 2 + 3) / 4 * 4 : 0);
+    // scales: [G4][rows][4] fp16, quads past the end read 0
+    const rsrc_t rsa = make_rsrc(sx, (MODE != 2) ? (int64_t)((G + 3) / 4) * M * 8 : 0);
+    const rsrc_t rsb = make_rsrc(sw, (MODE != 2) ? (int64_t)((G + 3) / 4) * N * 8 : 0);
     const int lr8 = lane >> 3;                       // row within an 8-row part
     const int cpe = (lane & 7) ^ (lr8 >> 1);          // chunk for even parts (f = lr8 / 2)
     const int cpo = cpe ^ 4;                          // odd parts (f = 4 + lr8 / 2)
@@ -154,23 +158,18 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_w4a4_kernel(
         vcb_e[k] = (int)(r * (K / 2)) + 16 * cpe;
         vcb_o[k] = (int)(r * (K / 2)) + 16 * cpo;
     }
-    // Scales: the quad's four fp16 scales of a row are 8 bytes at
-    // 2 (row G + 4 q), inside the 32-byte window that starts at the 16-byte
-    // boundary below 2 row G + 8 q (2 row G mod 16 is the row's offset in
-    // the window). One load covers 32 rows: lane l takes 16 bytes of row l / 2.
-    int vsa[C::APW], vsb[C::BPW];
-#pragma unroll
-    for (int k = 0; k < C::APW; ++k) {
-        const int64_t r = m0 + (int64_t)(wave + k * C::NW) * 32 + (lane >> 1);
-        vsa[k] = (int)((r * G * 2) & ~(int64_t)15) + 16 * (lane & 1);
-    }
-#pragma unroll
-    for (int k = 0; k < C::BPW; ++k) {
-        const int64_t r = n0 + (int64_t)(wave + k * C::NW) * 32 + (lane >> 1);
-        vsb[k] = (int)((r * G * 2) & ~(int64_t)15) + 16 * (lane & 1);
-    }
-    // quad q into a code slot and a scale slot (quads past the end read the
-    // next row's bytes or 0; their groups get a zero scale where read)
+    // Scales: quad q of the tile's A rows is the 1 KB at 8 (q M + m0) and of
+    // its B rows the 1 KB at 8 (q N + n0): even waves load A's into the first
+    // half of the scale slot, odd waves B's into the second half (waves 2 and
+    // 3 repeat waves 0 and 1 with identical bytes, which keeps the loop free
+    // of branches). Rows past the end of the matrix read the next quad's
+    // scales or 0 (their outputs are never stored).
+    const bool sb_side = (wave & 1) != 0;
+    const rsrc_t rss = sb_side ? rsb : rsa;
+    const int vss = (int)((sb_side ? n0 : m0) * 8) + 16 * lane;
+    const int sq_stride = (int)((sb_side ? N : M) * 8);
+    // quad q into a code slot and a scale slot (groups past the end of K
+    // read the next row's codes or 0, and zero scales)
     auto load_quad = [&](char* cs, char* ss, int q) __attribute__((always_inline)) {
         const int so = q * 128;
 #pragma unroll
@@ -187,14 +186,8 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_w4a4_kernel(
             for (int i = 0; i < 4; ++i)
                 dma16(rqb, dst + i * 1024, (i & 1) ? vcb_o[k] : vcb_e[k], so + 8 * i * (int)(K / 2));
         }
-        if constexpr (MODE != 2) {
-#pragma unroll
-            for (int k = 0; k < C::APW; ++k)
-                dma16(rsa, ss + (wave + k * C::NW) * 32 * 32, vsa[k], q * 8);
-#pragma unroll
-            for (int k = 0; k < C::BPW; ++k)
-                dma16(rsb, ss + (BM + (wave + k * C::NW) * 32) * 32, vsb[k], q * 8);
-        }
+        if constexpr (MODE != 2)
+            dma16(rss, ss + (sb_side ? BM * 8 : 0), vss, q * sq_stride);
     };
     // Wait for this wave's loads (the quad loaded one step ago) and publish
     // them with a barrier.
@@ -213,95 +206,126 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_w4a4_kernel(
 
     load_quad(cs0, ss0, 0);
 
-    // low-rank branch while the first quad is in flight: acc = xl1 L2
+    // ---- low-rank branch: acc = xl1 L2 --------------------------------------
+    // 32 ranks at a time, through code slot 1 (free until quad 1 is loaded):
+    // the chunk's xl1 rows of the tile (128 B each, fp32) at 0 and its l2t
+    // rows (64 B each, bf16) at 16 KB, both brought by line-friendly loads
+    // into LDS with the chunks of a row XOR-swizzled (16-byte chunk c of tile
+    // row r at position c ^ ((r / 2) % 8) for xl1, c ^ ((r / 4) % 4) for l2t)
+    // so the MFMA lanes read them without bank conflicts. The first chunk
+    // flies together with quad 0. A last chunk of 16 ranks reads 16 more
+    // bytes per row that are never used (or 0 past the end of the array).
     if (MODE != 2 && rank > 0) {
-        const int h = lane >> 5;
-        for (int ks = 0; ks < rank / 16; ++ks) {
-            v8bf ah[TM], al[TM], b[TN];
+        const rsrc_t rxl = make_rsrc(xl1, M * rank * 4);
+        const rsrc_t rl2 = make_rsrc(l2t, N * rank * 2);
+        const int vxl = (int)((m0 + 8 * wave + lr8) * rank * 4) + 16 * ((wave & 1) ? cpo : cpe);
+        const int vl2 = (int)((n0 + 16 * wave + (lane >> 2)) * rank * 2) + 16 * ((lane & 3) ^ ((lane >> 4) & 3));
+        const int h = lane >> 5, r32l = lane & 31;
+        for (int r0 = 0; r0 < rank; r0 += 32) {
 #pragma unroll
-            for (int i = 0; i < TM; ++i) {
-                int64_t row = m0 + wm * 32 * TM + i * 32 + (lane & 31);
-                row = row < M ? row : M - 1;
-                const float4 u0 = *(const float4*)(xl1 + row * rank + ks * 16 + 8 * h);
-                const float4 u1 = *(const float4*)(xl1 + row * rank + ks * 16 + 8 * h + 4);
-                const float xv[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+            for (int k = 0; k < 4; ++k)
+                dma16(rxl, cs1 + (wave + 4 * k) * 1024, vxl, k * 32 * rank * 4 + r0 * 4);
 #pragma unroll
-                for (int jj = 0; jj < 8; ++jj) {
-                    const __bf16 hb = (__bf16)xv[jj];
-                    ah[i][jj] = hb;
-                    al[i][jj] = (__bf16)(xv[jj] - (float)hb);
+            for (int k = 0; k < 2; ++k)
+                dma16(rl2, cs1 + 16384 + (wave + 4 * k) * 1024, vl2, k * 64 * rank * 2 + r0 * 2);
+            publish();
+            const int nks = (rank - r0) >= 32 ? 2 : 1;
+            for (int ks = 0; ks < nks; ++ks) {
+                v8bf ah[TM], al[TM], b[TN];
+#pragma unroll
+                for (int i = 0; i < TM; ++i) {
+                    const int tr = wm * 32 * TM + i * 32 + r32l;
+                    const int sw8 = (tr >> 1) & 7, c0 = 4 * ks + 2 * h;
+                    const float4 u0 = *(const float4*)(cs1 + tr * 128 + 16 * (c0 ^ sw8));
+                    const float4 u1 = *(const float4*)(cs1 + tr * 128 + 16 * ((c0 + 1) ^ sw8));
+                    const float xv[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+#pragma unroll
+                    for (int jj = 0; jj < 8; ++jj) {
+                        const __bf16 hb = (__bf16)xv[jj];
+                        ah[i][jj] = hb;
+                        al[i][jj] = (__bf16)(xv[jj] - (float)hb);
+                    }
                 }
-            }
-#pragma unroll
-            for (int j = 0; j < TN; ++j) {
-                int64_t col = n0 + wn * 32 * TN + j * 32 + (lane & 31);
-                col = col < N ? col : N - 1;
-                b[j] = *(const v8bf*)(l2t + col * rank + ks * 16 + 8 * h);
-            }
-#pragma unroll
-            for (int i = 0; i < TM; ++i)
 #pragma unroll
                 for (int j = 0; j < TN; ++j) {
-                    acc[i][j] = mfma_bf16_32x32x16(ah[i], b[j], acc[i][j]);
-                    acc[i][j] = mfma_bf16_32x32x16(al[i], b[j], acc[i][j]);
+                    const int tc = wn * 32 * TN + j * 32 + r32l;
+                    b[j] = *(const v8bf*)(cs1 + 16384 + tc * 64 + 16 * ((2 * ks + h) ^ ((tc >> 2) & 3)));
                 }
+#pragma unroll
+                for (int i = 0; i < TM; ++i)
+#pragma unroll
+                    for (int j = 0; j < TN; ++j) {
+                        acc[i][j] = mfma_bf16_32x32x16(ah[i], b[j], acc[i][j]);
+                        acc[i][j] = mfma_bf16_32x32x16(al[i], b[j], acc[i][j]);
+                    }
+            }
+            lds_barrier();     // slot 1 is read by every wave before it is refilled
         }
     }
 
     // ---- operands ---------------------------------------------------------
     // Codes of group gq (0..3) of a quad, for this lane (row r = lane % 32 of
-    // a block, half h = lane / 32): chunk 2 gq + h of the row. The scale of
-    // group gq of row r sits in its window at byte (2 r_glob G mod 16) + 2 gq.
-    // A's scale operand is {s, 0} with s = 0 in lanes 32..63 and for groups
-    // past the end of K; B's is {s, 0} (its lanes 32..63 meet A's zeros).
+    // a block, half h = lane / 32): chunk 2 gq + h of the row. The LDS
+    // addresses are kept whole in registers (wave block + lane chunk) so each
+    // read is one instruction with the slot and block as its immediate.
     const int r32 = lane & 31, hh = lane >> 5;
-    int xo[4];
-#pragma unroll
-    for (int gq = 0; gq < 4; ++gq) xo[gq] = 128 * r32 + 16 * ((2 * gq + hh) ^ ((r32 >> 1) & 7));
-    int soa[TM], sob[TN];
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
-        const int tr = (wm * TM + i) * 32 + r32;
-        soa[i] = tr * 32 + (int)(((m0 + tr) * G * 2) & 15);
-    }
-#pragma unroll
-    for (int j = 0; j < TN; ++j) {
-        const int tr = (wn * TN + j) * 32 + r32;
-        sob[j] = (BM + tr) * 32 + (int)(((n0 + tr) * G * 2) & 15);
-    }
     const int ablk = wm * TM, bblk = C::ABLK + wn * TN;
+    int xa[4], xb[4];
+#pragma unroll
+    for (int gq = 0; gq < 4; ++gq) {
+        const int xo = 128 * r32 + 16 * ((2 * gq + hh) ^ ((r32 >> 1) & 7));
+        xa[gq] = ablk * 4096 + xo;
+        xb[gq] = bblk * 4096 + xo;
+        order_point(xa[gq], xb[gq]);
+    }
+    // scales of the quad: A frag i reads tile row (wm TM + i) 32 + r32, B frag
+    // j tile row BM + (wn TN + j) 32 + r32, 8 bytes each
+    int sra = (wm * TM * 32 + r32) * 8, srb = (BM + wn * TN * 32 + r32) * 8;
+    order_point(sra, srb);
+    // B's scale operand of group gq: the column's scale in k = gq (lanes
+    // 0..31, which hold k = 0..3), zero in every other k; lanes 32..63 hold
+    // k = 4..7 and are all zero
+    const uint32_t msk_lo = hh ? 0u : 0xffffu, msk_hi = hh ? 0u : 0xffff0000u;
     v6i fa[TM], fb[TN];
-    v2i so[TM], wo[TN];
     uint4 ra_n[TM], rb_n[TN];
-#pragma unroll
-    for (int i = 0; i < TM; ++i) so[i] = v2i{0, 0};
-#pragma unroll
-    for (int j = 0; j < TN; ++j) wo[j] = v2i{0, 0};
-    // operand i / j of group gq of the quad in (cs, ss); `real`: the group
-    // lies inside K
-    auto read_a = [&](const char* cs, const char* ss, int gq, int i, bool real) __attribute__((always_inline)) {
-        ra_n[i] = *(const uint4*)(cs + (ablk + i) * 4096 + xo[gq]);
-        if constexpr (MODE != 2) {
-            const int s = (int)*(const uint16_t*)(ss + soa[i] + 2 * gq);
-            so[i][0] = (real && hh == 0) ? s : 0;
-        }
+    uint2 sca[2][TM], scb[2][TN];          // a quad's raw scales, by slot parity
+    auto read_a = [&](const char* cs, int gq, int i) __attribute__((always_inline)) {
+        ra_n[i] = *(const uint4*)(cs + i * 4096 + xa[gq]);
     };
-    auto read_b = [&](const char* cs, const char* ss, int gq, int j) __attribute__((always_inline)) {
-        rb_n[j] = *(const uint4*)(cs + (bblk + j) * 4096 + xo[gq]);
-        if constexpr (MODE != 2)
-            wo[j][0] = (int)*(const uint16_t*)(ss + sob[j] + 2 * gq);
+    auto read_b = [&](const char* cs, int gq, int j) __attribute__((always_inline)) {
+        rb_n[j] = *(const uint4*)(cs + j * 4096 + xb[gq]);
+    };
+    auto read_sa = [&](const char* ss, int par, int i) __attribute__((always_inline)) {
+        if constexpr (MODE != 2) sca[par][i] = *(const uint2*)(ss + i * 256 + sra);
+    };
+    auto read_sb = [&](const char* ss, int par, int j) __attribute__((always_inline)) {
+        if constexpr (MODE != 2) scb[par][j] = *(const uint2*)(ss + j * 256 + srb);
+    };
+    // B scale operands, one pair per frag and half of the quad: only the
+    // non-zero dword is rewritten per group, the other stays 0
+    v2i bso[TN][2];
+#pragma unroll
+    for (int j = 0; j < TN; ++j) bso[j][0] = bso[j][1] = v2i{0, 0};
+    auto b_scale = [&](const uint2& w, int gq, int j) __attribute__((always_inline)) {
+        const uint32_t m = (gq & 1) ? msk_hi : msk_lo;
+        if (gq < 2) bso[j][0][0] = (int)(w.x & m);
+        else bso[j][1][1] = (int)(w.y & m);
+        return bso[j][gq >> 1];
     };
 
     const v16f zero = {};
     // products and scale products of consecutive blocks, by parity
     v16f P0 = zero, P1 = zero, S0 = zero, S1 = zero;
 
-    // One group g (raw operands read). For block b = (i, j): operands used
-    // for the first time are turned into FP6; the two MFMAs of b, then the
-    // FMAs of block b - 1 (for b = 0: the last block of the previous group,
-    // parity 1); operands used for the last time are read for the next group
-    // (group ngq of the quad in (ncs, nss); nreal = it lies inside K).
-    auto group = [&](int g, const char* ncs, const char* nss, int ngq, bool nreal) __attribute__((always_inline)) {
+    // One group g = 4 q + gq of the quad whose scales have slot parity par
+    // (raw code operands read). For block b = (i, j): operands used for the
+    // first time are turned into FP6; the two MFMAs of b, then the FMAs of
+    // block b - 1 (for b = 0: the last block of the previous group, parity
+    // 1); operands used for the last time are read for the next group (group
+    // ngq of the quad in ncs; at the end of a quad, also the next quad's
+    // scales from nss, into the other parity).
+    auto group = [&](int g, int gq, int par, const char* ncs, const char* nss, int ngq)
+        __attribute__((always_inline)) {
 #pragma unroll
         for (int bl = 0; bl < TM * TN; ++bl) {
             const int i = bl / TN, j = bl % TN;
@@ -323,10 +347,11 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_w4a4_kernel(
                 v16f& Sn = (bl & 1) ? S1 : S0;
                 const v16f& Pp = (bl & 1) ? P0 : P1;
                 const v16f& Sp = (bl & 1) ? S0 : S1;
+                const v2i as = v2i{(int)sca[par][i].x, (int)sca[par][i].y};
+                const v2i bs = b_scale(scb[par][j], gq, j);
                 order_point(fa[i], fb[j]);
                 Pn = mfma_fp6_32x32x64(fa[i], fb[j], zero);
-                order_point(so[i], wo[j]);
-                Sn = mfma_f16_32x32x8(__builtin_bit_cast(v4h, so[i]), __builtin_bit_cast(v4h, wo[j]), zero);
+                Sn = mfma_f16_32x32x8(__builtin_bit_cast(v4h, as), __builtin_bit_cast(v4h, bs), zero);
                 // both MFMAs issue before the FMAs of the previous block,
                 // whose inputs are long complete, so one wave keeps the
                 // matrix pipe and the VALU busy at the same time
@@ -335,39 +360,46 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_w4a4_kernel(
                 for (int e = 0; e < 16; ++e) acc[pi][pj][e] = __builtin_fmaf(Pp[e], Sp[e], acc[pi][pj][e]);
                 order_point(acc[pi][pj]);
             }
-            if (j == TN - 1) read_a(ncs, nss, ngq, i, nreal);
-            if (i == TM - 1) read_b(ncs, nss, ngq, j);
+            if (j == TN - 1) {
+                read_a(ncs, ngq, i);
+                if (gq == 3) read_sa(nss, par ^ 1, i);
+            }
+            if (i == TM - 1) {
+                read_b(ncs, ngq, j);
+                if (gq == 3) read_sb(nss, par ^ 1, j);
+            }
             __builtin_amdgcn_sched_barrier(0);
         }
     };
 
-    // prologue: quad 0 published, quad 1 in flight, group 0's operands read
+    // prologue: quad 0 published, quad 1 in flight, group 0's operands and
+    // quad 0's scales read
     publish();
     load_quad(cs1, ss1, 1);
 #pragma unroll
-    for (int i = 0; i < TM; ++i) read_a(cs0, ss0, 0, i, true);
+    for (int i = 0; i < TM; ++i) { read_a(cs0, 0, i); read_sa(ss0, 0, i); }
 #pragma unroll
-    for (int j = 0; j < TN; ++j) read_b(cs0, ss0, 0, j);
+    for (int j = 0; j < TN; ++j) { read_b(cs0, 0, j); read_sb(ss0, 0, j); }
 
-    // Step q (quad q in slots cur): groups 4q .. 4q + 2, each reading the
-    // next one's operands; publish quad q + 1 (loaded one step ago); load
-    // quad q + 2 into quad q's slots, which nobody reads any more; group
-    // 4q + 3, reading group 4q + 4's operands from quad q + 1. The step count
-    // is rounded up to an even number so the loop body has no branches
-    // (which would blur the compiler's per-slot tracking of loads into LDS);
-    // the extra groups carry zero scales.
-    auto step = [&](int q, char* cs, char* ss, char* ncs, char* nss) __attribute__((always_inline)) {
+    // Step q (quad q in slots cur, scale parity par): groups 4q .. 4q + 2,
+    // each reading the next one's operands; publish quad q + 1 (loaded one
+    // step ago); load quad q + 2 into quad q's slots, which nobody reads any
+    // more; group 4q + 3, reading group 4q + 4's operands and quad q + 1's
+    // scales. The step count is rounded up to an even number so the loop
+    // body has no branches (which would blur the compiler's per-slot
+    // tracking of loads into LDS); the extra groups have zero scales.
+    auto step = [&](int q, int par, char* cs, char* ss, char* ncs, char* nss) __attribute__((always_inline)) {
         const int g0 = 4 * q;
-        group(g0, cs, ss, 1, g0 + 1 < G);
-        group(g0 + 1, cs, ss, 2, g0 + 2 < G);
-        group(g0 + 2, cs, ss, 3, g0 + 3 < G);
+        group(g0, 0, par, cs, ss, 1);
+        group(g0 + 1, 1, par, cs, ss, 2);
+        group(g0 + 2, 2, par, cs, ss, 3);
         publish();
         load_quad(cs, ss, q + 2);
-        group(g0 + 3, ncs, nss, 0, g0 + 4 < G);
+        group(g0 + 3, 3, par, ncs, nss, 0);
     };
     for (int q = 0; q < NQ; q += 2) {
-        step(q, cs0, ss0, cs1, ss1);
-        step(q + 1, cs1, ss1, cs0, ss0);
+        step(q, 0, cs0, ss0, cs1, ss1);
+        step(q + 1, 1, cs1, ss1, cs0, ss0);
     }
     if constexpr (MODE != 2) {
 #pragma unroll

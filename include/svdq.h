@@ -40,6 +40,11 @@
  *    magnitude or sign bit and any 64-bit pattern is valid. (The layout
  *    follows gfx950's FP6 MFMA operand stream; the pages fix only that codes
  *    are 4-bit.)
+ *  - SVDQ group scales (format v3): fp16, "quad-major". With G = K / 64 and
+ *    G4 = ceil(G / 4), the scales of a matrix with `rows` rows are an array
+ *    [G4][rows][4]: element [q][r][e] is the scale of group 4q + e of row r,
+ *    so a row's four scales of one quad are 8 consecutive bytes and the
+ *    rows of one quad are contiguous. Groups 4q + e >= G hold 0.
  *  - AWQ 4-bit codes (format v1): unsigned nibbles 0..15, byte i of a row
  *    holds element 2i in bits 0-3 and element 2i+1 in bits 4-7.
  *  - bf16 and fp16 values are passed as their 16-bit patterns.
@@ -92,7 +97,7 @@ int svdq_version(void);
  *             NULL iff rank == 0
  *  rank       0..128, multiple of 16
  *  qx         out: packed codes [M][K/2]
- *  sx_f16     out: fp16 scales [M][K/64]
+ *  sx_f16     out: fp16 scales [ceil(K/256)][M][4] (quad-major, zero padded)
  *  xl1        out: fp32 [M][rank] = X_hat L1 (NULL iff rank == 0)
  *
  * Per element: x_hat = fp32(x) * inv_lambda[k] (one fp32 multiply). Per
@@ -100,7 +105,7 @@ int svdq_version(void);
  * if s == 0 all codes are 0, else q = clamp(rtne(x_hat * fp32(1 / s)), -7, 7).
  * qx and sx are bit-exact with that definition. xl1 is accumulated in fp32
  * (relative error about 1e-6).
- * Alignment: x, inv_lambda, l1t, qx, xl1 16-byte aligned; sx_f16 4-byte aligned.
+ * Alignment: x, inv_lambda, l1t, qx, sx_f16, xl1 16-byte aligned.
  */
 svdq_status svdq_quantize_act(const void* x, int64_t M, int64_t K, int64_t ldx,
                               const float* inv_lambda, const void* l1t, int32_t rank,
@@ -111,18 +116,21 @@ svdq_status svdq_quantize_act(const void* x, int64_t M, int64_t K, int64_t ldx,
  * bias and optional GELU(tanh) in the epilogue (the remio.ai page, same
  * section: the up-projection was fused with the 4-bit matmul).
  *
- *  qx, sx_f16  [M][K/2] codes and fp16 [M][K/64] scales from svdq_quantize_act
- *  qw, sw_f16  [N][K/2] weight codes and fp16 [N][K/64] scales (residual R^T)
+ *  qx, sx_f16  [M][K/2] codes and fp16 [ceil(K/256)][M][4] quad-major scales
+ *              from svdq_quantize_act
+ *  qw, sw_f16  [N][K/2] weight codes and fp16 [ceil(K/256)][N][4] quad-major
+ *              scales (residual R^T); padding groups must hold 0
  *  xl1         fp32 [M][rank] from svdq_quantize_act (NULL iff rank == 0)
  *  l2t         bf16 [N][rank]: row n is column n of L2 (NULL iff rank == 0)
  *  bias        bf16 [N] or NULL
  *  act         SVDQ_ACT_NONE or SVDQ_ACT_GELU_TANH (applied in fp32)
  *  y           out: [M][ldy] of y_dtype (bf16 RTNE of the fp32 result, or fp32)
  *
- * N % 8 == 0, ldy >= N, ldy % 8 == 0; (M + 256) * K / 2 and
- * (N + 256) * K / 2 must stay below 2^31 (code bytes plus a tile of slack). The group partials P_g are exact; the fp32 result
+ * N % 8 == 0, ldy >= N, ldy % 8 == 0; (M + 256) * K / 2, (N + 256) * K / 2,
+ * (M + 256) * rank * 4 and (N + 256) * rank * 2 must stay below 2^31 (byte
+ * offsets plus a tile of slack). The group partials P_g are exact; the fp32 result
  * matches the fp64 definition to about 1e-6 relative.
- * Alignment: every pointer 16-byte aligned except sx_f16 / sw_f16 (4 bytes).
+ * Alignment: every pointer 16-byte aligned (bias: 2 bytes).
  */
 svdq_status svdq_gemm_w4a4(const uint8_t* qx, const void* sx_f16, int64_t M, int64_t K,
                            const uint8_t* qw, const void* sw_f16, int64_t N,

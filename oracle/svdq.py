@@ -35,7 +35,12 @@ the low half when that offset is an exponent position of T[0:32), else in
 the high half, where it is an exponent position of T[64:96)). So the
 word is a bit permutation of 16 sign-magnitude codes and the three 32-bit
 thirds of T come back with masks alone. Weights are stored transposed,
-[N][K/2]; scales are fp16 [rows][K/64].
+[N][K/2].
+
+Storage format of the scales (format v3): fp16, "quad-major": the scales of
+the groups 4q .. 4q+3 of a row are 8 consecutive bytes, and quad q of all rows
+comes before quad q+1, i.e. an array [ceil(G/4)][rows][4]; groups past the
+last one (G = K/64 not a multiple of 4) hold 0.
 """
 from __future__ import annotations
 
@@ -210,6 +215,30 @@ def unpack_int4(packed: np.ndarray) -> np.ndarray:
         neg = ((word >> np.uint64(_WORD_POS[e, 3])) & np.uint64(1)).astype(bool)
         out[:, :, e] = np.where(neg, -mag, mag)
     return out.reshape(rows, nb * 2)
+
+
+def pack_scales(scales: np.ndarray) -> np.ndarray:
+    """fp16 scales [rows, G] -> the quad-major storage array
+    [ceil(G/4), rows, 4] (format v3, see the module docstring)."""
+    s = np.asarray(scales, np.float16)
+    rows, G = s.shape
+    G4 = (G + 3) // 4
+    out = np.zeros((G4, rows, 4), np.float16)
+    for g in range(G):
+        out[g // 4, :, g % 4] = s[:, g]
+    return out
+
+
+def unpack_scales(packed: np.ndarray, G: int) -> np.ndarray:
+    """Inverse of pack_scales -> fp16 [rows, G] (the padding is dropped)."""
+    p = np.asarray(packed, np.float16)
+    G4, rows, four = p.shape
+    if four != 4 or G4 != (G + 3) // 4:
+        raise ValueError("not a quad-major scale array for this G")
+    out = np.empty((rows, G), np.float16)
+    for g in range(G):
+        out[:, g] = p[g // 4, :, g % 4]
+    return out
 
 
 @dataclass

@@ -23,6 +23,13 @@ def dev_f16(a: np.ndarray) -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(np.asarray(a, np.float16))).cuda()
 
 
+def dev_scales(s: np.ndarray) -> torch.Tensor:
+    """fp16 group scales [rows, G] -> the device array in the library's
+    quad-major layout [ceil(G/4)][rows][4]."""
+    from oracle import svdq as osv
+    return dev_f16(osv.pack_scales(s))
+
+
 def dev(a: np.ndarray) -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
@@ -53,7 +60,7 @@ class DevSvdq:
         self.l1t = dev_u16(np.ascontiguousarray(w.l1.T)) if w.rank else None
         self.l2t = dev_u16(np.ascontiguousarray(w.l2.T)) if w.rank else None
         self.qw = dev(w.qw)
-        self.sw = dev_f16(w.sw)
+        self.sw = dev_scales(w.sw)
         self.bias = dev_u16(w.bias) if w.bias is not None else None
 
 

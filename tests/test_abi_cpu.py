@@ -46,7 +46,7 @@ def test_status_strings(lib):
     for s in range(7):
         assert lib.svdq_status_string(s)
     assert lib.svdq_status_string(99) == b"unknown status"
-    assert lib.svdq_version() == 200
+    assert lib.svdq_version() == 300
 
 
 def _act(lib, **kw):
@@ -82,6 +82,8 @@ def _gemm(lib, **kw):
     (dict(ldy=132), ALIGN), (dict(act=2), UNSUP), (dict(ydt=3), UNSUP), (dict(qw=None), NULL),
     (dict(y=None), NULL), (dict(xl1=None), NULL), (dict(rank=20), SHAPE), (dict(qw=C + 4), ALIGN),
     (dict(y=E + 65536 + 8), ALIGN), (dict(M=1 << 20, K=4096), SHAPE), (dict(N=1 << 20, K=4096), SHAPE),
+    (dict(M=1 << 22, K=64, rank=128), SHAPE), (dict(N=1 << 23, K=64, rank=128), SHAPE),
+    (dict(sx=B + 8), ALIGN), (dict(sw=D + 8), ALIGN),
 ])
 def test_gemm_rejects(lib, kw, status):
     assert _gemm(lib, **kw) == status

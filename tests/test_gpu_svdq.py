@@ -15,7 +15,7 @@ import torch
 import synth
 from oracle import numfmt, svdq as osv
 from gpu_util import (DevSvdq, assert_bf16_is_rounded_fp32, assert_bf16_output,
-                      assert_fp32_output, dev, dev_f16, dev_u16, fp32_bound, host_bf16_f64,
+                      assert_fp32_output, dev, dev_f16, dev_scales, dev_u16, fp32_bound, host_bf16_f64,
                       host_u16, magnitude_sum, note, rel_fro)
 
 pytestmark = pytest.mark.gpu
@@ -38,7 +38,8 @@ def run_act(x_bits, dw, rank):
 
 def check_act(qa, qx, sx, xl1, rank):
     assert np.array_equal(qx.cpu().numpy(), qa.qx), "packed codes differ"
-    assert np.array_equal(sx.cpu().numpy().view(np.uint16), qa.sx.view(np.uint16)), "scales differ"
+    assert np.array_equal(sx.cpu().numpy().view(np.uint16),
+                          osv.pack_scales(qa.sx).view(np.uint16)), "scales differ"
     if rank:
         e = rel_fro(xl1.cpu().numpy(), qa.xl1)
         assert e <= 1e-4, e
@@ -129,7 +130,7 @@ def test_partials_qkv_sampled(rect):
 
 
 def gemm_gpu(qa, dw, rank, act="none", out=torch.bfloat16, bias=True):
-    return lib.w4a4_linear(dev(qa.qx), dev_f16(qa.sx), dev(qa.xl1) if rank else None, dw.qw, dw.sw,
+    return lib.w4a4_linear(dev(qa.qx), dev_scales(qa.sx), dev(qa.xl1) if rank else None, dw.qw, dw.sw,
                            dw.l2t, dw.bias if bias else None, rank, act=act, out_dtype=out)
 
 
@@ -159,9 +160,10 @@ def test_gemm_tiny(act, bias):
 
 
 def test_gemm_ragged_rank0_and_rank128():
-    """Ragged M and N against the 128 x 128 tile, rank 0 (plain W4A4) and
-    the maximum rank."""
-    for (M, K, N, r) in [(77, 192, 200, 0), (130, 320, 136, 128), (1, 64, 16, 16)]:
+    """Ragged M and N against the 128 x 128 tile, rank 0 (plain W4A4), the
+    maximum rank, and a rank that ends in a half chunk (32 + 16 ranks); K
+    values whose group count is not a multiple of 4 (padded scale quads)."""
+    for (M, K, N, r) in [(77, 192, 200, 0), (130, 320, 136, 128), (1, 64, 16, 16), (300, 704, 264, 48)]:
         note(f"gemm ragged M={M} K={K} N={N} r={r}")
         x = synth.make_matrix_bf16(M, K, seed=M, std=1.0)
         wb = synth.make_matrix_bf16(K, N, seed=N, std=0.05)
@@ -182,10 +184,10 @@ def test_gemm_empty_and_strided_output():
     dw = DevSvdq(w)
     qa = osv.quantize_act(li.x, w.inv_lambda, w.l1)
     y0 = torch.empty((0, cfg.N), dtype=torch.bfloat16, device="cuda")
-    lib.svdq_gemm_w4a4(dev(qa.qx), dev_f16(qa.sx), 0, cfg.K, dw.qw, dw.sw, cfg.N, None, None, 0,
+    lib.svdq_gemm_w4a4(dev(qa.qx), dev_scales(qa.sx), 0, cfg.K, dw.qw, dw.sw, cfg.N, None, None, 0,
                        None, 0, y0, 0, cfg.N)
     big = torch.full((cfg.M, cfg.N + 64), 7.0, dtype=torch.float32, device="cuda")
-    lib.svdq_gemm_w4a4(dev(qa.qx), dev_f16(qa.sx), cfg.M, cfg.K, dw.qw, dw.sw, cfg.N, dev(qa.xl1),
+    lib.svdq_gemm_w4a4(dev(qa.qx), dev_scales(qa.sx), cfg.M, cfg.K, dw.qw, dw.sw, cfg.N, dev(qa.xl1),
                        dw.l2t, cfg.rank, dw.bias, 0, big, 1, cfg.N + 64)
     torch.cuda.synchronize()
     yb = big.cpu().numpy()
@@ -219,7 +221,7 @@ def test_qkv_linear_full_size():
     torch.cuda.synchronize()
     assert rel_fro(yf.cpu().numpy()[rows], y64) <= 1e-5
     # GEMM alone on the oracle's operands
-    qxo, sxo, xlo = dev(qa.qx), dev_f16(qa.sx), dev(qa.xl1)
+    qxo, sxo, xlo = dev(qa.qx), dev_scales(qa.sx), dev(qa.xl1)
     y32 = lib.w4a4_linear(qxo, sxo, xlo, dw.qw, dw.sw, dw.l2t, dw.bias, cfg.rank, out_dtype=torch.float32)
     ybf = lib.w4a4_linear(qxo, sxo, xlo, dw.qw, dw.sw, dw.l2t, dw.bias, cfg.rank)
     torch.cuda.synchronize()

@@ -89,6 +89,23 @@ def test_pack_word_is_folded_e2m3_stream():
                 assert _e2m3_value(f) * 8 == c[r, 16 * w + e]
 
 
+def test_scale_layout_quad_major():
+    """Format v3 scale storage, checked element by element on a hand-written
+    case: G = 6 groups (one full quad and one half-filled quad) of 2 rows."""
+    s = np.array([[1, 2, 3, 4, 5, 6], [7, 8, 9, 10, 11, 12]], np.float16)
+    p = svdq.pack_scales(s)
+    exp = np.array([[[1, 2, 3, 4], [7, 8, 9, 10]],
+                    [[5, 6, 0, 0], [11, 12, 0, 0]]], np.float16)
+    assert p.shape == (2, 2, 4) and np.array_equal(p, exp)
+    # byte view: quad 1 of row 0 starts 2 rows * 8 bytes into the array
+    assert p.tobytes()[16:18] == np.float16(5).tobytes()
+    assert np.array_equal(svdq.unpack_scales(p, 6), s)
+    rng = np.random.default_rng(3)
+    for G in (1, 4, 7, 48):
+        r = rng.standard_normal((5, G)).astype(np.float16)
+        assert np.array_equal(svdq.unpack_scales(svdq.pack_scales(r), G), r)
+
+
 def test_qsym64_error_bound_and_idempotence():
     rng = np.random.default_rng(1)
     v = (rng.standard_normal((4000, 64)) * np.exp(rng.uniform(-8, 8, (4000, 1)))).astype(np.float32)
