@@ -168,27 +168,34 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_w4a4_kernel(
     const rsrc_t rss = sb_side ? rsb : rsa;
     const int vss = (int)((sb_side ? n0 : m0) * 8) + 16 * lane;
     const int sq_stride = (int)((sb_side ? N : M) * 8);
-    // quad q into a code slot and a scale slot (groups past the end of K
-    // read the next row's codes or 0, and zero scales)
-    auto load_quad = [&](char* cs, char* ss, int q) __attribute__((always_inline)) {
+    // Load d (0 .. NDMA - 1) of quad q into a code slot and a scale slot:
+    // the 8-row parts of this wave's A blocks, then of its B blocks, then
+    // the scales (groups past the end of K read the next row's codes or 0,
+    // and zero scales).
+    constexpr int NCODE = (C::APW + C::BPW) * 4, NDMA = NCODE + (MODE != 2 ? 1 : 0);
+    auto dma_one = [&](char* cs, char* ss, int q, int d) __attribute__((always_inline)) {
         const int so = q * 128;
-#pragma unroll
-        for (int k = 0; k < C::APW; ++k) {
-            char* dst = cs + (wave + k * C::NW) * 4096;
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                dma16(rqa, dst + i * 1024, (i & 1) ? vca_o[k] : vca_e[k], so + 8 * i * (int)(K / 2));
-        }
-#pragma unroll
-        for (int k = 0; k < C::BPW; ++k) {
-            char* dst = cs + (C::ABLK + wave + k * C::NW) * 4096;
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                dma16(rqb, dst + i * 1024, (i & 1) ? vcb_o[k] : vcb_e[k], so + 8 * i * (int)(K / 2));
-        }
-        if constexpr (MODE != 2)
+        if (d < C::APW * 4) {
+            const int k = d / 4, i = d % 4;
+            dma16(rqa, cs + (wave + k * C::NW) * 4096 + i * 1024, (i & 1) ? vca_o[k] : vca_e[k],
+                  so + 8 * i * (int)(K / 2));
+        } else if (d < NCODE) {
+            const int k = (d - C::APW * 4) / 4, i = d % 4;
+            dma16(rqb, cs + (C::ABLK + wave + k * C::NW) * 4096 + i * 1024, (i & 1) ? vcb_o[k] : vcb_e[k],
+                  so + 8 * i * (int)(K / 2));
+        } else if constexpr (MODE != 2) {
             dma16(rss, ss + (sb_side ? BM * 8 : 0), vss, q * sq_stride);
+        }
     };
+    auto load_quad = [&](char* cs, char* ss, int q, int dlo, int dhi) __attribute__((always_inline)) {
+#pragma unroll
+        for (int d = 0; d < NDMA; ++d)
+            if (d >= dlo && d < dhi) dma_one(cs, ss, q, d);
+    };
+    // a quad's loads are issued in two halves, spread over the blocks of
+    // two consecutive groups, so the waves of a CU never queue all of them
+    // at the texture unit at once
+    constexpr int DSPLIT = (NDMA + 1) / 2;
     // Wait for this wave's loads (the quad loaded one step ago) and publish
     // them with a barrier.
     auto publish = [&]() __attribute__((always_inline)) {
@@ -204,7 +211,7 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_w4a4_kernel(
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-    load_quad(cs0, ss0, 0);
+    load_quad(cs0, ss0, 0, 0, NDMA);
 
     // ---- low-rank branch: acc = xl1 L2 --------------------------------------
     // 32 ranks at a time, through code slot 1 (free until quad 1 is loaded):
@@ -324,8 +331,8 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_w4a4_kernel(
     // 1); operands used for the last time are read for the next group (group
     // ngq of the quad in ncs; at the end of a quad, also the next quad's
     // scales from nss, into the other parity).
-    auto group = [&](int g, int gq, int par, const char* ncs, const char* nss, int ngq)
-        __attribute__((always_inline)) {
+    auto group = [&](int g, int gq, int par, const char* ncs, const char* nss, int ngq,
+                     char* dcs, char* dss, int dq, int dlo, int dhi) __attribute__((always_inline)) {
 #pragma unroll
         for (int bl = 0; bl < TM * TN; ++bl) {
             const int i = bl / TN, j = bl % TN;
@@ -360,6 +367,12 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_w4a4_kernel(
                 for (int e = 0; e < 16; ++e) acc[pi][pj][e] = __builtin_fmaf(Pp[e], Sp[e], acc[pi][pj][e]);
                 order_point(acc[pi][pj]);
             }
+            // this block's share of the loads being spread (the last block
+            // takes what is left)
+            if (dhi > dlo) {
+                if (bl < TM * TN - 1) load_quad(dcs, dss, dq, dlo + bl, dlo + bl + 1);
+                else load_quad(dcs, dss, dq, dlo + bl, dhi);
+            }
             if (j == TN - 1) {
                 read_a(ncs, ngq, i);
                 if (gq == 3) read_sa(nss, par ^ 1, i);
@@ -375,27 +388,28 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_w4a4_kernel(
     // prologue: quad 0 published, quad 1 in flight, group 0's operands and
     // quad 0's scales read
     publish();
-    load_quad(cs1, ss1, 1);
+    load_quad(cs1, ss1, 1, 0, DSPLIT);
 #pragma unroll
     for (int i = 0; i < TM; ++i) { read_a(cs0, 0, i); read_sa(ss0, 0, i); }
 #pragma unroll
     for (int j = 0; j < TN; ++j) { read_b(cs0, 0, j); read_sb(ss0, 0, j); }
 
-    // Step q (quad q in slots cur, scale parity par): groups 4q .. 4q + 2,
-    // each reading the next one's operands; publish quad q + 1 (loaded one
-    // step ago); load quad q + 2 into quad q's slots, which nobody reads any
-    // more; group 4q + 3, reading group 4q + 4's operands and quad q + 1's
-    // scales. The step count is rounded up to an even number so the loop
-    // body has no branches (which would blur the compiler's per-slot
-    // tracking of loads into LDS); the extra groups have zero scales.
+    // Step q (quad q in slots cur, scale parity par): group 4q, which also
+    // issues the second half of quad q + 1's loads (into the other slots);
+    // groups 4q + 1 and 4q + 2, each reading the next group's operands;
+    // publish quad q + 1; group 4q + 3, reading group 4q + 4's operands and
+    // quad q + 1's scales and issuing the first half of quad q + 2's loads
+    // into quad q's slots, which nobody reads any more. The step count is
+    // rounded up to an even number so the loop body has no branches (which
+    // would blur the compiler's per-slot tracking of loads into LDS); the
+    // extra groups have zero scales.
     auto step = [&](int q, int par, char* cs, char* ss, char* ncs, char* nss) __attribute__((always_inline)) {
         const int g0 = 4 * q;
-        group(g0, 0, par, cs, ss, 1);
-        group(g0 + 1, 1, par, cs, ss, 2);
-        group(g0 + 2, 2, par, cs, ss, 3);
+        group(g0, 0, par, cs, ss, 1, ncs, nss, q + 1, DSPLIT, NDMA);
+        group(g0 + 1, 1, par, cs, ss, 2, cs, ss, 0, 0, 0);
+        group(g0 + 2, 2, par, cs, ss, 3, cs, ss, 0, 0, 0);
         publish();
-        load_quad(cs, ss, q + 2);
-        group(g0 + 3, 3, par, ncs, nss, 0);
+        group(g0 + 3, 3, par, ncs, nss, 0, cs, ss, q + 2, 0, DSPLIT);
     };
     for (int q = 0; q < NQ; q += 2) {
         step(q, 0, cs0, ss0, cs1, ss1);
