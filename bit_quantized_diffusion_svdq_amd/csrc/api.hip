@@ -191,6 +191,8 @@ svdq_status svdq_gemm_w4a4(const uint8_t* qx, const void* sx_f16, int64_t M, int
         return fail(SVDQ_ERR_SHAPE, "(M + 256) * rank * 4 and (N + 256) * rank * 2 must stay below 2^31 bytes");
     if (ldy < N) return fail(SVDQ_ERR_SHAPE, "ldy = %lld < N = %lld", (long long)ldy, (long long)N);
     if (ldy % 8) return fail(SVDQ_ERR_ALIGN, "ldy = %lld must be a multiple of 8", (long long)ldy);
+    if ((M + 128) * ldy * (y_dtype == SVDQ_DT_F32 ? 4 : 2) >= ((int64_t)1 << 31))
+        return fail(SVDQ_ERR_SHAPE, "(M + 128) * ldy * element size must stay below 2^31 bytes");
     if (act != SVDQ_ACT_NONE && act != SVDQ_ACT_GELU_TANH)
         return fail(SVDQ_ERR_UNSUPPORTED, "activation %d is not supported", act);
     if (y_dtype != SVDQ_DT_BF16 && y_dtype != SVDQ_DT_F32)

@@ -31,7 +31,7 @@
 //  - tiles are swizzled so each XCD (own L2) works on compact groups of tiles;
 //  - the accumulator starts from X_hat L1 L2 (bf16 MFMA on the hi/lo split of
 //    the fp32 xl1); bias and GELU run in fp32 before the single rounding of
-//    the output, which leaves through LDS as row-contiguous 16-byte stores.
+//    the output, which is stored straight from the MFMA layout.
 #include "common.h"
 
 namespace {
@@ -48,15 +48,12 @@ struct Cfg {
     // (A blocks, then B blocks; see the swizzle at the loads) and, in a slot
     // of its own, the scales [tile row][4] fp16 (A rows, then B rows).
     static constexpr int CODE_SLOT = SBLK * 4096, SC_SLOT = (BM + BN) * 8;
-    // bf16 output staging for the epilogue: OUT_ROWS rows at a time in code slot 0
-    static constexpr int OUT_LD = BN + 8, OUT_ROWS = 32 * TM;
     static_assert(TM * 32 * WGM == BM && TN * 32 * WGN == BN, "tile shape");
     static_assert(APW * NW == ABLK && BPW * NW == BBLK && APW >= 1 && BPW >= 1,
                   "blocks split evenly over the waves");
     static_assert((TM * TN) % 2 == 0, "blocks per wave must be even for the register rotation");
     static_assert(BM * 8 == 1024 && BN * 8 == 1024 && NW % 2 == 0,
                   "a quad's scales of the tile rows are one 64-lane load per side");
-    static_assert(OUT_ROWS * OUT_LD * 2 <= CODE_SLOT, "epilogue staging fits one slot");
     static_assert(2 * (CODE_SLOT + SC_SLOT) * MINB <= 160 * 1024, "LDS budget");
 };
 
@@ -270,6 +267,14 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_w4a4_kernel(
         }
     }
 
+    // bias of the lane's columns, fetched now so its latency is hidden
+    float bvj[TN];
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+        const int64_t col = n0 + wn * 32 * TN + j * 32 + (lane & 31);
+        bvj[j] = (MODE != 2 && bias && col < N) ? bf16_lo_to_f32(bias[col]) : 0.0f;
+    }
+
     // ---- operands ---------------------------------------------------------
     // Codes of group gq (0..3) of a quad, for this lane (row r = lane % 32 of
     // a block, half h = lane / 32): chunk 2 gq + h of the row. The LDS
@@ -422,65 +427,35 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_w4a4_kernel(
     // every load into LDS has landed and every wave is done with the slots
     __syncthreads();
 
-    if constexpr (MODE == 0) {
-        // bias, GELU and bf16 rounding in registers, then transposed through
-        // LDS (code slot 0), one wave row (OUT_ROWS rows) at a time, for
-        // row-contiguous stores
-        uint32_t ob[TM][TN][8];
+    if constexpr (MODE != 2) {
+        // bias, GELU and one rounding to the output type in registers, then
+        // buffer stores straight from the MFMA layout: a store instruction
+        // writes two 64-byte row segments (lanes 0..31 row r, lanes 32..63
+        // row r + 4); the row step is the scalar offset, so the stores need
+        // no address arithmetic. Rows past M fall outside the buffer range
+        // and are dropped; columns past N are masked.
+        constexpr int ESZ = (MODE == 0) ? 2 : 4;
+        const rsrc_t ry = make_rsrc(y, M * ldy * ESZ);
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
             const int64_t col = n0 + wn * 32 * TN + j * 32 + (lane & 31);
-            const float bv = (bias && col < N) ? bf16_lo_to_f32(bias[col]) : 0.0f;
+            if (col < N) {
 #pragma unroll
-            for (int i = 0; i < TM; ++i)
+                for (int i = 0; i < TM; ++i) {
+                    const int64_t row0 = m0 + wm * 32 * TM + i * 32 + 4 * (lane >> 5);
+                    const int vo = (int)((row0 * ldy + col) * ESZ);
 #pragma unroll
-                for (int e = 0; e < 16; e += 2) {
-                    float v0 = acc[i][j][e] + bv, v1 = acc[i][j][e + 1] + bv;
-                    if constexpr (ACT == 1) { v0 = gelu_tanh_f32(v0); v1 = gelu_tanh_f32(v1); }
-                    ob[i][j][e / 2] = pack_bf16x2(v0, v1);
-                }
-        }
-        uint16_t* out = (uint16_t*)cs0;
-        constexpr int CHUNKS = BN / 8;              // 16-byte chunks per tile row
-        for (int r = 0; r < C::WGM; ++r) {
-            if (wm == r) {
-#pragma unroll
-                for (int j = 0; j < TN; ++j) {
-                    const int lc = wn * 32 * TN + j * 32 + (lane & 31);
-#pragma unroll
-                    for (int i = 0; i < TM; ++i)
-#pragma unroll
-                        for (int e = 0; e < 16; ++e) {
-                            const int lr = i * 32 + out_row(e, lane);
-                            out[lr * C::OUT_LD + lc] = (uint16_t)(ob[i][j][e / 2] >> (16 * (e & 1)));
-                        }
+                    for (int e = 0; e < 16; ++e) {
+                        float v = acc[i][j][e] + bvj[j];
+                        if constexpr (ACT == 1) v = gelu_tanh_f32(v);
+                        const int so = (8 * (e >> 2) + (e & 3)) * (int)ldy * ESZ;
+                        if constexpr (MODE == 0)
+                            __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_bits(v), ry, vo, so, 0);
+                        else
+                            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), ry, vo, so, 0);
+                    }
                 }
             }
-            __syncthreads();
-            for (int c = tid; c < C::OUT_ROWS * CHUNKS; c += NT) {
-                const int lr = c / CHUNKS, lc = (c % CHUNKS) * 8;
-                const int64_t row = m0 + r * C::OUT_ROWS + lr, col = n0 + lc;
-                if (row < M && col < N)
-                    *(uint4*)((uint16_t*)y + row * ldy + col) = *(const uint4*)(out + lr * C::OUT_LD + lc);
-            }
-            __syncthreads();
-        }
-    } else if constexpr (MODE == 1) {
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-            const int64_t col = n0 + wn * 32 * TN + j * 32 + (lane & 31);
-            if (col >= N) continue;
-            const float bv = bias ? bf16_lo_to_f32(bias[col]) : 0.0f;
-#pragma unroll
-            for (int i = 0; i < TM; ++i)
-#pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const int64_t row = m0 + wm * 32 * TM + i * 32 + out_row(e, lane);
-                    if (row >= M) continue;
-                    float v = acc[i][j][e] + bv;
-                    if constexpr (ACT == 1) v = gelu_tanh_f32(v);
-                    ((float*)y)[row * ldy + col] = v;
-                }
         }
     }
 }

@@ -127,8 +127,8 @@ svdq_status svdq_quantize_act(const void* x, int64_t M, int64_t K, int64_t ldx,
  *  y           out: [M][ldy] of y_dtype (bf16 RTNE of the fp32 result, or fp32)
  *
  * N % 8 == 0, ldy >= N, ldy % 8 == 0; (M + 256) * K / 2, (N + 256) * K / 2,
- * (M + 256) * rank * 4 and (N + 256) * rank * 2 must stay below 2^31 (byte
- * offsets plus a tile of slack). The group partials P_g are exact; the fp32 result
+ * (M + 256) * rank * 4, (N + 256) * rank * 2 and (M + 128) * ldy * (2 or 4
+ * bytes) must stay below 2^31 (byte offsets plus a tile of slack). The group partials P_g are exact; the fp32 result
  * matches the fp64 definition to about 1e-6 relative.
  * Alignment: every pointer 16-byte aligned (bias: 2 bytes).
  */

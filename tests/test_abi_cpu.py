@@ -83,7 +83,7 @@ def _gemm(lib, **kw):
     (dict(y=None), NULL), (dict(xl1=None), NULL), (dict(rank=20), SHAPE), (dict(qw=C + 4), ALIGN),
     (dict(y=E + 65536 + 8), ALIGN), (dict(M=1 << 20, K=4096), SHAPE), (dict(N=1 << 20, K=4096), SHAPE),
     (dict(M=1 << 22, K=64, rank=128), SHAPE), (dict(N=1 << 23, K=64, rank=128), SHAPE),
-    (dict(sx=B + 8), ALIGN), (dict(sw=D + 8), ALIGN),
+    (dict(sx=B + 8), ALIGN), (dict(sw=D + 8), ALIGN), (dict(M=1 << 23, K=64, N=256, ldy=256), SHAPE),
 ])
 def test_gemm_rejects(lib, kw, status):
     assert _gemm(lib, **kw) == status
