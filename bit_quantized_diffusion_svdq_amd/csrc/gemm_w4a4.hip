@@ -28,7 +28,9 @@
 //  - products and scale products of consecutive blocks alternate between two
 //    register sets, so one wave's FMAs for a block run while the matrix pipe
 //    works on its next block;
-//  - tiles are swizzled so each XCD (own L2) works on compact groups of tiles;
+//  - persistent workgroups (two per CU) walk their tiles so each XCD (own L2)
+//    works on a compact region; a tile's first loads fly while the previous
+//    tile's outputs are stored;
 //  - the accumulator starts from X_hat L1 L2 (bf16 MFMA on the hi/lo split of
 //    the fp32 xl1); bias and GELU run in fp32 before the single rounding of
 //    the output, which is stored straight from the MFMA layout.
@@ -64,6 +66,30 @@ struct Cfg {
 // workgroups, never wait for each other at a barrier and so interleave their
 // MFMA and VALU work.
 using MainCfg = Cfg<128, 128, 2, 2, 2>;
+
+// Tile t -> (tile row, tile column). Workgroup b runs on XCD b % 8 (the
+// dispatcher deals workgroups round-robin to the XCDs), and with the grid a
+// multiple of 8 every tile of workgroup b has t % 8 == b % 8. When the tile
+// grid splits evenly, XCD x owns one of 2 x 4 regions of it and walks it in
+// bands of 8 tile rows, column by column, so the tiles in flight on an XCD
+// share 8 tile rows of activations and 8 tile columns of weights in its L2.
+// Otherwise: bands of 4 tile rows over the whole grid.
+DEV void tile_coords(int t, int tiles_m, int tiles_n, int grid, int& tm, int& tn) {
+    if (grid % 8 == 0 && (tiles_m * tiles_n) % 8 == 0 && tiles_m % 2 == 0 && tiles_n % 4 == 0) {
+        const int x = t & 7, l = t >> 3, RH = tiles_m >> 1, RW = tiles_n >> 2;
+        const int band = l / (8 * RW), first = band * 8;
+        const int gsz = (RH - first) < 8 ? (RH - first) : 8;
+        const int w = l - band * 8 * RW;
+        tm = (x & 1) * RH + first + w % gsz;
+        tn = (x >> 1) * RW + w / gsz;
+    } else {
+        constexpr int GM = 4;
+        const int grp = t / (GM * tiles_n), first = grp * GM;
+        const int gsz = (tiles_m - first) < GM ? (tiles_m - first) : GM;
+        tm = first + (t % (GM * tiles_n)) % gsz;
+        tn = (t % (GM * tiles_n)) / gsz;
+    }
+}
 
 DEV int out_row(int i, int lane) { return 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3); }
 
@@ -103,25 +129,13 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_w4a4_kernel(
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / C::WGN, wn = wave % C::WGN;
 
-    // tile index: blocks are dealt round-robin to the 8 XCDs; consecutive
-    // blocks of one XCD take a compact group of tiles (4 tile rows wide) so
-    // the XCD's L2 serves both their activation and weight blocks
+    // The workgroups are persistent: workgroup b takes tiles b, b + grid,
+    // ... (tile_coords places them so each XCD works on a compact region).
     const int64_t mext = (MODE == 2) ? pmc : M, next = (MODE == 2) ? pnc : N;
     const int tiles_n = (int)((next + BN - 1) / BN);
     const int tiles_m = (int)((mext + BM - 1) / BM);
     const int tiles = tiles_n * tiles_m;
-    int t = blockIdx.x;
-    if (tiles % 8 == 0) t = (t % 8) * (tiles / 8) + t / 8;
-    int tm, tn;
-    {
-        constexpr int GM = 4;
-        const int grp = t / (GM * tiles_n), first = grp * GM;
-        const int gsz = (tiles_m - first) < GM ? (tiles_m - first) : GM;
-        tm = first + (t % (GM * tiles_n)) % gsz;
-        tn = (t % (GM * tiles_n)) / gsz;
-    }
-    const int64_t m0 = (MODE == 2 ? pm0 : 0) + (int64_t)tm * BM;
-    const int64_t n0 = (MODE == 2 ? pn0 : 0) + (int64_t)tn * BN;
+    int64_t m0 = 0, n0 = 0;                          // origin of the current tile
     const int64_t mlim = (MODE == 2) ? pm0 + pmc : M;
     const int64_t nlim = (MODE == 2) ? pn0 + pnc : N;
     const int G = (int)(K / 64), NQ = (G + 3) / 4;   // groups, quads of groups
@@ -143,18 +157,6 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_w4a4_kernel(
     const int cpe = (lane & 7) ^ (lr8 >> 1);          // chunk for even parts (f = lr8 / 2)
     const int cpo = cpe ^ 4;                          // odd parts (f = 4 + lr8 / 2)
     int vca_e[C::APW], vca_o[C::APW], vcb_e[C::BPW], vcb_o[C::BPW];
-#pragma unroll
-    for (int k = 0; k < C::APW; ++k) {
-        const int64_t r = m0 + (int64_t)(wave + k * C::NW) * 32 + lr8;
-        vca_e[k] = (int)(r * (K / 2)) + 16 * cpe;
-        vca_o[k] = (int)(r * (K / 2)) + 16 * cpo;
-    }
-#pragma unroll
-    for (int k = 0; k < C::BPW; ++k) {
-        const int64_t r = n0 + (int64_t)(wave + k * C::NW) * 32 + lr8;
-        vcb_e[k] = (int)(r * (K / 2)) + 16 * cpe;
-        vcb_o[k] = (int)(r * (K / 2)) + 16 * cpo;
-    }
     // Scales: quad q of the tile's A rows is the 1 KB at 8 (q M + m0) and of
     // its B rows the 1 KB at 8 (q N + n0): even waves load A's into the first
     // half of the scale slot, odd waves B's into the second half (waves 2 and
@@ -163,7 +165,7 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_w4a4_kernel(
     // scales or 0 (their outputs are never stored).
     const bool sb_side = (wave & 1) != 0;
     const rsrc_t rss = sb_side ? rsb : rsa;
-    const int vss = (int)((sb_side ? n0 : m0) * 8) + 16 * lane;
+    int vss = 0;
     const int sq_stride = (int)((sb_side ? N : M) * 8);
     // Load d (0 .. NDMA - 1) of quad q into a code slot and a scale slot:
     // the 8-row parts of this wave's A blocks, then of its B blocks, then
@@ -200,16 +202,6 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_w4a4_kernel(
         lds_barrier();
     };
 
-    v16f acc[TM][TN];
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
-
-    load_quad(cs0, ss0, 0, 0, NDMA);
-
     // ---- low-rank branch: acc = xl1 L2 --------------------------------------
     // 32 ranks at a time, through code slot 1 (free until quad 1 is loaded):
     // the chunk's xl1 rows of the tile (128 B each, fp32) at 0 and its l2t
@@ -219,19 +211,50 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_w4a4_kernel(
     // so the MFMA lanes read them without bank conflicts. The first chunk
     // flies together with quad 0. A last chunk of 16 ranks reads 16 more
     // bytes per row that are never used (or 0 past the end of the array).
-    if (MODE != 2 && rank > 0) {
-        const rsrc_t rxl = make_rsrc(xl1, M * rank * 4);
-        const rsrc_t rl2 = make_rsrc(l2t, N * rank * 2);
-        const int vxl = (int)((m0 + 8 * wave + lr8) * rank * 4) + 16 * ((wave & 1) ? cpo : cpe);
-        const int vl2 = (int)((n0 + 16 * wave + (lane >> 2)) * rank * 2) + 16 * ((lane & 3) ^ ((lane >> 4) & 3));
+    const rsrc_t rxl = make_rsrc(xl1, (MODE != 2) ? M * rank * 4 : 0);
+    const rsrc_t rl2 = make_rsrc(l2t, (MODE != 2) ? N * rank * 2 : 0);
+    int vxl = 0, vl2 = 0;
+    auto load_lr = [&](int r0) __attribute__((always_inline)) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            dma16(rxl, cs1 + (wave + 4 * k) * 1024, vxl, k * 32 * rank * 4 + r0 * 4);
+#pragma unroll
+        for (int k = 0; k < 2; ++k)
+            dma16(rl2, cs1 + 16384 + (wave + 4 * k) * 1024, vl2, k * 64 * rank * 2 + r0 * 2);
+    };
+
+    // Tile t: its origin and this lane's load offsets, then the loads that
+    // start it (quad 0 and the first low-rank chunk), which the previous
+    // tile's stores overlap.
+    auto start_tile = [&](int t) __attribute__((always_inline)) {
+        int tm, tn;
+        tile_coords(t, tiles_m, tiles_n, (int)gridDim.x, tm, tn);
+        m0 = (MODE == 2 ? pm0 : 0) + (int64_t)tm * BM;
+        n0 = (MODE == 2 ? pn0 : 0) + (int64_t)tn * BN;
+#pragma unroll
+        for (int k = 0; k < C::APW; ++k) {
+            const int64_t r = m0 + (int64_t)(wave + k * C::NW) * 32 + lr8;
+            vca_e[k] = (int)(r * (K / 2)) + 16 * cpe;
+            vca_o[k] = (int)(r * (K / 2)) + 16 * cpo;
+        }
+#pragma unroll
+        for (int k = 0; k < C::BPW; ++k) {
+            const int64_t r = n0 + (int64_t)(wave + k * C::NW) * 32 + lr8;
+            vcb_e[k] = (int)(r * (K / 2)) + 16 * cpe;
+            vcb_o[k] = (int)(r * (K / 2)) + 16 * cpo;
+        }
+        vss = (int)((sb_side ? n0 : m0) * 8) + 16 * lane;
+        vxl = (int)((m0 + 8 * wave + lr8) * rank * 4) + 16 * ((wave & 1) ? cpo : cpe);
+        vl2 = (int)((n0 + 16 * wave + (lane >> 2)) * rank * 2) + 16 * ((lane & 3) ^ ((lane >> 4) & 3));
+        load_quad(cs0, ss0, 0, 0, NDMA);
+        if (MODE != 2 && rank > 0) load_lr(0);
+    };
+
+    v16f acc[TM][TN];
+    auto low_rank = [&]() __attribute__((always_inline)) {
         const int h = lane >> 5, r32l = lane & 31;
         for (int r0 = 0; r0 < rank; r0 += 32) {
-#pragma unroll
-            for (int k = 0; k < 4; ++k)
-                dma16(rxl, cs1 + (wave + 4 * k) * 1024, vxl, k * 32 * rank * 4 + r0 * 4);
-#pragma unroll
-            for (int k = 0; k < 2; ++k)
-                dma16(rl2, cs1 + 16384 + (wave + 4 * k) * 1024, vl2, k * 64 * rank * 2 + r0 * 2);
+            if (r0 > 0) load_lr(r0);
             publish();
             const int nks = (rank - r0) >= 32 ? 2 : 1;
             for (int ks = 0; ks < nks; ++ks) {
@@ -265,15 +288,7 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_w4a4_kernel(
             }
             lds_barrier();     // slot 1 is read by every wave before it is refilled
         }
-    }
-
-    // bias of the lane's columns, fetched now so its latency is hidden
-    float bvj[TN];
-#pragma unroll
-    for (int j = 0; j < TN; ++j) {
-        const int64_t col = n0 + wn * 32 * TN + j * 32 + (lane & 31);
-        bvj[j] = (MODE != 2 && bias && col < N) ? bf16_lo_to_f32(bias[col]) : 0.0f;
-    }
+    };
 
     // ---- operands ---------------------------------------------------------
     // Codes of group gq (0..3) of a quad, for this lane (row r = lane % 32 of
@@ -390,14 +405,6 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_w4a4_kernel(
         }
     };
 
-    // prologue: quad 0 published, quad 1 in flight, group 0's operands and
-    // quad 0's scales read
-    publish();
-    load_quad(cs1, ss1, 1, 0, DSPLIT);
-#pragma unroll
-    for (int i = 0; i < TM; ++i) { read_a(cs0, 0, i); read_sa(ss0, 0, i); }
-#pragma unroll
-    for (int j = 0; j < TN; ++j) { read_b(cs0, 0, j); read_sb(ss0, 0, j); }
 
     // Step q (quad q in slots cur, scale parity par): group 4q, which also
     // issues the second half of quad q + 1's loads (into the other slots);
@@ -416,48 +423,97 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_w4a4_kernel(
         publish();
         group(g0 + 3, 3, par, ncs, nss, 0, cs, ss, q + 2, 0, DSPLIT);
     };
-    for (int q = 0; q < NQ; q += 2) {
-        step(q, 0, cs0, ss0, cs1, ss1);
-        step(q + 1, 1, cs1, ss1, cs0, ss0);
-    }
-    if constexpr (MODE != 2) {
+    // ---- the tiles of this workgroup ----------------------------------------
+    int t = blockIdx.x;
+    start_tile(t);
+    for (;;) {
 #pragma unroll
-        for (int e = 0; e < 16; ++e) acc[TM - 1][TN - 1][e] = __builtin_fmaf(P1[e], S1[e], acc[TM - 1][TN - 1][e]);
-    }
-    // every load into LDS has landed and every wave is done with the slots
-    __syncthreads();
-
-    if constexpr (MODE != 2) {
-        // bias, GELU and one rounding to the output type in registers, then
-        // buffer stores straight from the MFMA layout: a store instruction
-        // writes two 64-byte row segments (lanes 0..31 row r, lanes 32..63
-        // row r + 4); the row step is the scalar offset, so the stores need
-        // no address arithmetic. Rows past M fall outside the buffer range
-        // and are dropped; columns past N are masked.
-        constexpr int ESZ = (MODE == 0) ? 2 : 4;
-        const rsrc_t ry = make_rsrc(y, M * ldy * ESZ);
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+        S1 = zero;     // the first group's "previous block" adds nothing
+        if (MODE != 2 && rank > 0) low_rank();
+        // bias of the lane's columns, fetched now so its latency is hidden
+        float bvj[TN];
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
             const int64_t col = n0 + wn * 32 * TN + j * 32 + (lane & 31);
-            if (col < N) {
+            bvj[j] = (MODE != 2 && bias && col < N) ? bf16_lo_to_f32(bias[col]) : 0.0f;
+        }
+        // quad 0 published, quad 1 in flight, group 0's operands and quad 0's
+        // scales read
+        publish();
+        load_quad(cs1, ss1, 1, 0, DSPLIT);
 #pragma unroll
-                for (int i = 0; i < TM; ++i) {
-                    const int64_t row0 = m0 + wm * 32 * TM + i * 32 + 4 * (lane >> 5);
-                    const int vo = (int)((row0 * ldy + col) * ESZ);
+        for (int i = 0; i < TM; ++i) { read_a(cs0, 0, i); read_sa(ss0, 0, i); }
 #pragma unroll
-                    for (int e = 0; e < 16; ++e) {
-                        float v = acc[i][j][e] + bvj[j];
-                        if constexpr (ACT == 1) v = gelu_tanh_f32(v);
-                        const int so = (8 * (e >> 2) + (e & 3)) * (int)ldy * ESZ;
-                        if constexpr (MODE == 0)
-                            __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_bits(v), ry, vo, so, 0);
-                        else
-                            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), ry, vo, so, 0);
+        for (int j = 0; j < TN; ++j) { read_b(cs0, 0, j); read_sb(ss0, 0, j); }
+
+        for (int q = 0; q < NQ; q += 2) {
+            step(q, 0, cs0, ss0, cs1, ss1);
+            step(q + 1, 1, cs1, ss1, cs0, ss0);
+        }
+        if constexpr (MODE != 2) {
+    #pragma unroll
+            for (int e = 0; e < 16; ++e) acc[TM - 1][TN - 1][e] = __builtin_fmaf(P1[e], S1[e], acc[TM - 1][TN - 1][e]);
+        }
+        // every load into LDS has landed and every wave is done with the
+        // slots: the next tile's first loads go out before this tile's stores
+        __syncthreads();
+        const int64_t em0 = m0, en0 = n0;
+        const bool more = t + (int)gridDim.x < tiles;
+        if (more) start_tile(t + (int)gridDim.x);
+
+        if constexpr (MODE != 2) {
+            // bias, GELU and one rounding to the output type in registers, then
+            // buffer stores straight from the MFMA layout: a store instruction
+            // writes two 64-byte row segments (lanes 0..31 row r, lanes 32..63
+            // row r + 4); the row step is the scalar offset, so the stores need
+            // no address arithmetic. Rows past M fall outside the buffer range
+            // and are dropped; columns past N are masked.
+            constexpr int ESZ = (MODE == 0) ? 2 : 4;
+            const rsrc_t ry = make_rsrc(y, M * ldy * ESZ);
+    #pragma unroll
+            for (int j = 0; j < TN; ++j) {
+                const int64_t col = en0 + wn * 32 * TN + j * 32 + (lane & 31);
+                if (col < N) {
+    #pragma unroll
+                    for (int i = 0; i < TM; ++i) {
+                        const int64_t row0 = em0 + wm * 32 * TM + i * 32 + 4 * (lane >> 5);
+                        const int vo = (int)((row0 * ldy + col) * ESZ);
+    #pragma unroll
+                        for (int e = 0; e < 16; ++e) {
+                            float v = acc[i][j][e] + bvj[j];
+                            if constexpr (ACT == 1) v = gelu_tanh_f32(v);
+                            const int so = (8 * (e >> 2) + (e & 3)) * (int)ldy * ESZ;
+                            if constexpr (MODE == 0)
+                                __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_bits(v), ry, vo, so, 0);
+                            else
+                                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), ry, vo, so, 0);
+                        }
                     }
                 }
             }
         }
+
+        if (!more) break;
+        t += (int)gridDim.x;
     }
+}
+
+// compute units of the current device (queried once per device)
+int device_cu_count() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cached[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
 }
 
 template <class C, int MODE, int ACT>
@@ -467,7 +523,10 @@ void launch_mode(hipStream_t stream, const uint8_t* qx, const uint16_t* sx,
                  int64_t K, int64_t pm0, int64_t pmc, int64_t pn0, int64_t pnc, int32_t* p) {
     const int64_t mext = (MODE == 2) ? pmc : M, next = (MODE == 2) ? pnc : N;
     const int64_t tiles = ((next + C::BN - 1) / C::BN) * ((mext + C::BM - 1) / C::BM);
-    hipLaunchKernelGGL((gemm_w4a4_kernel<C, MODE, ACT>), dim3((unsigned)tiles), dim3(C::NT),
+    // persistent workgroups: MINB per CU
+    const int64_t slots = (int64_t)C::MINB * device_cu_count();
+    const int64_t grid = tiles < slots ? tiles : slots;
+    hipLaunchKernelGGL((gemm_w4a4_kernel<C, MODE, ACT>), dim3((unsigned)grid), dim3(C::NT),
                        0, stream, qx, sx, qw, sw, xl1, l2t, rank, bias, y, ldy, M, N, K,
                        pm0, pmc, pn0, pnc, p);
 }
