@@ -35,6 +35,8 @@ _SIGS = {
     "svdq_quantize_act": [_P, _I64, _I64, _I64, _P, _P, _I32, _P, _P, _P, _P],
     "svdq_gemm_w4a4": [_P, _P, _I64, _I64, _P, _P, _I64, _P, _P, _I32, _P, _I32, _P, _I32, _I64, _P],
     "svdq_gemm_w4a4_partials": [_P, _I64, _I64, _P, _I64, _I64, _I64, _I64, _I64, _P, _P],
+    "svdq_quantize_act_mxfp4": [_P, _I64, _I64, _I64, _P, _P, _I32, _P, _P, _P, _P],
+    "svdq_gemm_mxfp4": [_P, _P, _I64, _I64, _P, _P, _I64, _P, _P, _I32, _P, _I32, _P, _I32, _I64, _P],
     "awq_gemv_w4a16": [_P, _I64, _I64, _P, _P, _P, _P, _I64, _P, _P, _P],
 }
 
@@ -114,6 +116,20 @@ def svdq_gemm_w4a4_partials(qx, M, K, qw, N, m0, mcount, n0, ncount, p, stream=N
            "svdq_gemm_w4a4_partials")
 
 
+def svdq_quantize_act_mxfp4(x, M, K, ldx, inv_lambda, l1t, rank, qx, sx, xl1, stream=None):
+    _check(load_library().svdq_quantize_act_mxfp4(_ptr(x), M, K, ldx, _ptr(inv_lambda), _ptr(l1t),
+                                                  rank, _ptr(qx), _ptr(sx), _ptr(xl1), _stream(stream)),
+           "svdq_quantize_act_mxfp4")
+
+
+def svdq_gemm_mxfp4(qx, sx, M, K, qw, sw, N, xl1, l2t, rank, bias, act, y, y_dtype, ldy,
+                    stream=None):
+    _check(load_library().svdq_gemm_mxfp4(_ptr(qx), _ptr(sx), M, K, _ptr(qw), _ptr(sw), N,
+                                          _ptr(xl1), _ptr(l2t), rank, _ptr(bias), act, _ptr(y),
+                                          y_dtype, ldy, _stream(stream)),
+           "svdq_gemm_mxfp4")
+
+
 def awq_gemv_w4a16(x, M, K, inv_s, qw, scale, zero, N, bias, y, stream=None):
     _check(load_library().awq_gemv_w4a16(_ptr(x), M, K, _ptr(inv_s), _ptr(qw), _ptr(scale),
                                          _ptr(zero), N, _ptr(bias), _ptr(y), _stream(stream)),
@@ -160,4 +176,31 @@ def awq_gemv(x, inv_s, qwt, scale_t, zero_t, bias, N=None, y=None, stream=None):
     if y is None:
         y = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
     awq_gemv_w4a16(x, M, K, inv_s, qwt, scale_t, zero_t, N, bias, y, stream)
+    return y
+
+
+def quantize_act_mxfp4(x: torch.Tensor, inv_lambda, l1t, rank: int, stream=None):
+    """x: bf16 [M, K] on the GPU -> (qx uint8 [M, K/2] E2M1 nibbles, sx uint8
+    [ceil(K/256), M, 8] E8M0 block exponents, xl1 fp32 [M, r])."""
+    M, K = x.shape
+    dev = x.device
+    qx = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
+    sx = torch.empty(((K // 64 + 3) // 4, M, 8), dtype=torch.uint8, device=dev)
+    xl1 = torch.empty((M, rank), dtype=torch.float32, device=dev) if rank else None
+    svdq_quantize_act_mxfp4(x, M, K, x.stride(0), inv_lambda, l1t if rank else None, rank, qx, sx,
+                            xl1, stream)
+    return qx, sx, xl1
+
+
+def mxfp4_linear(qx, sx, xl1, qw, sw, l2t, bias, rank: int, act: str = "none",
+                 out_dtype=torch.bfloat16, y=None, stream=None):
+    """Y = xl1 L2 + deq(qx) deq(qw)^T + bias (-> GELU), MXFP4 operands."""
+    M = qx.shape[0]
+    K = qx.shape[1] * 2
+    N = qw.shape[0]
+    if y is None:
+        y = torch.empty((M, N), dtype=out_dtype, device=qx.device)
+    y_dt = 1 if y.dtype == torch.float32 else 0
+    svdq_gemm_mxfp4(qx, sx, M, K, qw, sw, N, xl1 if rank else None, l2t if rank else None, rank,
+                    bias, ACT[act], y, y_dt, y.stride(0), stream)
     return y

@@ -18,6 +18,13 @@
 //    contiguous;
 //  - per-wave fp32 partials of X_hat L1 are reduced across the 8 waves in LDS
 //    in a fixed order (deterministic, no atomics).
+// The MXFP4 form (FMT 1) shares all of this and differs in the per-value
+// step: a 32-value block spans two lanes (l, l ^ 16); its E8M0 exponent is
+// floor(log2(amax)) - 2 clamped to [-127, 127], read off the exponent field
+// of amax; each value is scaled by the exact power of two 2^-e and rounded to
+// the nearest E2M1 value (ties to mantissa 0, saturating at 6) by seven
+// threshold compares (OCP Microscaling Formats v1.0: E2M1, E8M0, conversion
+// from FP32).
 #include "common.h"
 
 namespace {
@@ -48,7 +55,17 @@ DEV uint2 fold_fields(const uint32_t (&f)[16]) {
     return make_uint2(d0 | (d1 & 0x18618618u), d2 | (d1 & 0x61861861u));
 }
 
-template <int RT>   // RT = rank / 16 (0..8)
+// E2M1 nibble (sign bit 3, magnitude index bits 0-2) of t: nearest value,
+// ties to the even index, |t| > 6 saturates, zero has sign 0
+DEV uint32_t e2m1_nibble(float t) {
+    const float a = fabsf(t);
+    const uint32_t idx = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
+                         (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) +
+                         (uint32_t)(a > 5.0f);
+    return (t < 0.0f && idx != 0u) ? (idx | 8u) : idx;
+}
+
+template <int RT, int FMT>   // RT = rank / 16 (0..8); FMT 0: INT4 g64, 1: MXFP4
 __global__ __launch_bounds__(ROWS * 32) void act_quant_kernel(
     const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t ldx,
     const float* __restrict__ inv_lambda, const uint16_t* __restrict__ l1t,
@@ -58,7 +75,7 @@ __global__ __launch_bounds__(ROWS * 32) void act_quant_kernel(
     extern __shared__ float smem[];
     const int G = (int)(K / 64);
     float* s_inv = smem;                                   // [K]
-    uint16_t* s_sx = (uint16_t*)(smem + K);                // [ROWS][G]
+    uint16_t* s_sx = (uint16_t*)(smem + K);                // [ROWS][G] fp16, or [ROWS][2G] E8M0 bytes
     float* s_xl1 = smem + K + ((ROWS * G + 1) / 2);        // [WAVES][ROWS][16*RT]
 
     const int tid = threadIdx.x;
@@ -110,19 +127,37 @@ __global__ __launch_bounds__(ROWS * 32) void act_quant_kernel(
 #pragma unroll
         for (int j = 0; j < 16; ++j) amax = fmaxf(amax, fabsf(v[j]));
         amax = fmaxf(amax, __shfl_xor(amax, 16));
-        amax = fmaxf(amax, __shfl_xor(amax, 32));
-        const float s32 = fminf(amax / 7.0f, 65504.0f);
-        const _Float16 s16 = (_Float16)s32;
-        const float sf = (float)s16;
-        const float inv = (sf > 0.0f) ? 1.0f / sf : 0.0f;
+        if constexpr (FMT == 0) {
+            amax = fmaxf(amax, __shfl_xor(amax, 32));
+            const float s32 = fminf(amax / 7.0f, 65504.0f);
+            const _Float16 s16 = (_Float16)s32;
+            const float sf = (float)s16;
+            const float inv = (sf > 0.0f) ? 1.0f / sf : 0.0f;
 
-        uint32_t f[16];
+            uint32_t f[16];
 #pragma unroll
-        for (int j = 0; j < 16; ++j) f[j] = code_field(v[j], inv);
-        const uint2 word = fold_fields(f);
-        if (valid) {
-            *(uint2*)(qx + row * (K / 2) + g * 32 + 8 * p) = word;
-            if (p == 0) s_sx[r * G + g] = __builtin_bit_cast(uint16_t, s16);
+            for (int j = 0; j < 16; ++j) f[j] = code_field(v[j], inv);
+            const uint2 word = fold_fields(f);
+            if (valid) {
+                *(uint2*)(qx + row * (K / 2) + g * 32 + 8 * p) = word;
+                if (p == 0) s_sx[r * G + g] = __builtin_bit_cast(uint16_t, s16);
+            }
+        } else {
+            // block 2g + (p >> 1) of the row; e = floor(log2 amax) - 2 from the
+            // exponent field (a zero or subnormal amax clamps to -127)
+            const int ebits = (int)((__float_as_uint(amax) >> 23) & 0xffu);
+            const int e = ebits - 129 < -127 ? -127 : ebits - 129;
+            const float sc = __uint_as_float((uint32_t)(127 - e) << 23);   // 2^-e, exact
+            uint32_t lo = 0u, hi = 0u;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                lo |= e2m1_nibble(v[j] * sc) << (4 * j);
+                hi |= e2m1_nibble(v[8 + j] * sc) << (4 * j);
+            }
+            if (valid) {
+                *(uint2*)(qx + row * (K / 2) + g * 32 + 8 * p) = make_uint2(lo, hi);
+                if ((p & 1) == 0) ((uint8_t*)s_sx)[r * 2 * G + 2 * g + (p >> 1)] = (uint8_t)(e + 127);
+            }
         }
 
         if constexpr (RT > 0) {
@@ -188,13 +223,26 @@ __global__ __launch_bounds__(ROWS * 32) void act_quant_kernel(
     }
     __syncthreads();
 
-    // scales, quad-major [G4][M][4]: quad q of the block's rows is one
-    // contiguous 8 * ROWS-byte segment; groups past the last one are 0
+    // scales, quad-major [G4][M][8 bytes]: quad q of the block's rows is one
+    // contiguous 8 * ROWS-byte segment; groups past the last one are 0. INT4:
+    // four fp16 scales per record; MXFP4: eight E8M0 bytes, even blocks first
     const int G4 = (G + 3) / 4;
-    for (int e = tid; e < ROWS * G4 * 4; e += ROWS * 32) {
-        const int q = e / (ROWS * 4), rr = (e / 4) % ROWS, gg = 4 * q + (e & 3);
-        if (m0 + rr < M)
-            sx[((int64_t)q * M + m0 + rr) * 4 + (e & 3)] = gg < G ? s_sx[rr * G + gg] : (uint16_t)0;
+    if constexpr (FMT == 0) {
+        for (int e = tid; e < ROWS * G4 * 4; e += ROWS * 32) {
+            const int q = e / (ROWS * 4), rr = (e / 4) % ROWS, gg = 4 * q + (e & 3);
+            if (m0 + rr < M)
+                sx[((int64_t)q * M + m0 + rr) * 4 + (e & 3)] = gg < G ? s_sx[rr * G + gg] : (uint16_t)0;
+        }
+    } else {
+        const uint8_t* se = (const uint8_t*)s_sx;
+        uint8_t* sxb = (uint8_t*)sx;
+        const int nb = 2 * G;
+        for (int e = tid; e < ROWS * G4 * 8; e += ROWS * 32) {
+            const int q = e / (ROWS * 8), rr = (e / 8) % ROWS, idx = e & 7;
+            const int b = 8 * q + 2 * (idx & 3) + (idx >> 2);
+            if (m0 + rr < M)
+                sxb[((int64_t)q * M + m0 + rr) * 8 + idx] = b < nb ? se[rr * nb + b] : (uint8_t)0;
+        }
     }
     if constexpr (RT > 0) {
         const int RK = 16 * RT;
@@ -216,22 +264,41 @@ size_t act_quant_smem_bytes(int64_t K, int rank) {
     return sizeof(float) * (K + (ROWS * G + 1) / 2 + (size_t)WAVES * ROWS * rank);
 }
 
-hipError_t launch_act_quant(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
-                            const float* inv_lambda, const uint16_t* l1t, int rank,
-                            uint8_t* qx, uint16_t* sx, float* xl1, hipStream_t stream)
+namespace {
+
+template <int FMT>
+hipError_t launch_fmt(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
+                      const float* inv_lambda, const uint16_t* l1t, int rank,
+                      uint8_t* qx, uint16_t* sx, float* xl1, hipStream_t stream)
 {
     const dim3 grid((unsigned)((M + ROWS - 1) / ROWS)), block(ROWS * 32);
     const size_t smem = act_quant_smem_bytes(K, rank);
     switch (rank / 16) {
 #define CASE(RTV) case RTV: \
         if (smem > 65536) \
-            (void)hipFuncSetAttribute((const void*)act_quant_kernel<RTV>, \
+            (void)hipFuncSetAttribute((const void*)act_quant_kernel<RTV, FMT>, \
                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem); \
-        hipLaunchKernelGGL(act_quant_kernel<RTV>, grid, block, smem, stream, \
+        hipLaunchKernelGGL((act_quant_kernel<RTV, FMT>), grid, block, smem, stream, \
                            x, M, K, ldx, inv_lambda, l1t, qx, sx, xl1); break;
         CASE(0) CASE(1) CASE(2) CASE(3) CASE(4) CASE(5) CASE(6) CASE(7) CASE(8)
 #undef CASE
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_act_quant(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
+                            const float* inv_lambda, const uint16_t* l1t, int rank,
+                            uint8_t* qx, uint16_t* sx, float* xl1, hipStream_t stream)
+{
+    return launch_fmt<0>(x, M, K, ldx, inv_lambda, l1t, rank, qx, sx, xl1, stream);
+}
+
+hipError_t launch_act_quant_mxfp4(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
+                                  const float* inv_lambda, const uint16_t* l1t, int rank,
+                                  uint8_t* qx, uint8_t* sx, float* xl1, hipStream_t stream)
+{
+    return launch_fmt<1>(x, M, K, ldx, inv_lambda, l1t, rank, qx, (uint16_t*)sx, xl1, stream);
 }

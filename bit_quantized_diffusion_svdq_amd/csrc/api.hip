@@ -19,6 +19,13 @@ hipError_t launch_gemm_w4a4(const uint8_t* qx, const uint16_t* sx, const uint8_t
                             const uint16_t* sw, const float* xl1, const uint16_t* l2t, int rank,
                             const uint16_t* bias, int act, void* y, int y_f32, int64_t ldy,
                             int64_t M, int64_t N, int64_t K, hipStream_t stream);
+hipError_t launch_act_quant_mxfp4(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
+                                  const float* inv_lambda, const uint16_t* l1t, int rank,
+                                  uint8_t* qx, uint8_t* sx, float* xl1, hipStream_t stream);
+hipError_t launch_gemm_mxfp4(const uint8_t* qx, const uint8_t* sx, const uint8_t* qw,
+                             const uint8_t* sw, const float* xl1, const uint16_t* l2t, int rank,
+                             const uint16_t* bias, int act, void* y, int y_f32, int64_t ldy,
+                             int64_t M, int64_t N, int64_t K, hipStream_t stream);
 hipError_t launch_gemm_w4a4_partials(const uint8_t* qx, const uint8_t* qw, int64_t M, int64_t N,
                                      int64_t K, int64_t m0, int64_t mc, int64_t n0, int64_t nc,
                                      int32_t* p, hipStream_t stream);
@@ -122,34 +129,7 @@ svdq_status check_gemm_bytes(int64_t M, int64_t N, int64_t K) {
     return SVDQ_OK;
 }
 
-}  // namespace
-
-extern "C" {
-
-const char* svdq_status_string(svdq_status s) {
-    switch (s) {
-        case SVDQ_OK: return "ok";
-        case SVDQ_ERR_NULL: return "null pointer";
-        case SVDQ_ERR_SHAPE: return "invalid shape";
-        case SVDQ_ERR_ALIGN: return "misaligned pointer or leading dimension";
-        case SVDQ_ERR_UNSUPPORTED: return "unsupported option";
-        case SVDQ_ERR_DEVICE: return "unsupported or missing device";
-        case SVDQ_ERR_HIP: return "HIP runtime error";
-    }
-    return "unknown status";
-}
-
-const char* svdq_last_error(void) { return g_last_error.c_str(); }
-
-int svdq_version(void) { return 300; }
-
-svdq_status svdq_check_device(int device) {
-    svdq_status s = check_device_id(device);
-    if (s == SVDQ_OK) g_last_error.clear();
-    return s;
-}
-
-svdq_status svdq_quantize_act(const void* x, int64_t M, int64_t K, int64_t ldx,
+svdq_status quantize_act_impl(int mxfp4, const void* x, int64_t M, int64_t K, int64_t ldx,
                               const float* inv_lambda, const void* l1t, int32_t rank,
                               uint8_t* qx, void* sx_f16, float* xl1, void* stream) {
     svdq_status s;
@@ -168,14 +148,18 @@ svdq_status svdq_quantize_act(const void* x, int64_t M, int64_t K, int64_t ldx,
         (rank > 0 && (!aligned(l1t, 16) || !aligned(xl1, 16))))
         return fail(SVDQ_ERR_ALIGN, "x, inv_lambda, l1t, qx, sx_f16, xl1 need 16-byte alignment");
     if ((s = check_current_device()) != SVDQ_OK) return s;
-    return launched(launch_act_quant((const uint16_t*)x, M, K, ldx, inv_lambda,
-                                     rank > 0 ? (const uint16_t*)l1t : nullptr, rank, qx,
-                                     (uint16_t*)sx_f16, rank > 0 ? xl1 : nullptr,
-                                     (hipStream_t)stream),
+    const uint16_t* l1 = rank > 0 ? (const uint16_t*)l1t : nullptr;
+    float* xo = rank > 0 ? xl1 : nullptr;
+    if (mxfp4)
+        return launched(launch_act_quant_mxfp4((const uint16_t*)x, M, K, ldx, inv_lambda, l1, rank, qx,
+                                               (uint8_t*)sx_f16, xo, (hipStream_t)stream),
+                        "svdq_quantize_act_mxfp4 launch");
+    return launched(launch_act_quant((const uint16_t*)x, M, K, ldx, inv_lambda, l1, rank, qx,
+                                     (uint16_t*)sx_f16, xo, (hipStream_t)stream),
                     "svdq_quantize_act launch");
 }
 
-svdq_status svdq_gemm_w4a4(const uint8_t* qx, const void* sx_f16, int64_t M, int64_t K,
+svdq_status gemm_impl(int mxfp4, const uint8_t* qx, const void* sx_f16, int64_t M, int64_t K,
                            const uint8_t* qw, const void* sw_f16, int64_t N,
                            const float* xl1, const void* l2t, int32_t rank,
                            const void* bias, int32_t act,
@@ -205,11 +189,72 @@ svdq_status svdq_gemm_w4a4(const uint8_t* qx, const void* sx_f16, int64_t M, int
         (rank > 0 && (!aligned(xl1, 16) || !aligned(l2t, 16))))
         return fail(SVDQ_ERR_ALIGN, "qx, sx, qw, sw, xl1, l2t, y need 16-byte alignment");
     if ((s = check_current_device()) != SVDQ_OK) return s;
-    return launched(launch_gemm_w4a4(qx, (const uint16_t*)sx_f16, qw, (const uint16_t*)sw_f16,
-                                     rank > 0 ? xl1 : nullptr, rank > 0 ? (const uint16_t*)l2t : nullptr,
+    const float* xo = rank > 0 ? xl1 : nullptr;
+    const uint16_t* l2 = rank > 0 ? (const uint16_t*)l2t : nullptr;
+    if (mxfp4)
+        return launched(launch_gemm_mxfp4(qx, (const uint8_t*)sx_f16, qw, (const uint8_t*)sw_f16, xo, l2,
+                                          rank, (const uint16_t*)bias, act, y, y_dtype == SVDQ_DT_F32, ldy,
+                                          M, N, K, (hipStream_t)stream),
+                        "svdq_gemm_mxfp4 launch");
+    return launched(launch_gemm_w4a4(qx, (const uint16_t*)sx_f16, qw, (const uint16_t*)sw_f16, xo, l2,
                                      rank, (const uint16_t*)bias, act, y, y_dtype == SVDQ_DT_F32, ldy,
                                      M, N, K, (hipStream_t)stream),
                     "svdq_gemm_w4a4 launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* svdq_status_string(svdq_status s) {
+    switch (s) {
+        case SVDQ_OK: return "ok";
+        case SVDQ_ERR_NULL: return "null pointer";
+        case SVDQ_ERR_SHAPE: return "invalid shape";
+        case SVDQ_ERR_ALIGN: return "misaligned pointer or leading dimension";
+        case SVDQ_ERR_UNSUPPORTED: return "unsupported option";
+        case SVDQ_ERR_DEVICE: return "unsupported or missing device";
+        case SVDQ_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+const char* svdq_last_error(void) { return g_last_error.c_str(); }
+
+int svdq_version(void) { return 301; }
+
+svdq_status svdq_check_device(int device) {
+    svdq_status s = check_device_id(device);
+    if (s == SVDQ_OK) g_last_error.clear();
+    return s;
+}
+
+svdq_status svdq_quantize_act(const void* x, int64_t M, int64_t K, int64_t ldx,
+                              const float* inv_lambda, const void* l1t, int32_t rank,
+                              uint8_t* qx, void* sx_f16, float* xl1, void* stream) {
+    return quantize_act_impl(0, x, M, K, ldx, inv_lambda, l1t, rank, qx, sx_f16, xl1, stream);
+}
+
+svdq_status svdq_quantize_act_mxfp4(const void* x, int64_t M, int64_t K, int64_t ldx,
+                                    const float* inv_lambda, const void* l1t, int32_t rank,
+                                    uint8_t* qx, void* sx_e8m0, float* xl1, void* stream) {
+    return quantize_act_impl(1, x, M, K, ldx, inv_lambda, l1t, rank, qx, sx_e8m0, xl1, stream);
+}
+
+svdq_status svdq_gemm_w4a4(const uint8_t* qx, const void* sx_f16, int64_t M, int64_t K,
+                           const uint8_t* qw, const void* sw_f16, int64_t N,
+                           const float* xl1, const void* l2t, int32_t rank,
+                           const void* bias, int32_t act,
+                           void* y, int32_t y_dtype, int64_t ldy, void* stream) {
+    return gemm_impl(0, qx, sx_f16, M, K, qw, sw_f16, N, xl1, l2t, rank, bias, act, y, y_dtype, ldy, stream);
+}
+
+svdq_status svdq_gemm_mxfp4(const uint8_t* qx, const void* sx_e8m0, int64_t M, int64_t K,
+                            const uint8_t* qw, const void* sw_e8m0, int64_t N,
+                            const float* xl1, const void* l2t, int32_t rank,
+                            const void* bias, int32_t act,
+                            void* y, int32_t y_dtype, int64_t ldy, void* stream) {
+    return gemm_impl(1, qx, sx_e8m0, M, K, qw, sw_e8m0, N, xl1, l2t, rank, bias, act, y, y_dtype, ldy, stream);
 }
 
 svdq_status svdq_gemm_w4a4_partials(const uint8_t* qx, int64_t M, int64_t K,

@@ -48,6 +48,17 @@ DEV v16f mfma_fp6_32x32x64(const v6i& a, const v6i& b, const v16f& c) {
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, b8, c, 2, 2, 0, 0x82828282, 0, 0x82828282);
 }
 
+// D = A(32x64) * B(64x32) + C with both operands MXFP4: 32 E2M1 codes per lane
+// (4 dwords, code t at bits 4t), lane l holding row (or column) l % 32 and K
+// block l / 32, each lane scaled by its own E8M0 byte, byte OA / OB of sa / sb
+// (OCP MX block scales applied by the matrix pipe).
+template <int OA, int OB>
+DEV v16f mfma_mxfp4_32x32x64(const v4i& a, const v4i& b, const v16f& c, int sa, int sb) {
+    const v8i a8 = __builtin_shufflevector(a, a, 0, 1, 2, 3, -1, -1, -1, -1);
+    const v8i b8 = __builtin_shufflevector(b, b, 0, 1, 2, 3, -1, -1, -1, -1);
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, b8, c, 4, 4, OA, sa, OB, sb);
+}
+
 // Empty register ties: they emit no instruction, but code that uses the
 // value afterwards cannot be scheduled above them, which keeps independent
 // MFMAs in program order instead of being hoisted (and their results kept

@@ -108,7 +108,9 @@ DEV v6i unfold_frag(const uint4& raw) {
     return v6i{(int)d[0], (int)d[1], (int)d[2], (int)d[3], (int)d[4], (int)d[5]};
 }
 
-template <class C, int MODE, int ACT>   // MODE 0: bf16 out, 1: fp32 out, 2: integer partials dump
+// MODE 0: bf16 out, 1: fp32 out, 2: integer partials dump (INT4 only).
+// FMT 0: INT4 g64 with fp16 scales; 1: MXFP4 (E2M1 codes, E8M0 per 32).
+template <class C, int MODE, int ACT, int FMT = 0>
 __global__ __launch_bounds__(C::NT, C::MINB) void gemm_w4a4_kernel(
     const uint8_t* __restrict__ qx, const uint16_t* __restrict__ sx,
     const uint8_t* __restrict__ qw, const uint16_t* __restrict__ sw,
@@ -307,13 +309,16 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_w4a4_kernel(
     }
     // scales of the quad: A frag i reads tile row (wm TM + i) 32 + r32, B frag
     // j tile row BM + (wn TN + j) 32 + r32, 8 bytes each
-    int sra = (wm * TM * 32 + r32) * 8, srb = (BM + wn * TN * 32 + r32) * 8;
+    // (MXFP4: the lane's dword of the record, the exponents of its K half)
+    int sra = (wm * TM * 32 + r32) * 8 + (FMT == 1 ? 4 * hh : 0);
+    int srb = (BM + wn * TN * 32 + r32) * 8 + (FMT == 1 ? 4 * hh : 0);
     order_point(sra, srb);
     // B's scale operand of group gq: the column's scale in k = gq (lanes
     // 0..31, which hold k = 0..3), zero in every other k; lanes 32..63 hold
     // k = 4..7 and are all zero
     const uint32_t msk_lo = hh ? 0u : 0xffffu, msk_hi = hh ? 0u : 0xffff0000u;
     v6i fa[TM], fb[TN];
+    v4i fa4[TM], fb4[TN];
     uint4 ra_n[TM], rb_n[TN];
     uint2 sca[2][TM], scb[2][TN];          // a quad's raw scales, by slot parity
     auto read_a = [&](const char* cs, int gq, int i) __attribute__((always_inline)) {
@@ -323,10 +328,12 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_w4a4_kernel(
         rb_n[j] = *(const uint4*)(cs + j * 4096 + xb[gq]);
     };
     auto read_sa = [&](const char* ss, int par, int i) __attribute__((always_inline)) {
-        if constexpr (MODE != 2) sca[par][i] = *(const uint2*)(ss + i * 256 + sra);
+        if constexpr (MODE != 2 && FMT == 0) sca[par][i] = *(const uint2*)(ss + i * 256 + sra);
+        if constexpr (FMT == 1) sca[par][i].x = *(const uint32_t*)(ss + i * 256 + sra);
     };
     auto read_sb = [&](const char* ss, int par, int j) __attribute__((always_inline)) {
-        if constexpr (MODE != 2) scb[par][j] = *(const uint2*)(ss + j * 256 + srb);
+        if constexpr (MODE != 2 && FMT == 0) scb[par][j] = *(const uint2*)(ss + j * 256 + srb);
+        if constexpr (FMT == 1) scb[par][j].x = *(const uint32_t*)(ss + j * 256 + srb);
     };
     // B scale operands, one pair per frag and half of the quad: only the
     // non-zero dword is rewritten per group, the other stays 0
@@ -356,9 +363,26 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_w4a4_kernel(
 #pragma unroll
         for (int bl = 0; bl < TM * TN; ++bl) {
             const int i = bl / TN, j = bl % TN;
+            if constexpr (FMT == 1) {
+                // MXFP4: the raw 16 bytes are the operand; the block scales
+                // (byte gq of the lane's exponent dword) apply in the MFMA,
+                // which accumulates straight into acc
+                if (j == 0) fa4[i] = v4i{(int)ra_n[i].x, (int)ra_n[i].y, (int)ra_n[i].z, (int)ra_n[i].w};
+                if (i == 0) fb4[j] = v4i{(int)rb_n[j].x, (int)rb_n[j].y, (int)rb_n[j].z, (int)rb_n[j].w};
+                order_point(fa4[i], fb4[j]);
+                const int sa = (int)sca[par][i].x, sb = (int)scb[par][j].x;
+                switch (gq) {
+                    case 0: acc[i][j] = mfma_mxfp4_32x32x64<0, 0>(fa4[i], fb4[j], acc[i][j], sa, sb); break;
+                    case 1: acc[i][j] = mfma_mxfp4_32x32x64<1, 1>(fa4[i], fb4[j], acc[i][j], sa, sb); break;
+                    case 2: acc[i][j] = mfma_mxfp4_32x32x64<2, 2>(fa4[i], fb4[j], acc[i][j], sa, sb); break;
+                    default: acc[i][j] = mfma_mxfp4_32x32x64<3, 3>(fa4[i], fb4[j], acc[i][j], sa, sb); break;
+                }
+            } else {
             if (j == 0) fa[i] = unfold_frag(ra_n[i]);
             if (i == 0) fb[j] = unfold_frag(rb_n[j]);
-            if constexpr (MODE == 2) {
+            }
+            if constexpr (FMT == 1) {
+            } else if constexpr (MODE == 2) {
                 order_point(fa[i], fb[j]);
                 const v16f p = mfma_fp6_32x32x64(fa[i], fb[j], zero);
                 const int64_t col = n0 + wn * 32 * TN + j * 32 + (lane & 31);
@@ -455,8 +479,8 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_w4a4_kernel(
             step(q, 0, cs0, ss0, cs1, ss1);
             step(q + 1, 1, cs1, ss1, cs0, ss0);
         }
-        if constexpr (MODE != 2) {
-    #pragma unroll
+        if constexpr (MODE != 2 && FMT == 0) {
+#pragma unroll
             for (int e = 0; e < 16; ++e) acc[TM - 1][TN - 1][e] = __builtin_fmaf(P1[e], S1[e], acc[TM - 1][TN - 1][e]);
         }
         // every load into LDS has landed and every wave is done with the
@@ -475,15 +499,15 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_w4a4_kernel(
             // and are dropped; columns past N are masked.
             constexpr int ESZ = (MODE == 0) ? 2 : 4;
             const rsrc_t ry = make_rsrc(y, M * ldy * ESZ);
-    #pragma unroll
+#pragma unroll
             for (int j = 0; j < TN; ++j) {
                 const int64_t col = en0 + wn * 32 * TN + j * 32 + (lane & 31);
                 if (col < N) {
-    #pragma unroll
+#pragma unroll
                     for (int i = 0; i < TM; ++i) {
                         const int64_t row0 = em0 + wm * 32 * TM + i * 32 + 4 * (lane >> 5);
                         const int vo = (int)((row0 * ldy + col) * ESZ);
-    #pragma unroll
+#pragma unroll
                         for (int e = 0; e < 16; ++e) {
                             float v = acc[i][j][e] + bvj[j];
                             if constexpr (ACT == 1) v = gelu_tanh_f32(v);
@@ -516,7 +540,7 @@ int device_cu_count() {
     return cached[dev];
 }
 
-template <class C, int MODE, int ACT>
+template <class C, int MODE, int ACT, int FMT = 0>
 void launch_mode(hipStream_t stream, const uint8_t* qx, const uint16_t* sx,
                  const uint8_t* qw, const uint16_t* sw, const float* xl1, const uint16_t* l2t,
                  int rank, const uint16_t* bias, void* y, int64_t ldy, int64_t M, int64_t N,
@@ -526,7 +550,7 @@ void launch_mode(hipStream_t stream, const uint8_t* qx, const uint16_t* sx,
     // persistent workgroups: MINB per CU
     const int64_t slots = (int64_t)C::MINB * device_cu_count();
     const int64_t grid = tiles < slots ? tiles : slots;
-    hipLaunchKernelGGL((gemm_w4a4_kernel<C, MODE, ACT>), dim3((unsigned)grid), dim3(C::NT),
+    hipLaunchKernelGGL((gemm_w4a4_kernel<C, MODE, ACT, FMT>), dim3((unsigned)grid), dim3(C::NT),
                        0, stream, qx, sx, qw, sw, xl1, l2t, rank, bias, y, ldy, M, N, K,
                        pm0, pmc, pn0, pnc, p);
 }
@@ -545,6 +569,24 @@ hipError_t launch_gemm_w4a4(const uint8_t* qx, const uint16_t* sx, const uint8_t
     } else {
         if (act) launch_mode<C, 0, 1>(stream, qx, sx, qw, sw, xl1, l2t, rank, bias, y, ldy, M, N, K, 0, 0, 0, 0, nullptr);
         else launch_mode<C, 0, 0>(stream, qx, sx, qw, sw, xl1, l2t, rank, bias, y, ldy, M, N, K, 0, 0, 0, 0, nullptr);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm_mxfp4(const uint8_t* qx, const uint8_t* sx, const uint8_t* qw,
+                             const uint8_t* sw, const float* xl1, const uint16_t* l2t, int rank,
+                             const uint16_t* bias, int act, void* y, int y_f32, int64_t ldy,
+                             int64_t M, int64_t N, int64_t K, hipStream_t stream)
+{
+    using C = MainCfg;
+    const uint16_t* sx16 = (const uint16_t*)sx;
+    const uint16_t* sw16 = (const uint16_t*)sw;
+    if (y_f32) {
+        if (act) launch_mode<C, 1, 1, 1>(stream, qx, sx16, qw, sw16, xl1, l2t, rank, bias, y, ldy, M, N, K, 0, 0, 0, 0, nullptr);
+        else launch_mode<C, 1, 0, 1>(stream, qx, sx16, qw, sw16, xl1, l2t, rank, bias, y, ldy, M, N, K, 0, 0, 0, 0, nullptr);
+    } else {
+        if (act) launch_mode<C, 0, 1, 1>(stream, qx, sx16, qw, sw16, xl1, l2t, rank, bias, y, ldy, M, N, K, 0, 0, 0, 0, nullptr);
+        else launch_mode<C, 0, 0, 1>(stream, qx, sx16, qw, sw16, xl1, l2t, rank, bias, y, ldy, M, N, K, 0, 0, 0, 0, nullptr);
     }
     return hipGetLastError();
 }

@@ -139,6 +139,47 @@ svdq_status svdq_gemm_w4a4(const uint8_t* qx, const void* sx_f16, int64_t M, int
                            void* y, int32_t y_dtype, int64_t ldy, void* stream);
 
 /*
+ * MXFP4 form of the same layer (E2M1 codes, one E8M0 exponent per 32 values).
+ * The pages run the 4-bit path as INT4 or, on Blackwell, NVFP4 (remio.ai page,
+ * loading-path and benchmark sections); this is the microscaled 4-bit float
+ * format whose block scales the gfx950 matrix pipe applies itself. The number
+ * format follows the OCP Microscaling Formats (MX) Specification v1.0 (E2M1
+ * element, E8M0 scale, conversion from FP32); every other step (smoothing,
+ * low-rank branch, bias, GELU) is the INT4 layer's.
+ *
+ * Layouts (format v3, MXFP4 side):
+ *  - codes [rows][K/2]: one nibble per value, bit 3 sign, bits 0-2 the E2M1
+ *    exponent/mantissa (0, 0.5, 1, 1.5, 2, 3, 4, 6); element 2i in bits 0-3
+ *    of byte i, element 2i + 1 in bits 4-7; a zero is stored with sign 0;
+ *  - scales: E8M0 bytes (exponent + 127) in [ceil(K/256)][rows][8]: the 8
+ *    bytes of (q, r) are the exponents of blocks 8q .. 8q + 7 of row r, even
+ *    blocks first (byte 4h + j is block 8q + 2j + h); blocks past K/32 hold 0.
+ *
+ * svdq_quantize_act_mxfp4: arguments as svdq_quantize_act, with sx_e8m0 the
+ * scale array above. Per 32-value block: e = floor(log2(amax)) - 2 clamped to
+ * [-127, 127] (-127 for a block of zeros); each value x_hat * 2^-e rounded to
+ * the nearest E2M1 value, ties to mantissa 0, saturating at +-6. qx and
+ * sx_e8m0 are bit-exact with that definition; xl1 as for INT4.
+ */
+svdq_status svdq_quantize_act_mxfp4(const void* x, int64_t M, int64_t K, int64_t ldx,
+                                    const float* inv_lambda, const void* l1t, int32_t rank,
+                                    uint8_t* qx, void* sx_e8m0, float* xl1, void* stream);
+
+/*
+ * svdq_gemm_mxfp4: arguments, limits and errors as svdq_gemm_w4a4, with
+ * MXFP4 codes and E8M0 scale arrays (above) for both operands:
+ *   Y = X_hat L1 L2 + sum_k deq(a)[m,k] deq(w)[n,k] + bias   (-> GELU)
+ * The block scales are applied by the matrix pipe and the products of one
+ * 64-wide step are summed there in fp32 before joining the accumulator, so
+ * the result matches the fp64 definition to fp32 accumulation error.
+ */
+svdq_status svdq_gemm_mxfp4(const uint8_t* qx, const void* sx_e8m0, int64_t M, int64_t K,
+                            const uint8_t* qw, const void* sw_e8m0, int64_t N,
+                            const float* xl1, const void* l2t, int32_t rank,
+                            const void* bias, int32_t act,
+                            void* y, int32_t y_dtype, int64_t ldy, void* stream);
+
+/*
  * svdq_gemm_w4a4_partials -- test hook: the same device code path as
  * svdq_gemm_w4a4 (same staging, same MFMA) with the scale epilogue replaced
  * by a dump of the exact integer group partials P_g[m, n] for the rectangle

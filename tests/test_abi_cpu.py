@@ -37,6 +37,7 @@ def _declared_functions():
 def test_exports_every_declared_symbol(lib):
     names = _declared_functions()
     assert {"svdq_quantize_act", "svdq_gemm_w4a4", "awq_gemv_w4a16", "svdq_gemm_w4a4_partials",
+            "svdq_quantize_act_mxfp4", "svdq_gemm_mxfp4",
             "svdq_check_device", "svdq_status_string", "svdq_last_error", "svdq_version"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
@@ -46,7 +47,7 @@ def test_status_strings(lib):
     for s in range(7):
         assert lib.svdq_status_string(s)
     assert lib.svdq_status_string(99) == b"unknown status"
-    assert lib.svdq_version() == 300
+    assert lib.svdq_version() == 301
 
 
 def _act(lib, **kw):
@@ -133,3 +134,21 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(L, "library_path", lambda: str(tmp_path / "libsvdq.so"))
     with pytest.raises(RuntimeError, match="no fallback"):
         L.load_library()
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(K=96), SHAPE), (dict(N=100), SHAPE), (dict(qw=None), NULL), (dict(sx=B + 8), ALIGN),
+    (dict(act=2), UNSUP), (dict(M=1 << 20, K=4096), SHAPE),
+])
+def test_mxfp4_entry_points_validate_like_int4(lib, kw, status):
+    a = dict(qx=A, sx=B, M=64, K=256, qw=C, sw=D, N=128, xl1=E, l2t=E + 4096, rank=16,
+             bias=None, act=0, y=E + 65536, ydt=0, ldy=128)
+    a.update(kw)
+    assert lib.svdq_gemm_mxfp4(a["qx"], a["sx"], a["M"], a["K"], a["qw"], a["sw"], a["N"], a["xl1"],
+                               a["l2t"], a["rank"], a["bias"], a["act"], a["y"], a["ydt"], a["ldy"],
+                               None) == status
+    q = dict(x=A, M=128, K=256, ldx=256, inv=None, l1t=B, rank=16, qx=C, sx=D, xl1=E)
+    if "K" in kw and kw["K"] == 96:
+        q["K"], q["ldx"] = 96, 96
+        assert lib.svdq_quantize_act_mxfp4(q["x"], q["M"], q["K"], q["ldx"], q["inv"], q["l1t"], q["rank"],
+                                           q["qx"], q["sx"], q["xl1"], None) == SHAPE

@@ -1,0 +1,167 @@
+"""GPU parity of the MXFP4 form of the SVDQ layer against the CPU oracle
+(oracle/mxfp4.py), through the C ABI.
+
+Bars: E2M1 codes and E8M0 exponents bit-exact; xl1 relative Frobenius error
+<= 1e-4; fp32 output element-wise within the fp32 accumulation bound of the
+fp64 definition and within 1e-5 relative Frobenius; bf16 output the RTNE of
+the same kernel's fp32 output and within the 2e-3 relative Frobenius gate.
+"""
+import functools
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import mxfp4 as omx, numfmt, svdq as osv
+from gpu_util import (assert_bf16_is_rounded_fp32, dev, dev_u16, host_bf16_f64, host_u16, note,
+                      rel_fro)
+
+pytestmark = pytest.mark.gpu
+
+import bit_quantized_diffusion_svdq_amd as lib
+
+
+class DevMx:
+    """Oracle-prepared MXFP4 layer in the library's layouts."""
+
+    def __init__(self, w):
+        self.w = w
+        self.rank = w.rank
+        self.inv_lambda = dev(w.inv_lambda)
+        self.l1t = dev_u16(np.ascontiguousarray(w.l1.T)) if w.rank else None
+        self.l2t = dev_u16(np.ascontiguousarray(w.l2.T)) if w.rank else None
+        self.qw = dev(omx.pack_fp4(w.qw_codes))
+        self.sw = dev(omx.pack_scales(w.qw_exps))
+        self.bias = dev_u16(w.bias) if w.bias is not None else None
+
+
+@functools.lru_cache(maxsize=None)
+def layer(name, M=None):
+    cfg = synth.CONFIGS[name]
+    li = synth.make_layer(cfg, M=M)
+    w = omx.prepare_mx(li.x, li.w, li.bias, cfg.rank)
+    return cfg, li, w
+
+
+def check_act(qa, qx, sx, xl1, rank):
+    assert np.array_equal(qx.cpu().numpy(), omx.pack_fp4(qa.codes)), "E2M1 codes differ"
+    assert np.array_equal(sx.cpu().numpy(), omx.pack_scales(qa.exps)), "E8M0 exponents differ"
+    if rank:
+        e = rel_fro(xl1.cpu().numpy(), qa.xl1)
+        assert e <= 1e-4, e
+
+
+def magnitude(qa_codes, qa_exps, w_codes, w_exps, xl1, l2_bits, bias_bits):
+    """sum of |terms| per output (the scale of the fp32 accumulation error)."""
+    a = np.abs(omx.dequantize_rows(qa_codes, qa_exps))
+    w = np.abs(omx.dequantize_rows(w_codes, w_exps))
+    t = a @ w.T
+    if xl1 is not None and xl1.shape[1]:
+        t += np.abs(xl1.astype(np.float64)) @ np.abs(numfmt.bf16_bits_to_f32(l2_bits).astype(np.float64))
+    if bias_bits is not None:
+        t += np.abs(numfmt.bf16_bits_to_f32(bias_bits).astype(np.float64))[None, :]
+    return t
+
+
+def assert_fp32(y32, y64, tmag, K, rank):
+    # fp32 sums of K / 64 MFMA steps, the low-rank MFMAs, bias: a few ulps of
+    # the magnitude per term that meets the accumulator
+    bound = 2.0 * (K // 64 + rank + 4) * 2.0 ** -24 * tmag
+    assert np.all(np.abs(y32 - y64) <= bound + 1e-30), float(np.max(np.abs(y32 - y64) - bound))
+    assert rel_fro(y32, y64) <= 1e-5
+
+
+@pytest.mark.parametrize("name,M", [("tiny", None), ("tiny", 77), ("qkv", None)])
+def test_mx_act_parity(name, M):
+    note(f"mxfp4 act {name} M={M}")
+    cfg, li, w = layer(name, M)
+    dw = DevMx(w)
+    qx, sx, xl1 = lib.quantize_act_mxfp4(dev_u16(li.x), dw.inv_lambda, dw.l1t, cfg.rank)
+    torch.cuda.synchronize()
+    qa = omx.quantize_act(li.x, w.inv_lambda, w.l1)
+    check_act(qa, qx, sx, xl1, cfg.rank)
+
+
+def test_mx_act_edge_values():
+    """Exact E2M1 ties, saturation, zero blocks, tiny and clamped exponents."""
+    note("mxfp4 act edge values")
+    M, K = 16, 320                                   # 10 blocks: a padded scale quad
+    rng = np.random.default_rng(4)
+    xf = rng.standard_normal((M, K)).astype(np.float32)
+    xf[0] = 0.0
+    xf[1, :32] = 0.0
+    xf[2, :10] = [6, 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, -0.25, -5.0]
+    xf[2, 10:32] = 0.0
+    xf[3, :32] = np.linspace(-7.9, 7.9, 32)          # amax < 8: values above 6 saturate
+    xf[4] *= 1e-30
+    xf[5, :32] *= 2.0 ** -125                        # exponent clamps at -127
+    xf[6] *= 1e30
+    xbits = numfmt.f32_to_bf16_bits(xf)
+    qx, sx, _ = lib.quantize_act_mxfp4(dev_u16(xbits), None, None, 0)
+    torch.cuda.synchronize()
+    qa = omx.quantize_act(xbits, None, None)
+    check_act(qa, qx, sx, None, 0)
+
+
+@pytest.mark.parametrize("act,bias", [("none", True), ("gelu_tanh", True), ("none", False)])
+def test_mx_gemm_tiny(act, bias):
+    note(f"mxfp4 gemm tiny act={act} bias={bias}")
+    cfg, li, w = layer("tiny")
+    dw = DevMx(w)
+    qa = omx.quantize_act(li.x, w.inv_lambda, w.l1)
+    qxd, sxd, xld = dev(omx.pack_fp4(qa.codes)), dev(omx.pack_scales(qa.exps)), dev(qa.xl1)
+    b = dw.bias if bias else None
+    bb = w.bias if bias else None
+    y32 = lib.mxfp4_linear(qxd, sxd, xld, dw.qw, dw.sw, dw.l2t, b, cfg.rank, act=act, out_dtype=torch.float32)
+    ybf = lib.mxfp4_linear(qxd, sxd, xld, dw.qw, dw.sw, dw.l2t, b, cfg.rank, act=act)
+    torch.cuda.synchronize()
+    y64 = omx.linear_output(qa.codes, qa.exps, w.qw_codes, w.qw_exps, qa.xl1, w.l2, bb, act)
+    y32h = y32.cpu().numpy()
+    if act == "none":
+        tmag = magnitude(qa.codes, qa.exps, w.qw_codes, w.qw_exps, qa.xl1, w.l2, bb)
+        assert_fp32(y32h, y64, tmag, cfg.K, cfg.rank)
+    else:
+        assert rel_fro(y32h, y64) <= 1e-5
+    assert_bf16_is_rounded_fp32(host_u16(ybf), y32h)
+    assert rel_fro(host_bf16_f64(ybf), y64) <= 2e-3
+
+
+def test_mx_gemm_ragged_and_ranks():
+    """Ragged M and N against the tile, rank 0, the maximum rank, a half rank
+    chunk, and K with a partly filled scale quad."""
+    for (M, K, N, r) in [(77, 192, 200, 0), (130, 320, 136, 128), (300, 704, 264, 48)]:
+        note(f"mxfp4 ragged M={M} K={K} N={N} r={r}")
+        x = synth.make_matrix_bf16(M, K, seed=M, std=1.0)
+        wb = synth.make_matrix_bf16(K, N, seed=N, std=0.05)
+        b = synth.make_matrix_bf16(1, N, seed=3, std=0.02)[0]
+        w = omx.prepare_mx(x, wb, b, r)
+        dw = DevMx(w)
+        qx, sx, xl1 = lib.quantize_act_mxfp4(dev_u16(x), dw.inv_lambda, dw.l1t, r)
+        y = lib.mxfp4_linear(qx, sx, xl1, dw.qw, dw.sw, dw.l2t, dw.bias, r, out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        qa, y64 = omx.forward(w, x)
+        check_act(qa, qx, sx, xl1, r)
+        assert rel_fro(y.cpu().numpy(), y64) <= 1e-5, (M, K, N, r)
+
+
+def test_mx_qkv_full_size():
+    """The QKV shape end to end (act + GEMM, the launches the benchmark
+    times): every code and exponent compared; outputs on sampled rows."""
+    note("mxfp4 qkv full size")
+    cfg, li, w = layer("qkv")
+    dw = DevMx(w)
+    qx, sx, xl1 = lib.quantize_act_mxfp4(dev_u16(li.x), dw.inv_lambda, dw.l1t, cfg.rank)
+    y = lib.mxfp4_linear(qx, sx, xl1, dw.qw, dw.sw, dw.l2t, dw.bias, cfg.rank)
+    yf = lib.mxfp4_linear(qx, sx, xl1, dw.qw, dw.sw, dw.l2t, dw.bias, cfg.rank, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    qa = omx.quantize_act(li.x, w.inv_lambda, w.l1)
+    check_act(qa, qx, sx, xl1, cfg.rank)
+    rows = np.unique(np.concatenate([np.arange(0, 8), np.arange(cfg.M - 8, cfg.M),
+                                     np.random.default_rng(0).choice(cfg.M, 40, replace=False)]))
+    y64 = omx.linear_output(qa.codes[rows], qa.exps[rows], w.qw_codes, w.qw_exps, qa.xl1[rows],
+                            w.l2, w.bias)
+    tmag = magnitude(qa.codes[rows], qa.exps[rows], w.qw_codes, w.qw_exps, qa.xl1[rows], w.l2, w.bias)
+    assert_fp32(yf.cpu().numpy()[rows], y64, tmag, cfg.K, cfg.rank)
+    assert_bf16_is_rounded_fp32(host_u16(y), yf.cpu().numpy())
+    assert rel_fro(host_bf16_f64(y)[rows], y64) <= 2e-3
