@@ -29,7 +29,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
-PEAK_FP6_TFLOPS = 10100.0     # MI355X dense FP6/FP4 MFMA: the instruction the GEMM runs on
+PEAK_FP6_TFLOPS = 10100.0     # MI355X dense FP6 MFMA: the instruction the INT4 GEMM runs on
+PEAK_FP4_TFLOPS = 10100.0     # MI355X dense FP4 MFMA (the MXFP4 GEMM)
 PEAK_INT8_TOPS = 5000.0       # MI355X dense INT8 MFMA: the integer peak INT4 x INT4 is quoted against
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 
@@ -138,6 +139,69 @@ def gemm_traffic_bytes():
     if t is None or t["source_sha256"] != gemm_source_digest():
         return None
     return int(round(1024 * (t["fetch_kib"] * t["fetch_factor"] + t["write_kib"] * t["write_factor"])))
+
+
+def mxfp4_block(lib, dev, iters=50):
+    """The MXFP4 form on a transformer block's four linears at 4608 tokens
+    (4096 image + 512 text): QKV 3072->9216, out 3072->3072, fc1 3072->12288
+    with GELU, fc2 12288->3072 on fc1's output; rank 32. One step = activation
+    quantisation + GEMM for each. Weights are random codes with E8M0
+    exponents of a realistic range (kernel time does not depend on values)."""
+    import torch
+    M, R = 4608, 32
+    g = torch.Generator().manual_seed(21)
+
+    def layer(K, N):
+        G4 = (K // 64 + 3) // 4
+        return dict(K=K, N=N,
+                    inv=(torch.rand(K, generator=g) + 0.5).to(dev),
+                    l1t=(torch.randn((R, K), generator=g) * 0.05).to(torch.bfloat16).to(dev),
+                    l2t=(torch.randn((N, R), generator=g) * 0.1).to(torch.bfloat16).to(dev),
+                    qw=torch.randint(0, 256, (N, K // 2), generator=g, dtype=torch.uint8).to(dev),
+                    sw=torch.randint(114, 122, (G4, N, 8), generator=g, dtype=torch.uint8).to(dev),
+                    bias=(torch.randn(N, generator=g) * 0.02).to(torch.bfloat16).to(dev))
+    L = [layer(3072, 9216), layer(3072, 3072), layer(3072, 12288), layer(12288, 3072)]
+    xq = torch.randn((M, 3072), generator=g).to(torch.bfloat16).to(dev)
+    xo = torch.randn((M, 3072), generator=g).to(torch.bfloat16).to(dev)
+    xf = torch.randn((M, 3072), generator=g).to(torch.bfloat16).to(dev)
+    ys = [torch.empty((M, l["N"]), dtype=torch.bfloat16, device=dev) for l in L]
+    marks = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(4)]
+             for _ in range(iters)]
+
+    def run(li, x, act, y, mk):
+        l = L[li]
+        qx, sx, xl1 = lib.quantize_act_mxfp4(x, l["inv"], l["l1t"], R)
+        if mk is not None:
+            mk[0].record()
+        lib.mxfp4_linear(qx, sx, xl1, l["qw"], l["sw"], l["l2t"], l["bias"], R, act=act, y=y)
+        if mk is not None:
+            mk[1].record()
+
+    def step(i=None):
+        mk = marks[i] if i is not None else [None] * 4
+        run(0, xq, "none", ys[0], mk[0])
+        run(1, xo, "none", ys[1], mk[1])
+        run(2, xf, "gelu_tanh", ys[2], mk[2])
+        run(3, ys[2], "none", ys[3], mk[3])
+
+    for _ in range(20):
+        step()
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for i in range(iters):
+        step(i)
+    e.record()
+    e.synchronize()
+    block_ms = s.elapsed_time(e) / iters
+    gemm_ms = [sum(marks[i][k][0].elapsed_time(marks[i][k][1]) for i in range(iters)) / iters for k in range(4)]
+    ops = 2.0 * M * sum(l["K"] * l["N"] for l in L)
+    gsum = sum(gemm_ms)
+    return {"M": M, "ops": ops, "block_us": round(block_ms * 1e3, 2),
+            "block_TOPS": round(ops / (block_ms * 1e-3) / 1e12, 1),
+            "gemm_us": [round(x * 1e3, 2) for x in gemm_ms],
+            "gemm_TOPS": round(ops / (gsum * 1e-3) / 1e12, 1),
+            "gemm_frac_of_fp4_peak": round(ops / (gsum * 1e-3) / 1e12 / PEAK_FP4_TFLOPS, 4)}
 
 
 def cpu_baseline(M, K, N, rank, budget_s=20.0):
@@ -302,6 +366,9 @@ def main():
         extra.update({"mlp_pair_us": round(mlp_ms * 1e3, 2),
                       "mlp_pair_TOPS": round(mlp_flops / (mlp_ms * 1e-3) / 1e12, 1)})
         log(f"gemv {gemv_ms * 1e3:.2f} us, mlp pair {mlp_ms * 1e3:.1f} us")
+        del fc1, fc2, h, y2
+        extra["mxfp4_block"] = mxfp4_block(lib, dev)
+        log(f"mxfp4 block {extra['mxfp4_block']['block_us']} us")
 
     out = {
         "metric": "W4A4 linear effective TOPS (M4096 K3072 N9216 r32) + % of MI355X MFMA peak",
