@@ -22,9 +22,10 @@
 // step: a 32-value block spans two lanes (l, l ^ 16); its E8M0 exponent is
 // floor(log2(amax)) - 2 clamped to [-127, 127], read off the exponent field
 // of amax; each value is scaled by the exact power of two 2^-e and rounded to
-// the nearest E2M1 value (ties to mantissa 0, saturating at 6) by seven
-// threshold compares (OCP Microscaling Formats v1.0: E2M1, E8M0, conversion
-// from FP32).
+// the nearest E2M1 value (ties to mantissa 0, saturating at 6) by
+// v_cvt_scalef32_pk_fp4_f32 with scale 1 (OCP Microscaling Formats v1.0:
+// E2M1, E8M0, conversion from FP32). The instruction keeps the sign of values
+// that round to zero; those nibbles get sign 0 afterwards.
 #include "common.h"
 
 namespace {
@@ -55,14 +56,17 @@ DEV uint2 fold_fields(const uint32_t (&f)[16]) {
     return make_uint2(d0 | (d1 & 0x18618618u), d2 | (d1 & 0x61861861u));
 }
 
-// E2M1 nibble (sign bit 3, magnitude index bits 0-2) of t: nearest value,
-// ties to the even index, |t| > 6 saturates, zero has sign 0
-DEV uint32_t e2m1_nibble(float t) {
-    const float a = fabsf(t);
-    const uint32_t idx = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
-                         (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) +
-                         (uint32_t)(a > 5.0f);
-    return (t < 0.0f && idx != 0u) ? (idx | 8u) : idx;
+// Eight E2M1 nibbles (t[0] in bits 0-3): round to nearest, ties to mantissa
+// 0, saturating at 6 (the conversion instruction), then the sign of every
+// zero nibble cleared: (mag + 7) carries into bit 3 exactly when mag != 0.
+DEV uint32_t e2m1_x8(const float* t) {
+    uint32_t w = 0u;
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, t[0], t[1], 1.0f, 0);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, t[2], t[3], 1.0f, 1);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, t[4], t[5], 1.0f, 2);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, t[6], t[7], 1.0f, 3);
+    const uint32_t nonzero = ((w & 0x77777777u) + 0x77777777u) & 0x88888888u;
+    return w & (0x77777777u | nonzero);
 }
 
 template <int RT, int FMT>   // RT = rank / 16 (0..8); FMT 0: INT4 g64, 1: MXFP4
@@ -148,12 +152,10 @@ __global__ __launch_bounds__(ROWS * 32) void act_quant_kernel(
             const int ebits = (int)((__float_as_uint(amax) >> 23) & 0xffu);
             const int e = ebits - 129 < -127 ? -127 : ebits - 129;
             const float sc = __uint_as_float((uint32_t)(127 - e) << 23);   // 2^-e, exact
-            uint32_t lo = 0u, hi = 0u;
+            float t[16];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                lo |= e2m1_nibble(v[j] * sc) << (4 * j);
-                hi |= e2m1_nibble(v[8 + j] * sc) << (4 * j);
-            }
+            for (int j = 0; j < 16; ++j) t[j] = v[j] * sc;
+            const uint32_t lo = e2m1_x8(t), hi = e2m1_x8(t + 8);
             if (valid) {
                 *(uint2*)(qx + row * (K / 2) + g * 32 + 8 * p) = make_uint2(lo, hi);
                 if ((p & 1) == 0) ((uint8_t*)s_sx)[r * 2 * G + 2 * g + (p >> 1)] = (uint8_t)(e + 127);
