@@ -80,6 +80,13 @@ DEV uint4 ld128(rsrc_t r, int off, int soff) {
     return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
+// read-once data (codes, scales, zero points): non-temporal, so the stream
+// does not push x and inv_s (read by every workgroup) out of L2
+DEV uint4 ld128_stream(rsrc_t r, int off, int soff) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, soff, 2);   // nt
+    return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
 DEV uint32_t pk(uint16_t a, uint16_t b) { return (uint32_t)a | ((uint32_t)b << 16); }
 
 template <int NQ, int TPW>
@@ -135,16 +142,19 @@ __global__ __launch_bounds__(NT, 2) void gemv_w4a16_kernel(
     for (int pc0 = 0; pc0 < KP; pc0 += CP) {
         const int np = (KP - pc0) < CP ? (KP - pc0) : CP;       // pairs in this chunk
         const int gc = 2 * np, g0 = 2 * pc0;                    // groups in this chunk
-        // this wave's pairs [ps, pe) of the chunk
+        // this wave's pairs [ps, pe) of the chunk = its groups [gs, gs + ng); the
+        // wave prepares exactly the A blocks and scales it reads itself (no
+        // workgroup barrier: each wave starts once its own data has landed)
         const int ps = (wave * np) / NW, pe = ((wave + 1) * np) / NW;
         const int plast = pe > ps ? pe - 1 : ps;
-        const int xitems = gc * NQ * 8;                         // (group, quad, 8 channels)
-        const int sitems = TPW * gc * 2;                        // (tile, group, 8 columns) uint4
+        const int gs = 2 * ps, ng = 2 * (pe - ps), ngd = ng > 0 ? ng : 1;
+        const int xitems = ng * NQ * 8;                         // (group, quad, 8 channels)
+        const int sitems = TPW * ng * 2;                        // (tile, group, 8 columns) uint4
 
         // ---- 1. preparation loads (x, inv_s; scales, zero points), issued first
         auto xload = [&](int it, uint4 (&xr)[4], uint4& s0, uint4& s1) {
-            const int itc = it < xitems ? it : xitems - 1;      // clamped: stays in bounds
-            const int sub = itc & 7, q = (itc >> 3) & (NQ - 1), gl = itc >> (3 + LNQ);
+            const int itc = it < xitems ? it : (xitems > 0 ? xitems - 1 : 0);   // clamped: in bounds
+            const int sub = itc & 7, q = (itc >> 3) & (NQ - 1), gl = gs + (itc >> (3 + LNQ));
             const int k = (g0 + gl) * 64 + sub * 8;
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) {
@@ -162,24 +172,24 @@ __global__ __launch_bounds__(NT, 2) void gemv_w4a16_kernel(
         };
         // scale / zero item: 8 columns (half a tile row) of group gl of tile ti
         auto sitem = [&](int it, int& ti, int& gl, int& h) {
-            const int itc = it < sitems ? it : sitems - 1;
+            const int itc = it < sitems ? it : (sitems > 0 ? sitems - 1 : 0);
             h = itc & 1;
             const int r = itc >> 1;                             // row (tile, group) of the block
-            ti = r / gc;
-            gl = r - ti * gc;
+            ti = r / ngd;
+            gl = gs + r - ti * ngd;
         };
         auto sload = [&](int it, uint4& sb, uint4& zb) {
             int ti, gl, h;
             sitem(it, ti, gl, h);
             const int tt = t0 + ti < T ? t0 + ti : T - 1;
             const int off = ((tt * G + g0 + gl) * 16 + 8 * h) * 2;
-            sb = ld128(rsc, off, 0);
-            zb = ld128(rzr, off, 0);
+            sb = ld128_stream(rsc, off, 0);
+            zb = ld128_stream(rzr, off, 0);
         };
         uint4 xr0[4], xs0, xs1, sb0, zb0, sb1, zb1;
-        xload(tid, xr0, xs0, xs1);
-        sload(tid, sb0, zb0);
-        sload(tid + NT, sb1, zb1);
+        xload(lane, xr0, xs0, xs1);
+        sload(lane, sb0, zb0);
+        sload(lane + 64, sb1, zb1);
         // keep these ahead of the weight loads: loads complete in issue order,
         // so waiting for a preparation load must not wait for the weights
         __builtin_amdgcn_sched_barrier(0);
@@ -188,7 +198,7 @@ __global__ __launch_bounds__(NT, 2) void gemv_w4a16_kernel(
         // order, and (scale, 128 + zero) per (group, column)
         auto xprep = [&](const uint4 (&xr)[4], const uint4& s0, const uint4& s1, int it) {
             if (it >= xitems) return;
-            const int sub = it & 7, q = (it >> 3) & (NQ - 1), gl = it >> (3 + LNQ);
+            const int sub = it & 7, q = (it >> 3) & (NQ - 1), gl = gs + (it >> (3 + LNQ));
             // channels 8 sub .. 8 sub + 7 of group gl: lane p = 2 (gl & 1) + (sub >> 2), step sub & 3
             const int pl = 2 * (gl & 1) + (sub >> 2), st = sub & 3;
             char* blk = s_a + ((q * CP + (gl >> 1)) * 4 + st) * ABLK;
@@ -229,15 +239,15 @@ __global__ __launch_bounds__(NT, 2) void gemv_w4a16_kernel(
         // prepared before any weight load is issued (waiting for them then
         // never waits for the weight stream, and no control-flow merge
         // happens while weights are in flight)
-        for (int it0 = NT; it0 < xitems; it0 += NT) {
+        for (int it0 = 64; it0 < xitems; it0 += 64) {
             uint4 xr[4], s0, s1;
-            xload(it0 + tid, xr, s0, s1);
-            xprep(xr, s0, s1, it0 + tid);
+            xload(it0 + lane, xr, s0, s1);
+            xprep(xr, s0, s1, it0 + lane);
         }
-        for (int it0 = 2 * NT; it0 < sitems; it0 += NT) {
+        for (int it0 = 128; it0 < sitems; it0 += 64) {
             uint4 sb, zb;
-            sload(it0 + tid, sb, zb);
-            sprep(sb, zb, it0 + tid);
+            sload(it0 + lane, sb, zb);
+            sprep(sb, zb, it0 + lane);
         }
 
         // ---- 2. this wave's first batch of codes
@@ -254,23 +264,26 @@ __global__ __launch_bounds__(NT, 2) void gemv_w4a16_kernel(
                 // wave-uniform offset: keep it in an SGPR (a VGPR offset would turn
                 // each buffer load into a waterfall loop)
                 const int wb = __builtin_amdgcn_readfirstlane((tcl * KP + pcl) * 1024);
-                qv[i] = ld128(rw, woff, wb);
+                qv[i] = ld128_stream(rw, woff, wb);
                 __builtin_amdgcn_sched_barrier(0);     // issue in task order (= consumption order)
             }
         };
         load_batch(ps);
         __builtin_amdgcn_sched_barrier(0);
 
-        // ---- 3. preparation into LDS (first items)
-        // zero slots of the A blocks
-        for (int b = tid; b < NQ * np * 4; b += NT) {
-            const int q = b / (np * 4), rest = b - q * np * 4;
-            *(uint4*)(s_a + (q * CP * 4 + rest) * ABLK + 512) = make_uint4(0u, 0u, 0u, 0u);
+        // ---- 3. preparation into LDS (first items): zero slots of this
+        // wave's A blocks, then its x~ and scales. Only this wave reads them,
+        // and LDS operations of one wave complete in issue order, so a
+        // compiler fence and the wave's own LDS counter are the only waits.
+        const int nb = NQ * (pe - ps) * 4;
+        for (int b = lane; b < nb; b += 64) {
+            const int q = b / ((pe - ps) * 4), rest = b - q * (pe - ps) * 4;
+            *(uint4*)(s_a + ((q * CP + ps) * 4 + rest) * ABLK + 512) = make_uint4(0u, 0u, 0u, 0u);
         }
-        xprep(xr0, xs0, xs1, tid);
-        sprep(sb0, zb0, tid);
-        sprep(sb1, zb1, tid + NT);
-        __syncthreads();
+        xprep(xr0, xs0, xs1, lane);
+        sprep(sb0, zb0, lane);
+        sprep(sb1, zb1, lane + 64);
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 
         // ---- 4. stream the tasks, pair by pair: the pair's A fragments are
         // read once and serve its TPW tiles; X (the per-row group sums of
@@ -334,7 +347,8 @@ __global__ __launch_bounds__(NT, 2) void gemv_w4a16_kernel(
                 compute(j0);
             }
         }
-        __syncthreads();                  // LDS reuse by the next chunk
+        if (pc0 + CP < KP) __syncthreads();   // LDS reuse by the next chunk (the reduction
+                                              // buffer below is a region of its own)
     }
 
     // ---- 5. sum the 4 lanes of every column (hi/lo, both groups), then the
