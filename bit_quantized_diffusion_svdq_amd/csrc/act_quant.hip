@@ -35,14 +35,17 @@ constexpr int WAVES = 8;
 
 // Quantise one value given the group's fp32 reciprocal `inv` (0 when the
 // scale is 0) and return its FP6 E2M3 field: magnitude in bits 0-2, zero
-// exponent, sign in bit 5 (zero is stored with sign 0).
+// exponent, sign in bit 5 (zero is stored with sign 0). Clamping to [-7, 7]
+// before rounding equals clamping after it (the bounds are integers);
+// |a| + 1.5 * 2^23 rounds |a| half-to-even into the low mantissa bits (the
+// spacing there is 1 and the constant is even), and round(a) < 0 exactly
+// when a + 0.5 < 0, which gives the sign without a compare.
 DEV uint32_t code_field(float v, float inv) {
-    float t = v * inv;                         // one fp32 multiply (no contraction)
-    t = __builtin_rintf(t);                    // round half to even
-    t = fminf(fmaxf(t, -7.0f), 7.0f);
-    uint32_t mag = (uint32_t)(int)fabsf(t);
-    uint32_t sgn = (__float_as_uint(t) >> 26) & 32u;  // sign bit -> bit 5
-    return (t != 0.0f) ? (mag | sgn) : 0u;
+    const float t = v * inv;                   // one fp32 multiply (no contraction)
+    const float a = __builtin_amdgcn_fmed3f(t, -7.0f, 7.0f);
+    const uint32_t mag = __float_as_uint(fabsf(a) + 12582912.0f) & 7u;
+    const uint32_t sgn = (__float_as_uint(a + 0.5f) >> 26) & 32u;
+    return mag | sgn;
 }
 
 // Sixteen E2M3 fields (code e at bits 6e..6e+5 of a 96-bit stream T) -> the
