@@ -48,6 +48,16 @@
  *  - AWQ 4-bit codes (format v1): unsigned nibbles 0..15, byte i of a row
  *    holds element 2i in bits 0-3 and element 2i+1 in bits 4-7.
  *  - bf16 and fp16 values are passed as their 16-bit patterns.
+ *  - Fused projections (the query, key and value projections merged into one
+ *    grouped operation, which a loader must map back with a stated tensor
+ *    order: remio.ai page, section on the generic integration path): one
+ *    layer whose output columns are the projections in order along N
+ *    ([Q | K | V]), prepared offline on the concatenated weight (one
+ *    smoothing vector, one L1, so one activation pass). Every weight-side
+ *    array is indexed by output column and slices along N (qw rows, the
+ *    middle axis of the quad-major scales, rows of the [N][r] up-projection,
+ *    bias); a slice used with the fused layer's qx, sx and xl1 gives exactly
+ *    those output columns.
  */
 #ifndef SVDQ_H
 #define SVDQ_H

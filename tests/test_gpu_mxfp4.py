@@ -165,3 +165,18 @@ def test_mx_qkv_full_size():
     assert_fp32(yf.cpu().numpy()[rows], y64, tmag, cfg.K, cfg.rank)
     assert_bf16_is_rounded_fp32(host_u16(y), yf.cpu().numpy())
     assert rel_fro(host_bf16_f64(y)[rows], y64) <= 2e-3
+
+
+def test_mx_fused_projection_column_split():
+    """The fused-projection column split on the MXFP4 layer (QKV size)."""
+    note("mxfp4 fused projection split qkv")
+    cfg, li, w = layer("qkv")
+    dw = DevMx(w)
+    qx, sx, xl1 = lib.quantize_act_mxfp4(dev_u16(li.x), dw.inv_lambda, dw.l1t, cfg.rank)
+    sizes = (3072, 3072, 3072)
+    y = lib.mxfp4_linear(qx, sx, xl1, dw.qw, dw.sw, dw.l2t, dw.bias, cfg.rank)
+    parts = lib.projection_weights(dw.qw, dw.sw, dw.l2t, dw.bias, sizes)
+    ys = [lib.mxfp4_linear(qx, sx, xl1, q, s, l2, b, cfg.rank) for (q, s, l2, b) in parts]
+    torch.cuda.synchronize()
+    for view, yp in zip(lib.split_columns(y, sizes), ys):
+        assert torch.equal(view.contiguous().view(torch.int16), yp.view(torch.int16))

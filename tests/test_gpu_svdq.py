@@ -230,3 +230,20 @@ def test_qkv_linear_full_size():
     assert_fp32_output(y32h[rows], y64, tmag, cfg.K // 64 + cfg.rank)
     assert_bf16_is_rounded_fp32(host_u16(ybf), y32h)
     assert rel_fro(host_bf16_f64(ybf)[rows], y64) <= 2e-3
+
+
+@pytest.mark.parametrize("name,sizes", [("qkv", (3072, 3072, 3072)), ("tiny", (200, 160, 152))])
+def test_fused_projection_column_split(name, sizes):
+    """A fused [Q | K | V] layer: each projection's weight side (column
+    slices of the packed tensors) with the fused layer's activation side
+    gives bit-identical columns of the fused output."""
+    note(f"fused projection split {name} {sizes}")
+    cfg, li, w = layer(name)
+    dw = DevSvdq(w)
+    qx, sx, xl1 = run_act(li.x, dw, cfg.rank)
+    y = lib.w4a4_linear(qx, sx, xl1, dw.qw, dw.sw, dw.l2t, dw.bias, cfg.rank)
+    parts = lib.projection_weights(dw.qw, dw.sw, dw.l2t, dw.bias, sizes)
+    ys = [lib.w4a4_linear(qx, sx, xl1, q, s, l2, b, cfg.rank) for (q, s, l2, b) in parts]
+    torch.cuda.synchronize()
+    for view, yp in zip(lib.split_columns(y, sizes), ys):
+        assert torch.equal(view.contiguous().view(torch.int16), yp.view(torch.int16))
