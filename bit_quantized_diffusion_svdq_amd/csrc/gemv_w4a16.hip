@@ -26,14 +26,17 @@
 //    folds its own rows.
 //  - About one workgroup per CU: workgroup i owns TPW consecutive column
 //    tiles (TPW = 1, 2, 4, 5 or 8, template; 5 at 4 x 3072 -> 18432 on 256
-//    CUs) and prepares x~ = x inv_s (bf16 hi/lo in the A-operand order) and
-//    the scales and offsets of its tiles once in LDS. Its 8 waves split the
-//    group pairs into 8 parts; wave w streams part w of every tile of the workgroup, pair-major
-//    with the tile index a compile-time constant, so each tile keeps its own
-//    accumulator in registers and the task stream has no branch. The first
-//    loads are issued before the preparation so the weight stream starts at
-//    once. Lanes and parts are summed in LDS in a fixed order at the end
-//    (deterministic).
+//    CUs). Its 8 waves split the group pairs into 8 parts; wave w streams
+//    part w of every tile of the workgroup, pair-major with the tile index a
+//    compile-time constant, so each tile keeps its own accumulator in
+//    registers and the task stream has no branch. Each wave prepares, in its
+//    own LDS region, exactly what it reads: x~ = x inv_s (bf16 hi/lo in the
+//    A-operand order) for its group pairs and the scales and offsets of its
+//    groups of every tile; so no workgroup barrier stands between a wave's
+//    data landing and its arithmetic. The first loads are issued before the
+//    preparation so the weight stream starts at once; codes, scales and zero
+//    points are read with the non-temporal policy. Lanes and parts are summed
+//    in LDS in a fixed order at the end (deterministic).
 //  - Token rows are processed in quads (NQ = 1, 2 or 4, template): every quad
 //    has its own A operand and accumulator; weights are loaded once.
 #include "common.h"
