@@ -384,12 +384,10 @@ template <int NQ, int TPW>
 void launch(const uint16_t* x, int M, int K, const float* inv_s, const uint8_t* qwt,
             const uint16_t* scale, const uint16_t* zero, int N, const uint16_t* bias, uint16_t* y,
             hipStream_t stream) {
-    static bool attr = false;
-    if (!attr) {
-        (void)hipFuncSetAttribute((const void*)gemv_w4a16_kernel<NQ, TPW>,
-                                  hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BUDGET);
-        attr = true;
-    }
+    // set on every launch (a host-side call, no stream work): the attribute
+    // belongs to the current device, and a cached flag would miss a second one
+    (void)hipFuncSetAttribute((const void*)gemv_w4a16_kernel<NQ, TPW>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BUDGET);
     const int T = N / 16;
     hipLaunchKernelGGL((gemv_w4a16_kernel<NQ, TPW>), dim3((unsigned)((T + TPW - 1) / TPW)), dim3(NT),
                        LDS_BUDGET, stream, x, M, K, inv_s, qwt, scale, zero, N, bias, y);
