@@ -58,6 +58,7 @@ def synth_linear(M, K, N, rank, seed, device):
     import torch
 
     import synth
+    from bit_quantized_diffusion_svdq_amd import pack_l1
     cfg = synth.LayerConfig("bench", M=M, K=K, N=N, rank=rank, n_outliers=max(1, round(0.01 * K)),
                             outlier_factor=30.0, seed=seed)
     li = synth.make_layer(cfg)
@@ -70,7 +71,7 @@ def synth_linear(M, K, N, rank, seed, device):
     ops = dict(
         x=bf16(li.x),
         inv_lambda=torch.from_numpy(rng.uniform(0.05, 1.0, K).astype(np.float32)).to(device),
-        l1t=(torch.randn((rank, K), generator=g) * 0.05).to(torch.bfloat16).to(device),
+        l1t=pack_l1((torch.randn((K, rank), generator=g) * 0.05).to(torch.bfloat16)).to(device),
         l2t=(torch.randn((N, rank), generator=g) * 0.1).to(torch.bfloat16).to(device),
         qw=torch.randint(0, 256, (N, K // 2), generator=g, dtype=torch.uint8).to(device),
         sw=(torch.rand(((K // 64 + 3) // 4, N, 4), generator=g) * 0.02 + 0.01).to(torch.float16).to(device),
@@ -148,6 +149,8 @@ def mxfp4_block(lib, dev, iters=50):
     quantisation + GEMM for each. Weights are random codes with E8M0
     exponents of a realistic range (kernel time does not depend on values)."""
     import torch
+
+    from bit_quantized_diffusion_svdq_amd import pack_l1
     M, R = 4608, 32
     g = torch.Generator().manual_seed(21)
 
@@ -155,7 +158,7 @@ def mxfp4_block(lib, dev, iters=50):
         G4 = (K // 64 + 3) // 4
         return dict(K=K, N=N,
                     inv=(torch.rand(K, generator=g) + 0.5).to(dev),
-                    l1t=(torch.randn((R, K), generator=g) * 0.05).to(torch.bfloat16).to(dev),
+                    l1t=pack_l1((torch.randn((K, R), generator=g) * 0.05).to(torch.bfloat16)).to(dev),
                     l2t=(torch.randn((N, R), generator=g) * 0.1).to(torch.bfloat16).to(dev),
                     qw=torch.randint(0, 256, (N, K // 2), generator=g, dtype=torch.uint8).to(dev),
                     sw=torch.randint(114, 122, (G4, N, 8), generator=g, dtype=torch.uint8).to(dev),

@@ -139,9 +139,23 @@ def awq_gemv_w4a16(x, M, K, inv_s, qw, scale, zero, N, bias, y, stream=None):
 # ---------------------------------------------------------------- tensor helpers
 # (allocate outputs with torch, then call the entry points above)
 
+def pack_l1(l1: torch.Tensor) -> torch.Tensor:
+    """The down-projection L1 [K, r] (bf16; K a multiple of 64, r of 16) in the
+    L1 tile layout the activation kernels read (include/svdq.h, format v4):
+    a flat tensor ordered (group g, 16-rank tile t, step s, lane l, j) holding
+    L1[64 g + 16 (l // 16) + 8 s + j, 16 t + l % 16]. Indexing only."""
+    K, r = l1.shape
+    if K % 64 or r % 16:
+        raise ValueError(f"L1 must be [K, r] with K % 64 == 0 and r % 16 == 0, got {tuple(l1.shape)}")
+    # K = (g, p, s, j) with p = l // 16; r = (t, n) with n = l % 16
+    v = l1.reshape(K // 64, 4, 2, 8, r // 16, 16)
+    return v.permute(0, 4, 2, 1, 5, 3).contiguous().reshape(-1)
+
+
 def quantize_act(x: torch.Tensor, inv_lambda, l1t, rank: int, stream=None):
-    """x: bf16 [M, K] on the GPU -> (qx uint8 [M, K/2], sx fp16 [ceil(K/256), M, 4]
-    (quad-major group scales), xl1 fp32 [M, r])."""
+    """x: bf16 [M, K] on the GPU; l1t: L1 in the tile layout (pack_l1) ->
+    (qx uint8 [M, K/2], sx fp16 [ceil(K/256), M, 4] (quad-major group scales),
+    xl1 fp32 [M, r])."""
     M, K = x.shape
     dev = x.device
     qx = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)

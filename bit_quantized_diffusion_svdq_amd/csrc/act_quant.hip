@@ -14,8 +14,10 @@
 //    absmax with two cross-lane max steps;
 //  - the same registers feed the down-projection on the bf16 MFMA
 //    (16x16x32), with X_hat split into bf16 hi + lo so the product keeps
-//    ~16 mantissa bits; L1 is stored transposed so B-operand loads are
-//    contiguous;
+//    ~16 mantissa bits; L1 arrives in a tile layout in which the B operand
+//    of every (group, 16-rank tile, 32-channel step) is 1 KB in lane order
+//    (lane l holds channels 16 (l / 16) + 8 step .. + 7 of rank l % 16, the
+//    channels its A operand holds), so each L1 load is one contiguous 1 KB;
 //  - per-wave fp32 partials of X_hat L1 are reduced across the 8 waves in LDS
 //    in a fixed order (deterministic, no atomics).
 // The MXFP4 form (FMT 1) shares all of this and differs in the per-value
@@ -108,14 +110,17 @@ __global__ __launch_bounds__(ROWS * 32) void act_quant_kernel(
         d[0] = *(const uint4*)(xrow + kb);
         d[1] = *(const uint4*)(xrow + kb + 8);
     };
+    // L1 in its tile layout: the B fragments of (group, rank tile, step) are
+    // 1 KB in lane order, so each load instruction reads one contiguous
+    // kilobyte (a [rank][K] layout touches 16 rows per instruction, which
+    // costs the load pipe about twice as much)
     auto loadl = [&](v8bf (&d)[RTX][2], int i) {
         if constexpr (RT > 0) {
-            const int kb = gidx(i) * 64 + 16 * p;
 #pragma unroll
             for (int t = 0; t < RT; ++t) {
-                const uint16_t* lrow = l1t + (int64_t)(16 * t + r) * K + kb;
-                d[t][0] = *(const v8bf*)(lrow);
-                d[t][1] = *(const v8bf*)(lrow + 8);
+                const uint16_t* lf = l1t + ((int64_t)(gidx(i) * RT + t) * 2) * 512 + lane * 8;
+                d[t][0] = *(const v8bf*)(lf);
+                d[t][1] = *(const v8bf*)(lf + 512);
             }
         }
     };

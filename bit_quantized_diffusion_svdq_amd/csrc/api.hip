@@ -221,7 +221,7 @@ const char* svdq_status_string(svdq_status s) {
 
 const char* svdq_last_error(void) { return g_last_error.c_str(); }
 
-int svdq_version(void) { return 301; }
+int svdq_version(void) { return 401; }
 
 svdq_status svdq_check_device(int device) {
     svdq_status s = check_device_id(device);

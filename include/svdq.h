@@ -103,8 +103,13 @@ int svdq_version(void);
  *
  *  x          bf16 [M][ldx], row m's K values contiguous (ldx >= K, ldx % 8 == 0)
  *  inv_lambda fp32 [K] smoothing reciprocals, or NULL for lambda == 1
- *  l1t        bf16 [rank][K]: row j is column j of L1 (the down-projection);
- *             NULL iff rank == 0
+ *  l1t        the down-projection L1 (K x rank, bf16) in the L1 tile layout
+ *             (format v4): an array [K/64][rank/16][2][64][8] whose element
+ *             (g, t, s, l, j) is L1[64 g + 16 (l / 16) + 8 s + j][16 t + l % 16],
+ *             i.e. for each 64-channel group g, 16-rank tile t and 32-channel
+ *             step s, 1 KB in which lane l's 16 bytes are the 8 channels of
+ *             rank 16 t + l % 16 that pair with lane l's activation values;
+ *             K * rank values in all. NULL iff rank == 0
  *  rank       0..128, multiple of 16
  *  qx         out: packed codes [M][K/2]
  *  sx_f16     out: fp16 scales [ceil(K/256)][M][4] (quad-major, zero padded)

@@ -241,6 +241,45 @@ def unpack_scales(packed: np.ndarray, G: int) -> np.ndarray:
     return out
 
 
+def pack_l1_tiles(l1_bits: np.ndarray) -> np.ndarray:
+    """L1 (bf16 bits [K, r], r a multiple of 16) -> the L1 tile layout
+    (format v4) as a flat uint16 array: for each 64-channel group g, 16-rank
+    tile t, 32-channel step s and lane l = 0..63, eight values
+    L1[64 g + 16 (l // 16) + 8 s + j, 16 t + l % 16] for j = 0..7, in the
+    order (g, t, s, l, j)."""
+    l1 = np.asarray(l1_bits, np.uint16)
+    K, r = l1.shape
+    if K % 64 or r % 16:
+        raise ValueError("K must be a multiple of 64 and r of 16")
+    out = np.empty(K * r, np.uint16)
+    pos = 0
+    for g in range(K // 64):
+        for t in range(r // 16):
+            for st in range(2):
+                for lane in range(64):
+                    k0 = 64 * g + 16 * (lane // 16) + 8 * st
+                    out[pos:pos + 8] = l1[k0:k0 + 8, 16 * t + lane % 16]
+                    pos += 8
+    return out
+
+
+def unpack_l1_tiles(packed: np.ndarray, K: int, r: int) -> np.ndarray:
+    """Inverse of pack_l1_tiles -> bf16 bits [K, r]."""
+    p = np.asarray(packed, np.uint16).reshape(-1)
+    if p.size != K * r:
+        raise ValueError("size does not match K * r")
+    out = np.empty((K, r), np.uint16)
+    pos = 0
+    for g in range(K // 64):
+        for t in range(r // 16):
+            for st in range(2):
+                for lane in range(64):
+                    k0 = 64 * g + 16 * (lane // 16) + 8 * st
+                    out[k0:k0 + 8, 16 * t + lane % 16] = p[pos:pos + 8]
+                    pos += 8
+    return out
+
+
 @dataclass
 class SvdqWeights:
     """Offline artefacts of one SVDQ layer (what a quantised checkpoint holds)."""

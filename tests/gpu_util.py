@@ -51,13 +51,14 @@ def rel_fro(a, b) -> float:
 
 class DevSvdq:
     """Oracle-prepared SVDQ layer moved to the device in the ABI layouts:
-    L1 as [r][K] (transposed), L2 as [N][r] (transposed)."""
+    L1 in the L1 tile layout, L2 as [N][r] (transposed)."""
 
     def __init__(self, w):
+        from oracle import svdq as osv
         self.w = w
         self.rank = w.rank
         self.inv_lambda = dev(w.inv_lambda)
-        self.l1t = dev_u16(np.ascontiguousarray(w.l1.T)) if w.rank else None
+        self.l1t = dev_u16(osv.pack_l1_tiles(w.l1)) if w.rank else None
         self.l2t = dev_u16(np.ascontiguousarray(w.l2.T)) if w.rank else None
         self.qw = dev(w.qw)
         self.sw = dev_scales(w.sw)

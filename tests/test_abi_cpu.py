@@ -47,7 +47,7 @@ def test_status_strings(lib):
     for s in range(7):
         assert lib.svdq_status_string(s)
     assert lib.svdq_status_string(99) == b"unknown status"
-    assert lib.svdq_version() == 301
+    assert lib.svdq_version() == 401
 
 
 def _act(lib, **kw):

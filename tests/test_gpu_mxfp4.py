@@ -29,7 +29,7 @@ class DevMx:
         self.w = w
         self.rank = w.rank
         self.inv_lambda = dev(w.inv_lambda)
-        self.l1t = dev_u16(np.ascontiguousarray(w.l1.T)) if w.rank else None
+        self.l1t = dev_u16(osv.pack_l1_tiles(w.l1)) if w.rank else None
         self.l2t = dev_u16(np.ascontiguousarray(w.l2.T)) if w.rank else None
         self.qw = dev(omx.pack_fp4(w.qw_codes))
         self.sw = dev(omx.pack_scales(w.qw_exps))

@@ -66,7 +66,7 @@ def test_act_quant_ranks_and_no_smoothing(rank, use_inv):
     l1 = numfmt.f32_to_bf16_bits((rng.standard_normal((K, rank)) * 0.1).astype(np.float32))
     xd = dev_u16(x)
     qx, sx, xl1 = lib.quantize_act(xd, dev(inv) if use_inv else None,
-                                   dev_u16(np.ascontiguousarray(l1.T)) if rank else None, rank)
+                                   dev_u16(osv.pack_l1_tiles(l1)) if rank else None, rank)
     torch.cuda.synchronize()
     qa = osv.quantize_act(x, inv, l1 if rank else None)
     check_act(qa, qx, sx, xl1, rank)

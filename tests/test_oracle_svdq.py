@@ -290,3 +290,40 @@ def test_gelu_tanh_values():
     erf_gelu = np.array([0.5 * t * (1 + math.erf(t / math.sqrt(2))) for t in x])
     assert np.max(np.abs(g - erf_gelu)) < 1e-3                          # tanh form approximates erf form
     assert abs(svdq.gelu_tanh(np.array([30.0]))[0] - 30.0) < 1e-12
+
+
+def test_l1_tile_layout_hand_case_and_roundtrip():
+    """The L1 tile layout (format v4): element (g, t, s, l, j) of the flat
+    array is L1[64 g + 16 (l // 16) + 8 s + j, 16 t + l % 16]. Values that
+    encode their own (k, rank) position make every slot checkable by hand."""
+    K, r = 128, 32
+    l1 = (np.arange(K)[:, None] * 256 + np.arange(r)[None, :]).astype(np.uint16)   # = 256 k + n
+    p = svdq.pack_l1_tiles(l1)
+    assert p.shape == (K * r,)
+    # first 1 KB: g 0, t 0, s 0; lane 0 holds k 0..7 of rank 0, lane 17 k 16..23 of rank 1
+    assert p[0:8].tolist() == [256 * k for k in range(8)]
+    assert p[17 * 8:18 * 8].tolist() == [256 * k + 1 for k in range(16, 24)]
+    # step 1 of the same tile: lane 63 holds k 56..63 of rank 15
+    base = 512
+    assert p[base + 63 * 8:base + 64 * 8].tolist() == [256 * k + 15 for k in range(56, 64)]
+    # tile t = 1 of group 0 (ranks 16..31), then group 1 (k 64..127)
+    assert p[2 * 512:2 * 512 + 8].tolist() == [256 * k + 16 for k in range(8)]
+    assert p[4 * 512 + 5 * 8:4 * 512 + 6 * 8].tolist() == [256 * k + 5 for k in range(64, 72)]
+    rng = np.random.default_rng(2)
+    for K2, r2 in [(64, 16), (320, 48), (3072, 128)]:
+        a = rng.integers(0, 65536, (K2, r2)).astype(np.uint16)
+        assert np.array_equal(svdq.unpack_l1_tiles(svdq.pack_l1_tiles(a), K2, r2), a)
+
+
+def test_library_l1_packer_matches_oracle():
+    """The package's pack_l1 (torch indexing) and the oracle's packer (loops
+    over the definition) are written apart; they must agree."""
+    import torch
+    import bit_quantized_diffusion_svdq_amd as lib
+    rng = np.random.default_rng(3)
+    for K, r in [(64, 16), (320, 48), (3072, 32), (1024, 128)]:
+        a = rng.integers(0, 65536, (K, r)).astype(np.uint16)
+        got = lib.pack_l1(torch.from_numpy(a.view(np.int16))).numpy().view(np.uint16)
+        assert np.array_equal(got, svdq.pack_l1_tiles(a)), (K, r)
+    with pytest.raises(ValueError):
+        lib.pack_l1(torch.zeros((96, 16), dtype=torch.int16))
