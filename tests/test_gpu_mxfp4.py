@@ -180,3 +180,19 @@ def test_mx_fused_projection_column_split():
     torch.cuda.synchronize()
     for view, yp in zip(lib.split_columns(y, sizes), ys):
         assert torch.equal(view.contiguous().view(torch.int16), yp.view(torch.int16))
+
+
+def test_mx_act_strided_rows():
+    """MXFP4 activation kernel on rows with a leading dimension beyond K."""
+    note("mxfp4 act ldx > K")
+    M, K, r, pad = 70, 320, 32, 64
+    xw = synth.make_matrix_bf16(M, K + pad, seed=13, std=1.5)
+    x = np.ascontiguousarray(xw[:, 32:32 + K])
+    rng = np.random.default_rng(14)
+    inv = rng.uniform(0.3, 2.0, K).astype(np.float32)
+    l1 = numfmt.f32_to_bf16_bits((rng.standard_normal((K, r)) * 0.1).astype(np.float32))
+    xd = dev_u16(xw)[:, 32:32 + K]
+    qx, sx, xl1 = lib.quantize_act_mxfp4(xd, dev(inv), dev_u16(osv.pack_l1_tiles(l1)), r)
+    torch.cuda.synchronize()
+    qa = omx.quantize_act(x, inv, l1)
+    check_act(qa, qx, sx, xl1, r)

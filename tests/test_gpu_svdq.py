@@ -247,3 +247,21 @@ def test_fused_projection_column_split(name, sizes):
     torch.cuda.synchronize()
     for view, yp in zip(lib.split_columns(y, sizes), ys):
         assert torch.equal(view.contiguous().view(torch.int16), yp.view(torch.int16))
+
+
+def test_act_quant_strided_rows():
+    """X rows with a leading dimension beyond K (a column window of a wider
+    activation, 16-byte aligned): codes, scales and xl1 as for dense rows."""
+    note("act_quant ldx > K")
+    M, K, r, pad = 70, 320, 32, 64
+    xw = synth.make_matrix_bf16(M, K + pad, seed=11, std=1.5)
+    x = np.ascontiguousarray(xw[:, 32:32 + K])
+    rng = np.random.default_rng(12)
+    inv = rng.uniform(0.3, 2.0, K).astype(np.float32)
+    l1 = numfmt.f32_to_bf16_bits((rng.standard_normal((K, r)) * 0.1).astype(np.float32))
+    xd = dev_u16(xw)[:, 32:32 + K]
+    assert xd.stride(0) == K + pad
+    qx, sx, xl1 = lib.quantize_act(xd, dev(inv), dev_u16(osv.pack_l1_tiles(l1)), r)
+    torch.cuda.synchronize()
+    qa = osv.quantize_act(x, inv, l1)
+    check_act(qa, qx, sx, xl1, r)
