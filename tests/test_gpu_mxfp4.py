@@ -196,3 +196,25 @@ def test_mx_act_strided_rows():
     torch.cuda.synchronize()
     qa = omx.quantize_act(x, inv, l1)
     check_act(qa, qx, sx, xl1, r)
+
+
+def test_mx_fc2_full_size():
+    """The MXFP4 block's longest-K layer at full size: fc2, 4608 x 12288 ->
+    3072, rank 32 (a seeded stand-in for the GELU output as input). Every
+    code and exponent of the activation pass; outputs on sampled rows."""
+    note("mxfp4 fc2 full size")
+    c2 = synth.CONFIGS["mlp_fc2"]
+    li = synth.make_layer(c2, M=8)                   # fc2's weights and bias
+    x = synth.make_matrix_bf16(c2.M, c2.K, seed=31, std=0.4)
+    w = omx.prepare_mx(x, li.w, li.bias, c2.rank)
+    dw = DevMx(w)
+    qx, sx, xl1 = lib.quantize_act_mxfp4(dev_u16(x), dw.inv_lambda, dw.l1t, c2.rank)
+    y = lib.mxfp4_linear(qx, sx, xl1, dw.qw, dw.sw, dw.l2t, dw.bias, c2.rank)
+    torch.cuda.synchronize()
+    qa = omx.quantize_act(x, w.inv_lambda, w.l1)
+    check_act(qa, qx, sx, xl1, c2.rank)
+    rows = np.unique(np.concatenate([np.arange(0, 4), np.arange(c2.M - 4, c2.M),
+                                     np.random.default_rng(2).choice(c2.M, 24, replace=False)]))
+    y64 = omx.linear_output(qa.codes[rows], qa.exps[rows], w.qw_codes, w.qw_exps, qa.xl1[rows],
+                            w.l2, w.bias)
+    assert rel_fro(host_bf16_f64(y)[rows], y64) <= 2e-3

@@ -265,3 +265,40 @@ def test_act_quant_strided_rows():
     torch.cuda.synchronize()
     qa = osv.quantize_act(x, inv, l1)
     check_act(qa, qx, sx, xl1, r)
+
+
+def test_mlp_pair_full_size():
+    """The MLP pair at full size (4608 tokens): fc1 3072 -> 12288 with the GELU
+    epilogue, then fc2 12288 -> 3072 whose activation pass reads fc1's bf16
+    output (fc2's offline preparation is calibrated on that output). Codes and
+    scales of both activation passes are compared in full, xl1 and the GEMM
+    outputs on sampled rows."""
+    note("mlp pair full size")
+    c1, c2 = synth.CONFIGS["mlp_fc1"], synth.CONFIGS["mlp_fc2"]
+    li1 = synth.make_layer(c1)
+    w1 = osv.prepare_svdq(li1.x, li1.w, li1.bias, c1.rank)
+    d1 = DevSvdq(w1)
+    qx1, sx1, xl1_1 = run_act(li1.x, d1, c1.rank)
+    h = lib.w4a4_linear(qx1, sx1, xl1_1, d1.qw, d1.sw, d1.l2t, d1.bias, c1.rank, act="gelu_tanh")
+    torch.cuda.synchronize()
+    qa1 = osv.quantize_act(li1.x, w1.inv_lambda, w1.l1)
+    check_act(qa1, qx1, sx1, xl1_1, c1.rank)
+    rows = np.unique(np.concatenate([np.arange(0, 4), np.arange(c1.M - 4, c1.M),
+                                     np.random.default_rng(1).choice(c1.M, 24, replace=False)]))
+    y64_1 = osv.gelu_tanh(osv.linear_output(qa1.codes[rows], qa1.sx[rows], w1.qw_codes, w1.sw,
+                                            qa1.xl1[rows], w1.l2, w1.bias))
+    assert rel_fro(host_bf16_f64(h)[rows], y64_1) <= 2e-3
+
+    note("mlp pair fc2 (K 12288)")
+    h_bits = host_u16(h)
+    li2 = synth.make_layer(c2, M=8)                  # fc2's weights and bias (its x is not used)
+    w2 = osv.prepare_svdq(h_bits, li2.w, li2.bias, c2.rank)
+    d2 = DevSvdq(w2)
+    qx2, sx2, xl1_2 = lib.quantize_act(h, d2.inv_lambda, d2.l1t, c2.rank)
+    y2 = lib.w4a4_linear(qx2, sx2, xl1_2, d2.qw, d2.sw, d2.l2t, d2.bias, c2.rank)
+    torch.cuda.synchronize()
+    qa2 = osv.quantize_act(h_bits, w2.inv_lambda, w2.l1)
+    check_act(qa2, qx2, sx2, xl1_2, c2.rank)
+    y64_2 = osv.linear_output(qa2.codes[rows], qa2.sx[rows], w2.qw_codes, w2.sw, qa2.xl1[rows],
+                              w2.l2, w2.bias)
+    assert rel_fro(host_bf16_f64(y2)[rows], y64_2) <= 2e-3
