@@ -68,14 +68,21 @@ DEV int slot_of(int o) { return (o < 4) ? 2 * o : 2 * (o - 4) + 1; }
 
 DEV uint32_t and_or(uint32_t x, uint32_t m, uint32_t c) { return (x & m) | c; }
 
-DEV v8bf codes_to_bf16(uint32_t x, uint32_t magic) {
-    const uint32_t y = x >> 8;
-    uint32_t d[4];
-    d[0] = and_or(x, 0x000F000Fu, magic);
-    d[1] = and_or(x >> 4, 0x000F000Fu, magic);
-    d[2] = and_or(y, 0x000F000Fu, magic);
-    d[3] = and_or(y >> 4, 0x000F000Fu, magic);
-    return __builtin_bit_cast(v8bf, make_uint4(d[0], d[1], d[2], d[3]));
+// Two dwords of codes at once: one 64-bit shift serves both dwords (the bits
+// that cross from the high dword into the low one fall outside the nibble
+// mask), so 16 codes take 3 shifts instead of 6.
+DEV void codes2_to_bf16(uint32_t x0, uint32_t x1, uint32_t magic, v8bf& b0, v8bf& b1) {
+    const uint64_t v = ((uint64_t)x1 << 32) | x0;
+    uint64_t s4, s8, s12;
+    asm("v_lshrrev_b64 %0, 4, %1" : "=v"(s4) : "v"(v));
+    asm("v_lshrrev_b64 %0, 8, %1" : "=v"(s8) : "v"(v));
+    asm("v_lshrrev_b64 %0, 12, %1" : "=v"(s12) : "v"(v));
+    b0 = __builtin_bit_cast(v8bf, make_uint4(and_or(x0, 0x000F000Fu, magic), and_or((uint32_t)s4, 0x000F000Fu, magic),
+                                             and_or((uint32_t)s8, 0x000F000Fu, magic),
+                                             and_or((uint32_t)s12, 0x000F000Fu, magic)));
+    b1 = __builtin_bit_cast(v8bf, make_uint4(and_or(x1, 0x000F000Fu, magic), and_or((uint32_t)(s4 >> 32), 0x000F000Fu, magic),
+                                             and_or((uint32_t)(s8 >> 32), 0x000F000Fu, magic),
+                                             and_or((uint32_t)(s12 >> 32), 0x000F000Fu, magic)));
 }
 
 DEV uint4 ld128(rsrc_t r, int off, int soff) {
@@ -318,7 +325,7 @@ __global__ __launch_bounds__(NT, 2) void gemv_w4a16_kernel(
                     const uint32_t qd[4] = {qw.x, qw.y, qw.z, qw.w};
                     v8bf b[4];
 #pragma unroll
-                    for (int st = 0; st < 4; ++st) b[st] = codes_to_bf16(qd[st], magic);
+                    for (int st = 0; st < 4; st += 2) codes2_to_bf16(qd[st], qd[st + 1], magic, b[st], b[st + 1]);
                     const float2 so = s_so[g * TC + ti * 16 + c];
                     const float sc = live ? so.x : 0.0f;
                     const float oe = so.y;
