@@ -151,7 +151,7 @@ __global__ __launch_bounds__(NT, 2) void gemv_w4a16_kernel(
 
     for (int pc0 = 0; pc0 < KP; pc0 += CP) {
         const int np = (KP - pc0) < CP ? (KP - pc0) : CP;       // pairs in this chunk
-        const int gc = 2 * np, g0 = 2 * pc0;                    // groups in this chunk
+        const int g0 = 2 * pc0;                                 // first group of this chunk
         // this wave's pairs [ps, pe) of the chunk = its groups [gs, gs + ng); the
         // wave prepares exactly the A blocks and scales it reads itself (no
         // workgroup barrier: each wave starts once its own data has landed)
