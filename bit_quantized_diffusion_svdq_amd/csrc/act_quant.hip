@@ -4,11 +4,13 @@
 // The fusion of the low-rank down-projection with input quantisation is the
 // one the remio.ai page attributes to the original Nunchaku engine (section
 // "SVDQuant moves hard values out of 4-bit"); here it is re-derived for CDNA4:
-//  - one workgroup owns 16 token rows; its 8 waves take the 64-wide groups of
-//    K round-robin, so every row is read from HBM exactly once with 128-byte
-//    contiguous row segments per group; each wave issues the loads of six of
-//    its groups at once (and the L1 fragments one group ahead) before it
-//    quantises them, to keep enough bytes in flight for HBM;
+//  - one workgroup owns 16 token rows; its waves (16 for ranks up to 32,
+//    else 8, as registers allow) take the 64-wide groups of K round-robin, so
+//    every row is read from HBM exactly once with 128-byte contiguous row
+//    segments per group; each wave issues the loads of four (with 16 waves)
+//    or six of its groups at once (and the L1 fragments one group ahead)
+//    before it quantises them, to keep enough bytes in flight for HBM while
+//    a SIMD always has some wave whose data has landed;
 //  - a lane holds 16 consecutive channels of one row (two dwordx4 loads);
 //    the four lanes of a row (lanes l, l^16, l^32, l^48) reduce the group
 //    absmax with two cross-lane max steps;
@@ -18,7 +20,7 @@
 //    of every (group, 16-rank tile, 32-channel step) is 1 KB in lane order
 //    (lane l holds channels 16 (l / 16) + 8 step .. + 7 of rank l % 16, the
 //    channels its A operand holds), so each L1 load is one contiguous 1 KB;
-//  - per-wave fp32 partials of X_hat L1 are reduced across the 8 waves in LDS
+//  - per-wave fp32 partials of X_hat L1 are reduced across the waves in LDS
 //    in a fixed order (deterministic, no atomics).
 // The MXFP4 form (FMT 1) shares all of this and differs in the per-value
 // step: a 32-value block spans two lanes (l, l ^ 16); its E8M0 exponent is
@@ -33,7 +35,10 @@
 namespace {
 
 constexpr int ROWS = 16;
-constexpr int WAVES = 8;
+// waves per workgroup: 16 (four per SIMD) while the rank leaves room in 128
+// VGPRs (rank <= 32), else 8; more waves with fewer groups in flight each let a
+// SIMD work on whichever wave's data has landed
+__host__ __device__ constexpr int waves_for(int rt) { return rt <= 2 ? 16 : 8; }
 
 // Quantise one value given the group's fp32 reciprocal `inv` (0 when the
 // scale is 0) and return its FP6 E2M3 field: magnitude in bits 0-2, zero
@@ -75,12 +80,13 @@ DEV uint32_t e2m1_x8(const float* t) {
 }
 
 template <int RT, int FMT>   // RT = rank / 16 (0..8); FMT 0: INT4 g64, 1: MXFP4
-__global__ __launch_bounds__(ROWS * 32) void act_quant_kernel(
+__global__ __launch_bounds__(waves_for(RT) * 64) void act_quant_kernel(
     const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t ldx,
     const float* __restrict__ inv_lambda, const uint16_t* __restrict__ l1t,
     uint8_t* __restrict__ qx, uint16_t* __restrict__ sx, float* __restrict__ xl1)
 {
     constexpr int RTX = RT > 0 ? RT : 1;
+    constexpr int WAVES = waves_for(RT), NTH = WAVES * 64;
     extern __shared__ float smem[];
     const int G = (int)(K / 64);
     float* s_inv = smem;                                   // [K]
@@ -193,9 +199,9 @@ __global__ __launch_bounds__(ROWS * 32) void act_quant_kernel(
     };
 
     // the X loads of up to CH groups are all issued before any is processed
-    // (with 2 waves per SIMD that keeps ~96 KB per CU in flight); L1 fragments
+    // (16 waves x 4 groups or 8 x 6: 64 or 48 KB per CU in flight); L1 fragments
     // run one group ahead
-    constexpr int CH = 6;
+    constexpr int CH = WAVES == 16 ? 4 : 6;
     v8bf la[RTX][2], lb[RTX][2];
     for (int c0 = 0; c0 < ((n + CH - 1) / CH) * CH || c0 == 0; c0 += CH) {
         uint4 xs[CH][2];
@@ -204,7 +210,7 @@ __global__ __launch_bounds__(ROWS * 32) void act_quant_kernel(
         loadl(la, c0);
         if (c0 == 0) {
             // the smoothing reciprocals go to LDS while the first X loads fly
-            for (int64_t k = 4 * tid; k < K; k += 4 * ROWS * 32)
+            for (int64_t k = 4 * tid; k < K; k += 4 * NTH)
                 *(float4*)(s_inv + k) = inv_lambda ? *(const float4*)(inv_lambda + k)
                                                    : make_float4(1.f, 1.f, 1.f, 1.f);
             __syncthreads();
@@ -238,7 +244,7 @@ __global__ __launch_bounds__(ROWS * 32) void act_quant_kernel(
     // four fp16 scales per record; MXFP4: eight E8M0 bytes, even blocks first
     const int G4 = (G + 3) / 4;
     if constexpr (FMT == 0) {
-        for (int e = tid; e < ROWS * G4 * 4; e += ROWS * 32) {
+        for (int e = tid; e < ROWS * G4 * 4; e += NTH) {
             const int q = e / (ROWS * 4), rr = (e / 4) % ROWS, gg = 4 * q + (e & 3);
             if (m0 + rr < M)
                 sx[((int64_t)q * M + m0 + rr) * 4 + (e & 3)] = gg < G ? s_sx[rr * G + gg] : (uint16_t)0;
@@ -247,7 +253,7 @@ __global__ __launch_bounds__(ROWS * 32) void act_quant_kernel(
         const uint8_t* se = (const uint8_t*)s_sx;
         uint8_t* sxb = (uint8_t*)sx;
         const int nb = 2 * G;
-        for (int e = tid; e < ROWS * G4 * 8; e += ROWS * 32) {
+        for (int e = tid; e < ROWS * G4 * 8; e += NTH) {
             const int q = e / (ROWS * 8), rr = (e / 8) % ROWS, idx = e & 7;
             const int b = 8 * q + 2 * (idx & 3) + (idx >> 2);
             if (m0 + rr < M)
@@ -256,7 +262,7 @@ __global__ __launch_bounds__(ROWS * 32) void act_quant_kernel(
     }
     if constexpr (RT > 0) {
         const int RK = 16 * RT;
-        for (int e = tid; e < ROWS * RK; e += ROWS * 32) {
+        for (int e = tid; e < ROWS * RK; e += NTH) {
             const int rr = e / RK;
             if (m0 + rr >= M) continue;
             float s = 0.0f;
@@ -271,7 +277,7 @@ __global__ __launch_bounds__(ROWS * 32) void act_quant_kernel(
 
 size_t act_quant_smem_bytes(int64_t K, int rank) {
     const int64_t G = K / 64;
-    return sizeof(float) * (K + (ROWS * G + 1) / 2 + (size_t)WAVES * ROWS * rank);
+    return sizeof(float) * (K + (ROWS * G + 1) / 2 + (size_t)waves_for(rank / 16) * ROWS * rank);
 }
 
 namespace {
@@ -281,14 +287,14 @@ hipError_t launch_fmt(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
                       const float* inv_lambda, const uint16_t* l1t, int rank,
                       uint8_t* qx, uint16_t* sx, float* xl1, hipStream_t stream)
 {
-    const dim3 grid((unsigned)((M + ROWS - 1) / ROWS)), block(ROWS * 32);
+    const dim3 grid((unsigned)((M + ROWS - 1) / ROWS));
     const size_t smem = act_quant_smem_bytes(K, rank);
     switch (rank / 16) {
 #define CASE(RTV) case RTV: \
         if (smem > 65536) \
             (void)hipFuncSetAttribute((const void*)act_quant_kernel<RTV, FMT>, \
                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem); \
-        hipLaunchKernelGGL((act_quant_kernel<RTV, FMT>), grid, block, smem, stream, \
+        hipLaunchKernelGGL((act_quant_kernel<RTV, FMT>), grid, dim3(waves_for(RTV) * 64), smem, stream, \
                            x, M, K, ldx, inv_lambda, l1t, qx, sx, xl1); break;
         CASE(0) CASE(1) CASE(2) CASE(3) CASE(4) CASE(5) CASE(6) CASE(7) CASE(8)
 #undef CASE
