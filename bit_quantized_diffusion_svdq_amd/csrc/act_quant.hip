@@ -7,7 +7,7 @@
 //  - one workgroup owns 16 token rows; its waves (16 for ranks up to 32,
 //    else 8, as registers allow) take the 64-wide groups of K round-robin, so
 //    every row is read from HBM exactly once with 128-byte contiguous row
-//    segments per group; each wave issues the loads of four (with 16 waves)
+//    segments per group; each wave issues the loads of two (with 16 waves)
 //    or six of its groups at once (and the L1 fragments one group ahead)
 //    before it quantises them, to keep enough bytes in flight for HBM while
 //    a SIMD always has some wave whose data has landed;
@@ -199,9 +199,9 @@ __global__ __launch_bounds__(waves_for(RT) * 64) void act_quant_kernel(
     };
 
     // the X loads of up to CH groups are all issued before any is processed
-    // (16 waves x 4 groups or 8 x 6: 64 or 48 KB per CU in flight); L1 fragments
+    // (16 waves x 2 groups or 8 x 6: 32 or 48 KB per CU in flight); L1 fragments
     // run one group ahead
-    constexpr int CH = WAVES == 16 ? 4 : 6;
+    constexpr int CH = WAVES == 16 ? 2 : 6;
     v8bf la[RTX][2], lb[RTX][2];
     for (int c0 = 0; c0 < ((n + CH - 1) / CH) * CH || c0 == 0; c0 += CH) {
         uint4 xs[CH][2];
