@@ -42,8 +42,8 @@ PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 # traffic is reported as null.
 GEMM_TRAFFIC = {
     "source_sha256": "bf40777b0a807bfba2ab9ffcda60dbd0d1b831a18449a5a694cf92fdf741250e",
-    "fetch_kib": 66594.55, "write_kib": 74720.51,        # QKV GEMM, mean of 40 dispatches
-    "fetch_factor": 262144.0 / 131084.48,                 # 256 MiB copy: known bytes / FETCH_SIZE
+    "fetch_kib": 66638.78, "write_kib": 74732.45,        # QKV GEMM, mean of 40 dispatches
+    "fetch_factor": 262144.0 / 131084.49,                 # 256 MiB copy: known bytes / FETCH_SIZE
     "write_factor": 262144.0 / 262144.0,                  # 256 MiB copy: known bytes / WRITE_SIZE
 }
 
