@@ -79,7 +79,9 @@ DEV uint32_t e2m1_x8(const float* t) {
     return w & (0x77777777u | nonzero);
 }
 
-template <int RT, int FMT>   // RT = rank / 16 (0..8); FMT 0: INT4 g64, 1: MXFP4
+// RT = rank / 16 (0..8); FMT 0: INT4 g64, 1: MXFP4; CHT: groups each wave
+// keeps in flight (0: the default for the wave count)
+template <int RT, int FMT, int CHT>
 __global__ __launch_bounds__(waves_for(RT) * 64) void act_quant_kernel(
     const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t ldx,
     const float* __restrict__ inv_lambda, const uint16_t* __restrict__ l1t,
@@ -102,7 +104,7 @@ __global__ __launch_bounds__(waves_for(RT) * 64) void act_quant_kernel(
     const bool valid = row < M;
     // rows past the end read the last row; nothing of theirs is stored
     const uint16_t* xrow = x + (valid ? row : M - 1) * ldx;
-    // this wave's groups are wave, wave + 8, ...; indices past the end are
+    // this wave's groups are wave, wave + WAVES, ...; indices past the end are
     // clamped to a real group so prefetches stay in bounds
     const int n = (G > wave) ? (G - wave + WAVES - 1) / WAVES : 0;
     auto gidx = [&](int i) { const int gi = wave + WAVES * i; return gi < G ? gi : G - 1; };
@@ -199,9 +201,10 @@ __global__ __launch_bounds__(waves_for(RT) * 64) void act_quant_kernel(
     };
 
     // the X loads of up to CH groups are all issued before any is processed
-    // (16 waves x 2 groups or 8 x 6: 32 or 48 KB per CU in flight); L1 fragments
-    // run one group ahead
-    constexpr int CH = WAVES == 16 ? 2 : 6;
+    // (by default 16 waves x 2 groups or 8 x 6: 32 or 48 KB per CU in flight);
+    // L1 fragments run one group ahead
+    constexpr int CH = CHT ? CHT : (WAVES == 16 ? 2 : 6);
+    static_assert(CH % 2 == 0, "groups are processed in pairs");
     v8bf la[RTX][2], lb[RTX][2];
     for (int c0 = 0; c0 < ((n + CH - 1) / CH) * CH || c0 == 0; c0 += CH) {
         uint4 xs[CH][2];
@@ -282,6 +285,18 @@ size_t act_quant_smem_bytes(int64_t K, int rank) {
 
 namespace {
 
+template <int RT, int FMT, int CHT>
+void launch_one(dim3 grid, size_t smem, hipStream_t stream, const uint16_t* x, int64_t M, int64_t K,
+                int64_t ldx, const float* inv_lambda, const uint16_t* l1t, uint8_t* qx, uint16_t* sx,
+                float* xl1)
+{
+    if (smem > 65536)
+        (void)hipFuncSetAttribute((const void*)act_quant_kernel<RT, FMT, CHT>,
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+    hipLaunchKernelGGL((act_quant_kernel<RT, FMT, CHT>), grid, dim3(waves_for(RT) * 64), smem, stream,
+                       x, M, K, ldx, inv_lambda, l1t, qx, sx, xl1);
+}
+
 template <int FMT>
 hipError_t launch_fmt(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
                       const float* inv_lambda, const uint16_t* l1t, int rank,
@@ -290,12 +305,16 @@ hipError_t launch_fmt(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
     const dim3 grid((unsigned)((M + ROWS - 1) / ROWS));
     const size_t smem = act_quant_smem_bytes(K, rank);
     switch (rank / 16) {
+    // the MXFP4 form with 16 waves and at least 8 groups per wave (K >= 8192)
+    // runs faster with four groups in flight; the INT4 form does not
 #define CASE(RTV) case RTV: \
-        if (smem > 65536) \
-            (void)hipFuncSetAttribute((const void*)act_quant_kernel<RTV, FMT>, \
-                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem); \
-        hipLaunchKernelGGL((act_quant_kernel<RTV, FMT>), grid, dim3(waves_for(RTV) * 64), smem, stream, \
-                           x, M, K, ldx, inv_lambda, l1t, qx, sx, xl1); break;
+        if constexpr (FMT == 1 && waves_for(RTV) == 16) { \
+            if (K >= 8192) { \
+                launch_one<RTV, FMT, 4>(grid, smem, stream, x, M, K, ldx, inv_lambda, l1t, qx, sx, xl1); \
+                break; \
+            } \
+        } \
+        launch_one<RTV, FMT, 0>(grid, smem, stream, x, M, K, ldx, inv_lambda, l1t, qx, sx, xl1); break;
         CASE(0) CASE(1) CASE(2) CASE(3) CASE(4) CASE(5) CASE(6) CASE(7) CASE(8)
 #undef CASE
         default: return hipErrorInvalidValue;
