@@ -38,7 +38,24 @@ _SIGS = {
     "svdq_quantize_act_mxfp4": [_P, _I64, _I64, _I64, _P, _P, _I32, _P, _P, _P, _P],
     "svdq_gemm_mxfp4": [_P, _P, _I64, _I64, _P, _P, _I64, _P, _P, _I32, _P, _I32, _P, _I32, _I64, _P],
     "awq_gemv_w4a16": [_P, _I64, _I64, _P, _P, _P, _P, _I64, _P, _P, _P],
+    "svdq_probe_clock": [_P, _I32, _P],
+    "svdq_probe_read": [_P, _I64, _P, _I32, _P],
 }
+
+
+FMT = {"int4": 0, "mxfp4": 1}
+
+
+class LayerDesc(ctypes.Structure):
+    """svdq_layer_desc: K, N, rank, group, fmt, act of one SVDQ layer."""
+    _fields_ = [("K", ctypes.c_int64), ("N", ctypes.c_int64), ("rank", ctypes.c_int32),
+                ("group", ctypes.c_int32), ("fmt", ctypes.c_int32), ("act", ctypes.c_int32)]
+
+
+class LayerSizes(ctypes.Structure):
+    """svdq_layer_sizes: byte sizes of a layer's arrays (see include/svdq.h)."""
+    _fields_ = [(n, ctypes.c_int64) for n in
+                ("qw", "sw", "l1t", "l2t", "inv_lambda", "bias", "qx_row", "sx_row", "xl1_row")]
 
 
 def load_library():
@@ -60,6 +77,10 @@ def load_library():
         lib.svdq_last_error.restype = ctypes.c_char_p
         lib.svdq_version.argtypes = []
         lib.svdq_version.restype = ctypes.c_int
+        lib.svdq_validate_desc.argtypes = [ctypes.POINTER(LayerDesc)]
+        lib.svdq_validate_desc.restype = ctypes.c_int
+        lib.svdq_layer_sizes_of.argtypes = [ctypes.POINTER(LayerDesc), ctypes.POINTER(LayerSizes)]
+        lib.svdq_layer_sizes_of.restype = ctypes.c_int
         _LIB = lib
     return _LIB
 
@@ -136,6 +157,39 @@ def awq_gemv_w4a16(x, M, K, inv_s, qw, scale, zero, N, bias, y, stream=None):
            "awq_gemv_w4a16")
 
 
+def layer_desc(K: int, N: int, rank: int, group: int = 64, fmt: str = "int4",
+               act: str = "none") -> LayerDesc:
+    """A layer description (fmt "int4" or "mxfp4", act "none" or "gelu_tanh")."""
+    return LayerDesc(K, N, rank, group, FMT[fmt] if isinstance(fmt, str) else fmt,
+                     ACT[act] if isinstance(act, str) else act)
+
+
+def svdq_validate_desc(desc) -> int:
+    """Status of svdq_validate_desc (desc None -> the NULL check)."""
+    return load_library().svdq_validate_desc(None if desc is None else ctypes.byref(desc))
+
+
+def validate_desc(desc):
+    _check(svdq_validate_desc(desc), "svdq_validate_desc")
+
+
+def layer_sizes(desc) -> dict:
+    """Validate desc and return the byte sizes of its arrays."""
+    out = LayerSizes()
+    _check(load_library().svdq_layer_sizes_of(ctypes.byref(desc), ctypes.byref(out)),
+           "svdq_layer_sizes_of")
+    return {n: getattr(out, n) for n, _ in LayerSizes._fields_}
+
+
+def svdq_probe_clock(ticks, spins, stream=None):
+    _check(load_library().svdq_probe_clock(_ptr(ticks), spins, _stream(stream)), "svdq_probe_clock")
+
+
+def svdq_probe_read(buf, nbytes, sink, blocks, stream=None):
+    _check(load_library().svdq_probe_read(_ptr(buf), nbytes, _ptr(sink), blocks, _stream(stream)),
+           "svdq_probe_read")
+
+
 # ---------------------------------------------------------------- tensor helpers
 # (allocate outputs with torch, then call the entry points above)
 
@@ -152,11 +206,74 @@ def pack_l1(l1: torch.Tensor) -> torch.Tensor:
     return v.permute(0, 4, 2, 1, 5, 3).contiguous().reshape(-1)
 
 
+def _require(cond: bool, msg: str):
+    if not cond:
+        raise ValueError(msg)
+
+
+def _check_rows(x: torch.Tensor, name: str, dtype):
+    """A [rows, cols] tensor of `dtype` whose rows may be strided but whose
+    columns are contiguous (the ABI takes a leading dimension, not a column
+    stride)."""
+    _require(x.dim() == 2, f"{name} must be 2-D, got shape {tuple(x.shape)}")
+    _require(x.dtype == dtype, f"{name} must be {dtype}, got {x.dtype}")
+    _require(x.stride(1) == 1 or x.shape[1] <= 1, f"{name} must have contiguous columns (stride(1) == 1)")
+
+
+def _check_same_device(ref: torch.Tensor, **ts):
+    _require(ref.is_cuda, f"tensors must be on a GPU device, got {ref.device}")
+    for n, t in ts.items():
+        if t is not None:
+            _require(t.device == ref.device, f"{n} is on {t.device}, expected {ref.device}")
+
+
+def _check_act_inputs(x, inv_lambda, l1t, rank):
+    _check_rows(x, "x", torch.bfloat16)
+    M, K = x.shape
+    if inv_lambda is not None:
+        _require(inv_lambda.dtype == torch.float32 and inv_lambda.numel() == K and inv_lambda.is_contiguous(),
+                 f"inv_lambda must be a contiguous fp32 vector of K = {K} values")
+    if rank:
+        _require(l1t is not None and l1t.dtype == torch.bfloat16 and l1t.numel() == K * rank
+                 and l1t.is_contiguous(), f"l1t must be {K} x {rank} bf16 values in the tile layout (pack_l1)")
+    _check_same_device(x, inv_lambda=inv_lambda, l1t=l1t if rank else None)
+    return M, K
+
+
+def _check_gemm_inputs(qx, sx, xl1, qw, sw, l2t, bias, rank, y, sx_last, sx_dtype):
+    _check_rows(qx, "qx", torch.uint8)
+    _require(qx.is_contiguous(), "qx must be contiguous [M, K/2]")
+    M, K = qx.shape[0], qx.shape[1] * 2
+    _require(qw.dim() == 2 and qw.dtype == torch.uint8 and qw.is_contiguous() and qw.shape[1] * 2 == K,
+             f"qw must be contiguous uint8 [N, K/2] with K = {K}, got {tuple(qw.shape)}")
+    N = qw.shape[0]
+    G4 = (K // 64 + 3) // 4
+    _require(tuple(sx.shape) == (G4, M, sx_last) and sx.dtype == sx_dtype and sx.is_contiguous(),
+             f"sx must be contiguous {sx_dtype} [{G4}, {M}, {sx_last}], got {tuple(sx.shape)} {sx.dtype}")
+    _require(tuple(sw.shape) == (G4, N, sx_last) and sw.dtype == sx_dtype and sw.is_contiguous(),
+             f"sw must be contiguous {sx_dtype} [{G4}, {N}, {sx_last}], got {tuple(sw.shape)} {sw.dtype}")
+    if rank:
+        _require(xl1 is not None and tuple(xl1.shape) == (M, rank) and xl1.dtype == torch.float32
+                 and xl1.is_contiguous(), f"xl1 must be contiguous fp32 [{M}, {rank}]")
+        _require(l2t is not None and tuple(l2t.shape) == (N, rank) and l2t.dtype == torch.bfloat16
+                 and l2t.is_contiguous(), f"l2t must be contiguous bf16 [{N}, {rank}]")
+    if bias is not None:
+        _require(bias.numel() == N and bias.dtype == torch.bfloat16 and bias.is_contiguous(),
+                 f"bias must be a contiguous bf16 vector of N = {N} values")
+    if y is not None:
+        _require(y.dtype in (torch.bfloat16, torch.float32), f"y must be bf16 or fp32, got {y.dtype}")
+        _check_rows(y, "y", y.dtype)
+        _require(tuple(y.shape) == (M, N), f"y must be [{M}, {N}], got {tuple(y.shape)}")
+    _check_same_device(qx, sx=sx, qw=qw, sw=sw, xl1=xl1 if rank else None, l2t=l2t if rank else None,
+                       bias=bias, y=y)
+    return M, K, N
+
+
 def quantize_act(x: torch.Tensor, inv_lambda, l1t, rank: int, stream=None):
     """x: bf16 [M, K] on the GPU; l1t: L1 in the tile layout (pack_l1) ->
     (qx uint8 [M, K/2], sx fp16 [ceil(K/256), M, 4] (quad-major group scales),
     xl1 fp32 [M, r])."""
-    M, K = x.shape
+    M, K = _check_act_inputs(x, inv_lambda, l1t, rank)
     dev = x.device
     qx = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
     sx = torch.empty(((K // 64 + 3) // 4, M, 4), dtype=torch.float16, device=dev)
@@ -169,9 +286,7 @@ def quantize_act(x: torch.Tensor, inv_lambda, l1t, rank: int, stream=None):
 def w4a4_linear(qx, sx, xl1, qw, sw, l2t, bias, rank: int, act: str = "none",
                 out_dtype=torch.bfloat16, y=None, stream=None):
     """Y = xl1 L2 + sum_g sx sw P_g + bias (-> GELU) for already quantised activations."""
-    M = qx.shape[0]
-    K = qx.shape[1] * 2
-    N = qw.shape[0]
+    M, K, N = _check_gemm_inputs(qx, sx, xl1, qw, sw, l2t, bias, rank, y, 4, torch.float16)
     if y is None:
         y = torch.empty((M, N), dtype=out_dtype, device=qx.device)
     y_dt = 1 if y.dtype == torch.float32 else 0
@@ -184,9 +299,26 @@ def awq_gemv(x, inv_s, qwt, scale_t, zero_t, bias, N=None, y=None, stream=None):
     """x bf16 [M, K]; qwt, scale_t, zero_t: codes, fp16 scales and zero points
     in the GEMV tile layout (any shape: N * K / 2 bytes, N * K / 64 values)
     -> y bf16 [M, N]."""
+    _check_rows(x, "x", torch.bfloat16)
+    _require(x.is_contiguous(), "x must be contiguous [M, K] (the GEMV reads dense rows)")
     M, K = x.shape
     if N is None:
         N = scale_t.numel() // (K // 64)
+    _require(qwt.dtype == torch.uint8 and qwt.numel() * 2 == N * K and qwt.is_contiguous(),
+             f"qwt must hold N * K / 2 = {N * K // 2} contiguous bytes")
+    for n, t in (("scale_t", scale_t), ("zero_t", zero_t)):
+        _require(t.dtype == torch.float16 and t.numel() * 64 == N * K and t.is_contiguous(),
+                 f"{n} must hold N * K / 64 = {N * K // 64} contiguous fp16 values")
+    if inv_s is not None:
+        _require(inv_s.dtype == torch.float32 and inv_s.numel() == K and inv_s.is_contiguous(),
+                 f"inv_s must be a contiguous fp32 vector of K = {K} values")
+    if bias is not None:
+        _require(bias.dtype == torch.bfloat16 and bias.numel() == N and bias.is_contiguous(),
+                 f"bias must be a contiguous bf16 vector of N = {N} values")
+    if y is not None:
+        _require(y.dtype == torch.bfloat16 and tuple(y.shape) == (M, N) and y.is_contiguous(),
+                 f"y must be contiguous bf16 [{M}, {N}]")
+    _check_same_device(x, inv_s=inv_s, qwt=qwt, scale_t=scale_t, zero_t=zero_t, bias=bias, y=y)
     if y is None:
         y = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
     awq_gemv_w4a16(x, M, K, inv_s, qwt, scale_t, zero_t, N, bias, y, stream)
@@ -196,7 +328,7 @@ def awq_gemv(x, inv_s, qwt, scale_t, zero_t, bias, N=None, y=None, stream=None):
 def quantize_act_mxfp4(x: torch.Tensor, inv_lambda, l1t, rank: int, stream=None):
     """x: bf16 [M, K] on the GPU -> (qx uint8 [M, K/2] E2M1 nibbles, sx uint8
     [ceil(K/256), M, 8] E8M0 block exponents, xl1 fp32 [M, r])."""
-    M, K = x.shape
+    M, K = _check_act_inputs(x, inv_lambda, l1t, rank)
     dev = x.device
     qx = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
     sx = torch.empty(((K // 64 + 3) // 4, M, 8), dtype=torch.uint8, device=dev)
@@ -209,9 +341,7 @@ def quantize_act_mxfp4(x: torch.Tensor, inv_lambda, l1t, rank: int, stream=None)
 def mxfp4_linear(qx, sx, xl1, qw, sw, l2t, bias, rank: int, act: str = "none",
                  out_dtype=torch.bfloat16, y=None, stream=None):
     """Y = xl1 L2 + deq(qx) deq(qw)^T + bias (-> GELU), MXFP4 operands."""
-    M = qx.shape[0]
-    K = qx.shape[1] * 2
-    N = qw.shape[0]
+    M, K, N = _check_gemm_inputs(qx, sx, xl1, qw, sw, l2t, bias, rank, y, 8, torch.uint8)
     if y is None:
         y = torch.empty((M, N), dtype=out_dtype, device=qx.device)
     y_dt = 1 if y.dtype == torch.float32 else 0

@@ -33,6 +33,9 @@ hipError_t launch_gemv_w4a16(const uint16_t* x, int M, int64_t K, const float* i
                              const uint8_t* qwt, const uint16_t* scale, const uint16_t* zero,
                              int64_t N, const uint16_t* bias, uint16_t* y, int cus, hipStream_t stream);
 size_t gemv_smem_bytes(int M, int64_t K);
+hipError_t launch_clock_probe(long long* out, int spins, hipStream_t stream);
+hipError_t launch_read_probe(const uint8_t* buf, int64_t bytes, uint32_t* sink, int blocks,
+                             hipStream_t stream);
 
 namespace {
 
@@ -114,6 +117,18 @@ svdq_status check_rank(int32_t rank) {
     return SVDQ_OK;
 }
 
+svdq_status check_n(int64_t N) {
+    if (N <= 0 || N % 8) return fail(SVDQ_ERR_SHAPE, "N = %lld must be a positive multiple of 8", (long long)N);
+    if (N > ((int64_t)1 << 31)) return fail(SVDQ_ERR_SHAPE, "N = %lld too large", (long long)N);
+    return SVDQ_OK;
+}
+
+svdq_status check_act(int32_t act) {
+    if (act != SVDQ_ACT_NONE && act != SVDQ_ACT_GELU_TANH)
+        return fail(SVDQ_ERR_UNSUPPORTED, "activation %d is not supported", act);
+    return SVDQ_OK;
+}
+
 svdq_status check_k(int64_t K) {
     if (K <= 0 || K % 64 != 0) return fail(SVDQ_ERR_SHAPE, "K = %lld must be a positive multiple of 64", (long long)K);
     if (K > (int64_t)1 << 30) return fail(SVDQ_ERR_SHAPE, "K = %lld too large", (long long)K);
@@ -168,8 +183,8 @@ svdq_status gemm_impl(int mxfp4, const uint8_t* qx, const void* sx_f16, int64_t 
     if (M < 0) return fail(SVDQ_ERR_SHAPE, "M = %lld is negative", (long long)M);
     if ((s = check_k(K)) != SVDQ_OK) return s;
     if ((s = check_rank(rank)) != SVDQ_OK) return s;
-    if (N <= 0 || N % 8) return fail(SVDQ_ERR_SHAPE, "N = %lld must be a positive multiple of 8", (long long)N);
-    if (M > ((int64_t)1 << 31) || N > ((int64_t)1 << 31)) return fail(SVDQ_ERR_SHAPE, "M or N too large");
+    if ((s = check_n(N)) != SVDQ_OK) return s;
+    if (M > ((int64_t)1 << 31)) return fail(SVDQ_ERR_SHAPE, "M = %lld too large", (long long)M);
     if ((s = check_gemm_bytes(M, N, K)) != SVDQ_OK) return s;
     if ((M + 256) * rank * 4 >= ((int64_t)1 << 31) || (N + 256) * rank * 2 >= ((int64_t)1 << 31))
         return fail(SVDQ_ERR_SHAPE, "(M + 256) * rank * 4 and (N + 256) * rank * 2 must stay below 2^31 bytes");
@@ -177,8 +192,7 @@ svdq_status gemm_impl(int mxfp4, const uint8_t* qx, const void* sx_f16, int64_t 
     if (ldy % 8) return fail(SVDQ_ERR_ALIGN, "ldy = %lld must be a multiple of 8", (long long)ldy);
     if ((M + 128) * ldy * (y_dtype == SVDQ_DT_F32 ? 4 : 2) >= ((int64_t)1 << 31))
         return fail(SVDQ_ERR_SHAPE, "(M + 128) * ldy * element size must stay below 2^31 bytes");
-    if (act != SVDQ_ACT_NONE && act != SVDQ_ACT_GELU_TANH)
-        return fail(SVDQ_ERR_UNSUPPORTED, "activation %d is not supported", act);
+    if ((s = check_act(act)) != SVDQ_OK) return s;
     if (y_dtype != SVDQ_DT_BF16 && y_dtype != SVDQ_DT_F32)
         return fail(SVDQ_ERR_UNSUPPORTED, "output dtype %d is not supported", y_dtype);
     if (M == 0) { g_last_error.clear(); return SVDQ_OK; }   // empty batch
@@ -202,9 +216,43 @@ svdq_status gemm_impl(int mxfp4, const uint8_t* qx, const void* sx_f16, int64_t 
                     "svdq_gemm_w4a4 launch");
 }
 
+svdq_status validate_desc(const svdq_layer_desc* d) {
+    svdq_status s;
+    if (!d) return fail(SVDQ_ERR_NULL, "layer description is NULL");
+    if ((s = check_k(d->K)) != SVDQ_OK) return s;
+    if ((s = check_n(d->N)) != SVDQ_OK) return s;
+    if ((s = check_rank(d->rank)) != SVDQ_OK) return s;
+    if (d->group != 64) return fail(SVDQ_ERR_UNSUPPORTED, "group size %d is not supported (only 64)", d->group);
+    if (d->fmt != SVDQ_FMT_INT4 && d->fmt != SVDQ_FMT_MXFP4)
+        return fail(SVDQ_ERR_UNSUPPORTED, "format %d is not supported (0 = INT4, 1 = MXFP4)", d->fmt);
+    if ((s = check_act(d->act)) != SVDQ_OK) return s;
+    if ((s = check_gemm_bytes(0, d->N, d->K)) != SVDQ_OK) return s;
+    g_last_error.clear();
+    return SVDQ_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+svdq_status svdq_validate_desc(const svdq_layer_desc* desc) { return validate_desc(desc); }
+
+svdq_status svdq_layer_sizes_of(const svdq_layer_desc* d, svdq_layer_sizes* out) {
+    svdq_status s;
+    if ((s = validate_desc(d)) != SVDQ_OK) return s;
+    if (!out) return fail(SVDQ_ERR_NULL, "sizes is NULL");
+    const int64_t G4 = (d->K / 64 + 3) / 4;
+    out->qw = d->N * (d->K / 2);
+    out->sw = G4 * d->N * 8;              // 4 fp16 or 8 E8M0 bytes per (quad, row)
+    out->l1t = d->K * d->rank * 2;
+    out->l2t = d->N * d->rank * 2;
+    out->inv_lambda = d->K * 4;
+    out->bias = d->N * 2;
+    out->qx_row = d->K / 2;
+    out->sx_row = G4 * 8;
+    out->xl1_row = (int64_t)d->rank * 4;
+    return SVDQ_OK;
+}
 
 const char* svdq_status_string(svdq_status s) {
     switch (s) {
@@ -302,6 +350,27 @@ svdq_status awq_gemv_w4a16(const void* x, int64_t M, int64_t K, const float* inv
                                       (const uint16_t*)scale_f16, (const uint16_t*)zero_f16, N,
                                       (const uint16_t*)bias, (uint16_t*)y, cus, (hipStream_t)stream),
                     "awq_gemv_w4a16 launch");
+}
+
+svdq_status svdq_probe_clock(int64_t* ticks, int32_t spins, void* stream) {
+    svdq_status s;
+    if (spins < 1 || spins > 10000000) return fail(SVDQ_ERR_SHAPE, "spins = %d must be in [1, 1e7]", spins);
+    if (!ticks) return fail(SVDQ_ERR_NULL, "ticks is required");
+    if (!aligned(ticks, 8)) return fail(SVDQ_ERR_ALIGN, "ticks needs 8-byte alignment");
+    if ((s = check_current_device()) != SVDQ_OK) return s;
+    return launched(launch_clock_probe((long long*)ticks, spins, (hipStream_t)stream), "svdq_probe_clock launch");
+}
+
+svdq_status svdq_probe_read(const void* buf, int64_t bytes, uint32_t* sink, int32_t blocks, void* stream) {
+    svdq_status s;
+    if (bytes <= 0 || bytes % 16 || bytes >= ((int64_t)1 << 31))
+        return fail(SVDQ_ERR_SHAPE, "bytes = %lld must be a positive multiple of 16 below 2^31", (long long)bytes);
+    if (blocks < 1 || blocks > 65536) return fail(SVDQ_ERR_SHAPE, "blocks = %d must be in [1, 65536]", blocks);
+    if (!buf || !sink) return fail(SVDQ_ERR_NULL, "buf and sink are required");
+    if (!aligned(buf, 16) || !aligned(sink, 4)) return fail(SVDQ_ERR_ALIGN, "buf needs 16-byte alignment");
+    if ((s = check_current_device()) != SVDQ_OK) return s;
+    return launched(launch_read_probe((const uint8_t*)buf, bytes, sink, blocks, (hipStream_t)stream),
+                    "svdq_probe_read launch");
 }
 
 }  // extern "C"

@@ -100,9 +100,16 @@ DEV void unfold_fp6(uint32_t x0, uint32_t x1, uint32_t& d0, uint32_t& d1, uint32
     d2 = x1 & ~0x61861861u;
 }
 
+// GELU, tanh form: 0.5 y (1 + tanh(u)), u = sqrt(2/pi) (y + 0.044715 y^3).
+// Since 0.5 (1 + tanh(u)) = 1 / (1 + e^(-2u)), this is y / (1 + 2^t) with
+// t = -2 u log2(e) = y (c1 + c2 y^2), c1 = -2 sqrt(2/pi) log2(e) and
+// c2 = 0.044715 c1 (fp32 roundings of those products): one v_exp_f32 (2^t)
+// and one v_rcp_f32. Large negative y: 2^t overflows to inf and the result is
+// -0; large positive y: 2^t -> 0 and the result is y. The error is a few fp32
+// ulps of the result, plus about an ulp of |y| far in the negative tail,
+// where the function itself is below 1e-28 (the 1 + tanh form cancels there).
 DEV float gelu_tanh_f32(float y) {
-    const float k0 = 0.7978845608028654f;   // sqrt(2/pi)
-    const float k1 = 0.044715f;
-    float u = k0 * (y + k1 * y * y * y);
-    return 0.5f * y * (1.0f + tanhf(u));
+    const float c1 = -2.302208185195923f, c2 = -0.10294324159622192f;
+    const float t = y * __builtin_fmaf(c2, y * y, c1);
+    return y * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(t));
 }

@@ -80,6 +80,60 @@ typedef enum {
 
 typedef enum { SVDQ_DT_BF16 = 0, SVDQ_DT_F32 = 1 } svdq_dtype;
 typedef enum { SVDQ_ACT_NONE = 0, SVDQ_ACT_GELU_TANH = 1 } svdq_act;
+typedef enum { SVDQ_FMT_INT4 = 0, SVDQ_FMT_MXFP4 = 1 } svdq_fmt;
+
+/*
+ * svdq_layer_desc -- the per-module quantisation settings of one SVDQ layer.
+ * The remio.ai page (section on how Diffusers support changes the loading
+ * path) describes a quantization config that names, per module, the scheme,
+ * the precision, the group size and the low-rank correction; its section on
+ * what to watch after the Lite release asks for clear errors on malformed
+ * configurations. This struct is that record for one layer:
+ *
+ *  K, N    input and output widths (K % 64 == 0, N % 8 == 0, both >= 1)
+ *  rank    low-rank correction rank r (0..128, multiple of 16; 0 = none)
+ *  group   quantisation group along K: must be 64 (the only group size built)
+ *  fmt     SVDQ_FMT_INT4 (symmetric INT4, fp16 scale per 64) or
+ *          SVDQ_FMT_MXFP4 (E2M1, E8M0 exponent per 32)
+ *  act     SVDQ_ACT_NONE or SVDQ_ACT_GELU_TANH (the output epilogue)
+ *
+ * The caller owns the struct; the library reads it during the call only.
+ */
+typedef struct {
+    int64_t K, N;
+    int32_t rank;
+    int32_t group;
+    int32_t fmt;
+    int32_t act;
+} svdq_layer_desc;
+
+/*
+ * Byte sizes of the weight-side arrays of a layer (what a loader must hand
+ * to svdq_gemm_w4a4 / svdq_gemm_mxfp4 and svdq_quantize_act*):
+ *  qw      packed codes [N][K/2]
+ *  sw      scales: INT4 fp16 [ceil(K/256)][N][4]; MXFP4 E8M0 [ceil(K/256)][N][8]
+ *  l1t     down-projection in the L1 tile layout, K * rank bf16 (0 if rank 0)
+ *  l2t     up-projection [N][rank] bf16 (0 if rank 0)
+ *  inv_lambda  smoothing reciprocals fp32 [K]
+ *  bias    bf16 [N]
+ * and, for an activation batch of M rows, per row:
+ *  qx_row  K/2 bytes; sx_row  ceil(K/256) * 8 bytes; xl1_row  rank * 4 bytes.
+ */
+typedef struct {
+    int64_t qw, sw, l1t, l2t, inv_lambda, bias;
+    int64_t qx_row, sx_row, xl1_row;
+} svdq_layer_sizes;
+
+/* Check a layer description: NULL -> SVDQ_ERR_NULL; K, N, rank out of the
+ * rules above -> SVDQ_ERR_SHAPE; group != 64, unknown fmt or act ->
+ * SVDQ_ERR_UNSUPPORTED. The detail names the offending field
+ * (svdq_last_error). Touches no device. The compute entry points apply the
+ * same rules to their own K, N, rank and act arguments. */
+svdq_status svdq_validate_desc(const svdq_layer_desc* desc);
+
+/* Validate `desc`, then fill `sizes` (caller-owned) with the array sizes
+ * above. Touches no device. */
+svdq_status svdq_layer_sizes_of(const svdq_layer_desc* desc, svdq_layer_sizes* sizes);
 
 /* Capability check done up front (the remio.ai page, hardware section: the
  * loader verifies GPU capability at start-up and unsupported combinations
@@ -235,6 +289,24 @@ svdq_status svdq_gemm_w4a4_partials(const uint8_t* qx, int64_t M, int64_t K,
 svdq_status awq_gemv_w4a16(const void* x, int64_t M, int64_t K, const float* inv_s,
                            const uint8_t* qwt, const void* scale_f16, const void* zero_f16,
                            int64_t N, const void* bias, void* y, void* stream);
+
+/*
+ * Measurement helpers. They take no part in the layer's arithmetic; a
+ * benchmark uses them to state the conditions its figures were taken under
+ * (the hysygc.com page, section on speed and image comparisons, asks that
+ * a latency figure say what it includes and how it was taken).
+ *
+ * svdq_probe_clock: one lane spins `spins` short no-op groups (1..1e7) and
+ *   writes two int64 values to the device buffer `ticks`: shader-clock ticks
+ *   and ticks of the constant 100 MHz real-time counter over the same span,
+ *   so clock_MHz = 100 * ticks[0] / ticks[1].
+ * svdq_probe_read: reads every byte of the device buffer `buf` once (bytes a
+ *   positive multiple of 16 below 2^31, `buf` 16-byte aligned) with
+ *   `blocks` (1..65536) workgroups of 256 lanes, and stores one XOR word per
+ *   workgroup into `sink` [blocks]: the time of a pure read of that size.
+ */
+svdq_status svdq_probe_clock(int64_t* ticks, int32_t spins, void* stream);
+svdq_status svdq_probe_read(const void* buf, int64_t bytes, uint32_t* sink, int32_t blocks, void* stream);
 
 #ifdef __cplusplus
 }

@@ -133,3 +133,28 @@ def assert_bf16_is_rounded_fp32(ybf_bits: np.ndarray, y32: np.ndarray):
     from oracle import numfmt
     exp = numfmt.f32_to_bf16_bits(np.asarray(y32, np.float32))
     assert np.array_equal(np.asarray(ybf_bits, np.uint16), exp)
+
+
+def assert_fp32_gelu(y32, pre64, pre_bound):
+    """fp32 output of the GELU epilogue against GELU(fp64 pre-activation):
+    the pre-activation error (at most pre_bound, the fp32 accumulation bound)
+    passes through GELU, whose slope never exceeds 1.13; evaluating GELU in
+    fp32 adds a small relative error (allowed: 2^-18 of the value) and, in the
+    far negative tail where GELU is below 1e-28 and its tanh form cancels,
+    about an ulp of the input (allowed: 2^-22 of |pre|)."""
+    from oracle import svdq as osv
+    y32 = np.asarray(y32, np.float64)
+    pre64 = np.asarray(pre64, np.float64)
+    g64 = osv.gelu_tanh(pre64)
+    bound = (1.13 * np.asarray(pre_bound, np.float64) + 2.0 ** -18 * np.abs(g64) + 2.0 ** -22 * np.abs(pre64)
+             + 1e-30)
+    bad = np.abs(y32 - g64) > bound
+    assert not bad.any(), (f"{bad.sum()} of {bad.size} GELU outputs outside the bound; "
+                           f"worst ratio {np.max(np.abs(y32 - g64) / bound):.3g}")
+    assert rel_fro(y32, g64) <= 1e-5
+
+
+def sample_rows(M: int, n_edge: int, n_rand: int, seed: int) -> np.ndarray:
+    """First and last n_edge rows plus n_rand seeded random rows, sorted."""
+    return np.unique(np.concatenate([np.arange(0, n_edge), np.arange(M - n_edge, M),
+                                     np.random.default_rng(seed).choice(M, n_rand, replace=False)]))

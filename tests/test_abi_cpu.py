@@ -152,3 +152,81 @@ def test_mxfp4_entry_points_validate_like_int4(lib, kw, status):
         q["K"], q["ldx"] = 96, 96
         assert lib.svdq_quantize_act_mxfp4(q["x"], q["M"], q["K"], q["ldx"], q["inv"], q["l1t"], q["rank"],
                                            q["qx"], q["sx"], q["xl1"], None) == SHAPE
+
+
+# ---------------------------------------------------------------- layer descriptions
+
+def _desc(**kw):
+    a = dict(K=3072, N=9216, rank=32, group=64, fmt="int4", act="none")
+    a.update(kw)
+    return svdq.layer_desc(**a)
+
+
+@pytest.mark.parametrize("kw", [{}, dict(fmt="mxfp4"), dict(rank=0), dict(rank=128), dict(act="gelu_tanh"),
+                                dict(K=64, N=8), dict(K=12288, N=3072)])
+def test_validate_desc_accepts(kw):
+    assert svdq.svdq_validate_desc(_desc(**kw)) == OK
+
+
+@pytest.mark.parametrize("kw,status,word", [
+    (dict(K=3000), SHAPE, "K"), (dict(K=0), SHAPE, "K"), (dict(K=-64), SHAPE, "K"),
+    (dict(N=9220), SHAPE, "N"), (dict(N=0), SHAPE, "N"),
+    (dict(rank=8), SHAPE, "rank"), (dict(rank=144), SHAPE, "rank"), (dict(rank=-16), SHAPE, "rank"),
+    (dict(group=128), UNSUP, "group"), (dict(group=32), UNSUP, "group"),
+    (dict(fmt=2), UNSUP, "format"), (dict(fmt=-1), UNSUP, "format"),
+    (dict(act=7), UNSUP, "activation"),
+])
+def test_validate_desc_rejects(lib, kw, status, word):
+    assert svdq.svdq_validate_desc(_desc(**kw)) == status
+    assert word in lib.svdq_last_error().decode()
+    with pytest.raises(svdq.SvdqError):
+        svdq.validate_desc(_desc(**kw))
+
+
+def test_validate_desc_null(lib):
+    assert svdq.svdq_validate_desc(None) == NULL
+    assert lib.svdq_layer_sizes_of(None, None) == NULL
+
+
+def test_layer_sizes():
+    s = svdq.layer_sizes(_desc())
+    assert s == dict(qw=9216 * 1536, sw=12 * 9216 * 8, l1t=3072 * 32 * 2, l2t=9216 * 32 * 2,
+                     inv_lambda=3072 * 4, bias=9216 * 2, qx_row=1536, sx_row=96, xl1_row=128)
+    # K = 192: three groups round up to one quad of scales
+    s = svdq.layer_sizes(_desc(K=192, N=16, rank=0, fmt="mxfp4"))
+    assert (s["sw"], s["sx_row"], s["l1t"], s["l2t"]) == (16 * 8, 8, 0, 0)
+    with pytest.raises(svdq.SvdqError):
+        svdq.layer_sizes(_desc(group=16))
+
+
+# ---------------------------------------------------------------- binding argument checks
+# (raised in Python before any C call, so they run without a GPU)
+
+def test_binding_rejects_bad_tensors():
+    import torch
+    x = torch.zeros((4, 256), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU"):          # host tensors never reach a kernel
+        svdq.quantize_act(x, None, None, 0)
+    with pytest.raises(ValueError, match="bfloat16"):
+        svdq.quantize_act(x.float(), None, None, 0)
+    with pytest.raises(ValueError, match="contiguous columns"):
+        svdq.quantize_act(torch.zeros((4, 512), dtype=torch.bfloat16)[:, ::2], None, None, 0)
+    with pytest.raises(ValueError, match="l1t"):
+        svdq.quantize_act(x, None, torch.zeros(10, dtype=torch.bfloat16), 16)
+    qx = torch.zeros((4, 128), dtype=torch.uint8)
+    sx = torch.zeros((1, 4, 4), dtype=torch.float16)
+    qw = torch.zeros((8, 128), dtype=torch.uint8)
+    sw = torch.zeros((1, 8, 4), dtype=torch.float16)
+    with pytest.raises(ValueError, match="qw"):            # K of the weights differs
+        svdq.w4a4_linear(qx, sx, None, torch.zeros((8, 64), dtype=torch.uint8), sw, None, None, 0)
+    with pytest.raises(ValueError, match="y must be bf16 or fp32"):
+        svdq.w4a4_linear(qx, sx, None, qw, sw, None, None, 0, y=torch.zeros((4, 8), dtype=torch.float16))
+    with pytest.raises(ValueError, match="sw"):
+        svdq.w4a4_linear(qx, sx, None, qw, sw[:, :4], None, None, 0)
+    with pytest.raises(ValueError, match="bias"):
+        svdq.w4a4_linear(qx, sx, None, qw, sw, None, torch.zeros(7, dtype=torch.bfloat16), 0)
+    with pytest.raises(ValueError, match="sx"):            # INT4 scales given to the MXFP4 GEMM
+        svdq.mxfp4_linear(qx, sx, None, qw, sw, None, None, 0)
+    with pytest.raises(ValueError, match="qwt"):
+        svdq.awq_gemv(x, None, torch.zeros(10, dtype=torch.uint8), torch.zeros(64, dtype=torch.float16),
+                      torch.zeros(64, dtype=torch.float16), None, N=16)

@@ -14,8 +14,8 @@ import torch
 
 import synth
 from oracle import mxfp4 as omx, numfmt, svdq as osv
-from gpu_util import (assert_bf16_is_rounded_fp32, dev, dev_u16, host_bf16_f64, host_u16, note,
-                      rel_fro)
+from gpu_util import (assert_bf16_is_rounded_fp32, assert_fp32_gelu, dev, dev_u16, host_bf16_f64,
+                      host_u16, note, rel_fro, sample_rows)
 
 pytestmark = pytest.mark.gpu
 
@@ -64,10 +64,14 @@ def magnitude(qa_codes, qa_exps, w_codes, w_exps, xl1, l2_bits, bias_bits):
     return t
 
 
-def assert_fp32(y32, y64, tmag, K, rank):
+def fp32_bound_mx(tmag, K, rank):
     # fp32 sums of K / 64 MFMA steps, the low-rank MFMAs, bias: a few ulps of
     # the magnitude per term that meets the accumulator
-    bound = 2.0 * (K // 64 + rank + 4) * 2.0 ** -24 * tmag
+    return 2.0 * (K // 64 + rank + 4) * 2.0 ** -24 * tmag
+
+
+def assert_fp32(y32, y64, tmag, K, rank):
+    bound = fp32_bound_mx(tmag, K, rank)
     assert np.all(np.abs(y32 - y64) <= bound + 1e-30), float(np.max(np.abs(y32 - y64) - bound))
     assert rel_fro(y32, y64) <= 1e-5
 
@@ -118,11 +122,12 @@ def test_mx_gemm_tiny(act, bias):
     torch.cuda.synchronize()
     y64 = omx.linear_output(qa.codes, qa.exps, w.qw_codes, w.qw_exps, qa.xl1, w.l2, bb, act)
     y32h = y32.cpu().numpy()
+    tmag = magnitude(qa.codes, qa.exps, w.qw_codes, w.qw_exps, qa.xl1, w.l2, bb)
     if act == "none":
-        tmag = magnitude(qa.codes, qa.exps, w.qw_codes, w.qw_exps, qa.xl1, w.l2, bb)
         assert_fp32(y32h, y64, tmag, cfg.K, cfg.rank)
     else:
-        assert rel_fro(y32h, y64) <= 1e-5
+        pre64 = omx.linear_output(qa.codes, qa.exps, w.qw_codes, w.qw_exps, qa.xl1, w.l2, bb, "none")
+        assert_fp32_gelu(y32h, pre64, fp32_bound_mx(tmag, cfg.K, cfg.rank))
     assert_bf16_is_rounded_fp32(host_u16(ybf), y32h)
     assert rel_fro(host_bf16_f64(ybf), y64) <= 2e-3
 
@@ -139,10 +144,13 @@ def test_mx_gemm_ragged_and_ranks():
         dw = DevMx(w)
         qx, sx, xl1 = lib.quantize_act_mxfp4(dev_u16(x), dw.inv_lambda, dw.l1t, r)
         y = lib.mxfp4_linear(qx, sx, xl1, dw.qw, dw.sw, dw.l2t, dw.bias, r, out_dtype=torch.float32)
+        ybf = lib.mxfp4_linear(qx, sx, xl1, dw.qw, dw.sw, dw.l2t, dw.bias, r)
         torch.cuda.synchronize()
         qa, y64 = omx.forward(w, x)
         check_act(qa, qx, sx, xl1, r)
-        assert rel_fro(y.cpu().numpy(), y64) <= 1e-5, (M, K, N, r)
+        tmag = magnitude(qa.codes, qa.exps, w.qw_codes, w.qw_exps, qa.xl1 if r else None, w.l2, w.bias)
+        assert_fp32(y.cpu().numpy(), y64, tmag, K, r)
+        assert_bf16_is_rounded_fp32(host_u16(ybf), y.cpu().numpy())
 
 
 def test_mx_qkv_full_size():
@@ -210,11 +218,50 @@ def test_mx_fc2_full_size():
     dw = DevMx(w)
     qx, sx, xl1 = lib.quantize_act_mxfp4(dev_u16(x), dw.inv_lambda, dw.l1t, c2.rank)
     y = lib.mxfp4_linear(qx, sx, xl1, dw.qw, dw.sw, dw.l2t, dw.bias, c2.rank)
+    yf = lib.mxfp4_linear(qx, sx, xl1, dw.qw, dw.sw, dw.l2t, dw.bias, c2.rank, out_dtype=torch.float32)
     torch.cuda.synchronize()
     qa = omx.quantize_act(x, w.inv_lambda, w.l1)
     check_act(qa, qx, sx, xl1, c2.rank)
-    rows = np.unique(np.concatenate([np.arange(0, 4), np.arange(c2.M - 4, c2.M),
-                                     np.random.default_rng(2).choice(c2.M, 24, replace=False)]))
+    rows = sample_rows(c2.M, 4, 24, 2)
     y64 = omx.linear_output(qa.codes[rows], qa.exps[rows], w.qw_codes, w.qw_exps, qa.xl1[rows],
                             w.l2, w.bias)
+    tmag = magnitude(qa.codes[rows], qa.exps[rows], w.qw_codes, w.qw_exps, qa.xl1[rows], w.l2, w.bias)
+    yfh = yf.cpu().numpy()
+    assert_fp32(yfh[rows], y64, tmag, c2.K, c2.rank)
+    assert_bf16_is_rounded_fp32(host_u16(y), yfh)
+    assert rel_fro(host_bf16_f64(y)[rows], y64) <= 2e-3
+
+
+@pytest.mark.parametrize("K,N,act", [(3072, 3072, "none"), (3072, 12288, "gelu_tanh")],
+                         ids=["out_proj", "fc1_gelu"])
+def test_mx_block_layers_full_size(K, N, act):
+    """The MXFP4 block's out-projection (3072 -> 3072) and fc1 with the GELU
+    epilogue (3072 -> 12288) at 4608 tokens, rank 32: every code and exponent
+    of the activation pass; fp32 outputs element-wise on sampled rows (GELU:
+    the pre-activation bound carried through GELU), bf16 = RTNE of fp32."""
+    M, R = 4608, 32
+    note(f"mxfp4 block layer K={K} N={N} act={act}")
+    cfg = synth.LayerConfig("blk", M=M, K=K, N=N, rank=R, n_outliers=31, outlier_factor=30.0,
+                            seed=K + N)
+    li = synth.make_layer(cfg)
+    w = omx.prepare_mx(li.x, li.w, li.bias, R)
+    dw = DevMx(w)
+    qx, sx, xl1 = lib.quantize_act_mxfp4(dev_u16(li.x), dw.inv_lambda, dw.l1t, R)
+    y = lib.mxfp4_linear(qx, sx, xl1, dw.qw, dw.sw, dw.l2t, dw.bias, R, act=act)
+    yf = lib.mxfp4_linear(qx, sx, xl1, dw.qw, dw.sw, dw.l2t, dw.bias, R, act=act, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    qa = omx.quantize_act(li.x, w.inv_lambda, w.l1)
+    check_act(qa, qx, sx, xl1, R)
+    rows = sample_rows(M, 4, 24, 3)
+    pre = omx.linear_output(qa.codes[rows], qa.exps[rows], w.qw_codes, w.qw_exps, qa.xl1[rows], w.l2, w.bias)
+    tmag = magnitude(qa.codes[rows], qa.exps[rows], w.qw_codes, w.qw_exps, qa.xl1[rows], w.l2, w.bias)
+    yfh = yf.cpu().numpy()
+    if act == "none":
+        assert_fp32(yfh[rows], pre, tmag, K, R)
+        y64 = pre
+    else:
+        assert_fp32_gelu(yfh[rows], pre, fp32_bound_mx(tmag, K, R))
+        y64 = omx.linear_output(qa.codes[rows], qa.exps[rows], w.qw_codes, w.qw_exps, qa.xl1[rows], w.l2,
+                                w.bias, act)
+    assert_bf16_is_rounded_fp32(host_u16(y), yfh)
     assert rel_fro(host_bf16_f64(y)[rows], y64) <= 2e-3

@@ -14,9 +14,9 @@ import torch
 
 import synth
 from oracle import numfmt, svdq as osv
-from gpu_util import (DevSvdq, assert_bf16_is_rounded_fp32, assert_bf16_output,
+from gpu_util import (DevSvdq, assert_bf16_is_rounded_fp32, assert_bf16_output, assert_fp32_gelu,
                       assert_fp32_output, dev, dev_f16, dev_scales, dev_u16, fp32_bound, host_bf16_f64,
-                      host_u16, magnitude_sum, note, rel_fro)
+                      host_u16, magnitude_sum, note, rel_fro, sample_rows)
 
 pytestmark = pytest.mark.gpu
 
@@ -149,10 +149,7 @@ def test_gemm_tiny(act, bias):
     tmag = magnitude_sum(qa.codes, qa.sx, w.qw_codes, w.sw, qa.xl1, w.l2, b)
     y32h = y32.cpu().numpy()
     if act == "gelu_tanh":
-        # GELU is 1-Lipschitz-ish (|gelu'| <= 1.13) plus fp32 tanh error
-        assert np.all(np.abs(y32h - y64) <= 1.13 * fp32_bound(tmag, cfg.K // 64 + cfg.rank)
-                      + 4e-7 * np.abs(y64) + 1e-7)
-        assert rel_fro(y32h, y64) <= 1e-5
+        assert_fp32_gelu(y32h, pre64, fp32_bound(tmag, cfg.K // 64 + cfg.rank))
     else:
         assert_fp32_output(y32h, y64, tmag, cfg.K // 64 + cfg.rank)
     assert_bf16_is_rounded_fp32(host_u16(ybf), y32h)
@@ -172,10 +169,13 @@ def test_gemm_ragged_rank0_and_rank128():
         dw = DevSvdq(w)
         qx, sx, xl1 = lib.quantize_act(dev_u16(x), dw.inv_lambda, dw.l1t, r)
         y = lib.w4a4_linear(qx, sx, xl1, dw.qw, dw.sw, dw.l2t, dw.bias, r, out_dtype=torch.float32)
+        ybf = lib.w4a4_linear(qx, sx, xl1, dw.qw, dw.sw, dw.l2t, dw.bias, r)
         torch.cuda.synchronize()
         qa, y64 = osv.forward(w, x)
         check_act(qa, qx, sx, xl1, r)
-        assert rel_fro(y.cpu().numpy(), y64) <= 1e-5, (M, K, N, r)
+        tmag = magnitude_sum(qa.codes, qa.sx, w.qw_codes, w.sw, qa.xl1 if r else None, w.l2, w.bias)
+        assert_fp32_output(y.cpu().numpy(), y64, tmag, K // 64 + r)
+        assert_bf16_is_rounded_fp32(host_u16(ybf), y.cpu().numpy())
 
 
 def test_gemm_empty_and_strided_output():
@@ -280,14 +280,20 @@ def test_mlp_pair_full_size():
     d1 = DevSvdq(w1)
     qx1, sx1, xl1_1 = run_act(li1.x, d1, c1.rank)
     h = lib.w4a4_linear(qx1, sx1, xl1_1, d1.qw, d1.sw, d1.l2t, d1.bias, c1.rank, act="gelu_tanh")
+    h32 = lib.w4a4_linear(qx1, sx1, xl1_1, d1.qw, d1.sw, d1.l2t, d1.bias, c1.rank, act="gelu_tanh",
+                          out_dtype=torch.float32)
     torch.cuda.synchronize()
     qa1 = osv.quantize_act(li1.x, w1.inv_lambda, w1.l1)
     check_act(qa1, qx1, sx1, xl1_1, c1.rank)
-    rows = np.unique(np.concatenate([np.arange(0, 4), np.arange(c1.M - 4, c1.M),
-                                     np.random.default_rng(1).choice(c1.M, 24, replace=False)]))
-    y64_1 = osv.gelu_tanh(osv.linear_output(qa1.codes[rows], qa1.sx[rows], w1.qw_codes, w1.sw,
-                                            qa1.xl1[rows], w1.l2, w1.bias))
+    rows = sample_rows(c1.M, 4, 24, 1)
+    pre1 = osv.linear_output(qa1.codes[rows], qa1.sx[rows], w1.qw_codes, w1.sw, qa1.xl1[rows], w1.l2, w1.bias)
+    y64_1 = osv.gelu_tanh(pre1)
+    tmag1 = magnitude_sum(qa1.codes[rows], qa1.sx[rows], w1.qw_codes, w1.sw, qa1.xl1[rows], w1.l2, w1.bias)
+    h32h = h32.cpu().numpy()
+    assert_fp32_gelu(h32h[rows], pre1, fp32_bound(tmag1, c1.K // 64 + c1.rank))
+    assert_bf16_is_rounded_fp32(host_u16(h), h32h)
     assert rel_fro(host_bf16_f64(h)[rows], y64_1) <= 2e-3
+    del h32, h32h
 
     note("mlp pair fc2 (K 12288)")
     h_bits = host_u16(h)
@@ -296,9 +302,14 @@ def test_mlp_pair_full_size():
     d2 = DevSvdq(w2)
     qx2, sx2, xl1_2 = lib.quantize_act(h, d2.inv_lambda, d2.l1t, c2.rank)
     y2 = lib.w4a4_linear(qx2, sx2, xl1_2, d2.qw, d2.sw, d2.l2t, d2.bias, c2.rank)
+    y2f = lib.w4a4_linear(qx2, sx2, xl1_2, d2.qw, d2.sw, d2.l2t, d2.bias, c2.rank, out_dtype=torch.float32)
     torch.cuda.synchronize()
     qa2 = osv.quantize_act(h_bits, w2.inv_lambda, w2.l1)
     check_act(qa2, qx2, sx2, xl1_2, c2.rank)
     y64_2 = osv.linear_output(qa2.codes[rows], qa2.sx[rows], w2.qw_codes, w2.sw, qa2.xl1[rows],
                               w2.l2, w2.bias)
+    tmag2 = magnitude_sum(qa2.codes[rows], qa2.sx[rows], w2.qw_codes, w2.sw, qa2.xl1[rows], w2.l2, w2.bias)
+    y2fh = y2f.cpu().numpy()
+    assert_fp32_output(y2fh[rows], y64_2, tmag2, c2.K // 64 + c2.rank)
+    assert_bf16_is_rounded_fp32(host_u16(y2), y2fh)
     assert rel_fro(host_bf16_f64(y2)[rows], y64_2) <= 2e-3

@@ -133,6 +133,48 @@ def test_smoothing_closed_form():
     assert np.allclose(lam0, [4.0, 9.0])
 
 
+def test_calib_absmax_hand_case():
+    """Per input channel k: ax over the tokens of X [M, K], aw over the
+    outputs of W [K, N]. Non-square shapes, and the largest-magnitude entry of
+    most channels is negative, so a dropped abs() or a reduction over the
+    wrong axis gives different numbers (or a different length)."""
+    x = np.array([[1.0, -5.0, 2.0, 0.0],
+                  [-3.0, 4.0, -7.0, 0.5],
+                  [2.0, 1.0, 6.0, -0.25]], np.float32)          # M = 3, K = 4
+    w = np.array([[-0.5, 0.25],
+                  [0.125, -0.375],
+                  [-0.25, 0.25],
+                  [0.0, -0.0]], np.float32)                      # K = 4, N = 2
+    ax, aw = svdq.calib_absmax(x, w)
+    assert ax.shape == (4,) and aw.shape == (4,)
+    assert ax.tolist() == [3.0, 5.0, 7.0, 0.5]
+    assert aw.tolist() == [0.5, 0.375, 0.25, 0.0]
+    assert ax.dtype == np.float32 and aw.dtype == np.float32
+
+
+def test_prepare_uses_channel_maxima():
+    """prepare_svdq's smoothing vector on a non-square layer (M 5, K 64,
+    N 16) whose channel maxima are planted with negative signs: inv_lambda[k]
+    = 1 / sqrt(ax[k] / aw[k]) by hand, and 1 where the weight row is zero."""
+    rng = np.random.default_rng(7)
+    M, K, N = 5, 64, 16
+    x = numfmt.bf16_bits_to_f32(numfmt.f32_to_bf16_bits(rng.uniform(-0.5, 0.5, (M, K)).astype(np.float32)))
+    w = numfmt.bf16_bits_to_f32(numfmt.f32_to_bf16_bits(rng.uniform(-0.005, 0.005, (K, N)).astype(np.float32)))
+    ax = np.ldexp(1.0, rng.integers(0, 4, K)).astype(np.float64)      # powers of two
+    aw = np.ldexp(1.0, -rng.integers(5, 8, K)).astype(np.float64)
+    for k in range(K):
+        x[(3 * k) % M, k] = -ax[k]
+        w[k, (5 * k) % N] = -aw[k]
+    w[9, :] = 0.0
+    xb = numfmt.f32_to_bf16_bits(x)
+    wb = numfmt.f32_to_bf16_bits(w)
+    assert np.array_equal(numfmt.bf16_bits_to_f32(xb), x) and np.array_equal(numfmt.bf16_bits_to_f32(wb), w)
+    p = svdq.prepare_svdq(xb, wb, None, 0)
+    lam = np.sqrt(ax / aw)
+    lam[9] = 1.0
+    assert np.array_equal(p.inv_lambda, (1.0 / lam).astype(np.float32))
+
+
 def test_smoothing_preserves_product():
     """X_hat W_hat = X W (the migration changes nothing before quantisation)."""
     li = synth.make_layer(synth.CONFIGS["tiny"], M=64)
