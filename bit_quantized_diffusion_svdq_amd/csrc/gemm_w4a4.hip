@@ -203,15 +203,33 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_w4a4_kernel(
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         lds_barrier();
     };
+    // The first wait of a tile: the previous tile's output stores (NST per
+    // wave) were issued after this tile's first loads, and vector memory
+    // operations retire in issue order, so waiting until NST remain waits for
+    // the loads and lets the stores drain in the background.
+    constexpr int NST = 8;
+    bool stores_in_flight = false;
+    auto publish_first = [&]() __attribute__((always_inline)) {
+        if constexpr (MODE == 0) {
+            if (stores_in_flight) {
+                asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+                stores_in_flight = false;
+                lds_barrier();
+                return;
+            }
+        }
+        publish();
+    };
 
-    // ---- low-rank branch: acc = xl1 L2 --------------------------------------
-    // 32 ranks at a time, through code slot 1 (free until quad 1 is loaded):
-    // the chunk's xl1 rows of the tile (128 B each, fp32) at 0 and its l2t
-    // rows (64 B each, bf16) at 16 KB, both brought by line-friendly loads
-    // into LDS with the chunks of a row XOR-swizzled (16-byte chunk c of tile
-    // row r at position c ^ ((r / 2) % 8) for xl1, c ^ ((r / 4) % 4) for l2t)
-    // so the MFMA lanes read them without bank conflicts. The first chunk
-    // flies together with quad 0. A last chunk of 16 ranks reads 16 more
+    // ---- low-rank branch: acc += xl1 L2 -------------------------------------
+    // Runs after the main loop, 32 ranks at a time, through code slot 0: the
+    // chunk's xl1 rows of the tile (128 B each, fp32) at 0 and its l2t rows
+    // (64 B each, bf16) at 16 KB, both brought by line-friendly loads into LDS
+    // with the chunks of a row XOR-swizzled (16-byte chunk c of tile row r at
+    // position c ^ ((r / 2) % 8) for xl1, c ^ ((r / 4) % 4) for l2t) so the
+    // MFMA lanes read them without bank conflicts. The first chunk takes the
+    // place of the quad past the end of K in the main loop's prefetch, so it
+    // has landed when the loop ends. A last chunk of 16 ranks reads 16 more
     // bytes per row that are never used (or 0 past the end of the array).
     const rsrc_t rxl = make_rsrc(xl1, (MODE != 2) ? M * rank * 4 : 0);
     const rsrc_t rl2 = make_rsrc(l2t, (MODE != 2) ? N * rank * 2 : 0);
@@ -219,15 +237,14 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_w4a4_kernel(
     auto load_lr = [&](int r0) __attribute__((always_inline)) {
 #pragma unroll
         for (int k = 0; k < 4; ++k)
-            dma16(rxl, cs1 + (wave + 4 * k) * 1024, vxl, k * 32 * rank * 4 + r0 * 4);
+            dma16(rxl, cs0 + (wave + 4 * k) * 1024, vxl, k * 32 * rank * 4 + r0 * 4);
 #pragma unroll
         for (int k = 0; k < 2; ++k)
-            dma16(rl2, cs1 + 16384 + (wave + 4 * k) * 1024, vl2, k * 64 * rank * 2 + r0 * 2);
+            dma16(rl2, cs0 + 16384 + (wave + 4 * k) * 1024, vl2, k * 64 * rank * 2 + r0 * 2);
     };
 
-    // Tile t: its origin and this lane's load offsets, then the loads that
-    // start it (quad 0 and the first low-rank chunk), which the previous
-    // tile's stores overlap.
+    // Tile t: its origin and this lane's load offsets, then the loads of its
+    // quad 0, which the previous tile's output work overlaps.
     auto start_tile = [&](int t) __attribute__((always_inline)) {
         int tm, tn;
         tile_coords(t, tiles_m, tiles_n, (int)gridDim.x, tm, tn);
@@ -249,15 +266,16 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_w4a4_kernel(
         vxl = (int)((m0 + 8 * wave + lr8) * rank * 4) + 16 * ((wave & 1) ? cpo : cpe);
         vl2 = (int)((n0 + 16 * wave + (lane >> 2)) * rank * 2) + 16 * ((lane & 3) ^ ((lane >> 4) & 3));
         load_quad(cs0, ss0, 0, 0, NDMA);
-        if (MODE != 2 && rank > 0) load_lr(0);
     };
 
     v16f acc[TM][TN];
     auto low_rank = [&]() __attribute__((always_inline)) {
         const int h = lane >> 5, r32l = lane & 31;
         for (int r0 = 0; r0 < rank; r0 += 32) {
-            if (r0 > 0) load_lr(r0);
-            publish();
+            if (r0 > 0 || FMT != 0) {
+                load_lr(r0);
+                publish();
+            }
             const int nks = (rank - r0) >= 32 ? 2 : 1;
             for (int ks = 0; ks < nks; ++ks) {
                 v8bf ah[TM], al[TM], b[TN];
@@ -265,8 +283,8 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_w4a4_kernel(
                 for (int i = 0; i < TM; ++i) {
                     const int tr = wm * 32 * TM + i * 32 + r32l;
                     const int sw8 = (tr >> 1) & 7, c0 = 4 * ks + 2 * h;
-                    const float4 u0 = *(const float4*)(cs1 + tr * 128 + 16 * (c0 ^ sw8));
-                    const float4 u1 = *(const float4*)(cs1 + tr * 128 + 16 * ((c0 + 1) ^ sw8));
+                    const float4 u0 = *(const float4*)(cs0 + tr * 128 + 16 * (c0 ^ sw8));
+                    const float4 u1 = *(const float4*)(cs0 + tr * 128 + 16 * ((c0 + 1) ^ sw8));
                     const float xv[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
 #pragma unroll
                     for (int jj = 0; jj < 8; ++jj) {
@@ -278,7 +296,7 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_w4a4_kernel(
 #pragma unroll
                 for (int j = 0; j < TN; ++j) {
                     const int tc = wn * 32 * TN + j * 32 + r32l;
-                    b[j] = *(const v8bf*)(cs1 + 16384 + tc * 64 + 16 * ((2 * ks + h) ^ ((tc >> 2) & 3)));
+                    b[j] = *(const v8bf*)(cs0 + 16384 + tc * 64 + 16 * ((2 * ks + h) ^ ((tc >> 2) & 3)));
                 }
 #pragma unroll
                 for (int i = 0; i < TM; ++i)
@@ -288,7 +306,7 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_w4a4_kernel(
                         acc[i][j] = mfma_bf16_32x32x16(al[i], b[j], acc[i][j]);
                     }
             }
-            lds_barrier();     // slot 1 is read by every wave before it is refilled
+            lds_barrier();     // slot 0 is read by every wave before it is refilled
         }
     };
 
@@ -359,7 +377,7 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_w4a4_kernel(
     // ngq of the quad in ncs; at the end of a quad, also the next quad's
     // scales from nss, into the other parity).
     auto group = [&](int g, int gq, int par, const char* ncs, const char* nss, int ngq,
-                     char* dcs, char* dss, int dq, int dlo, int dhi) __attribute__((always_inline)) {
+                     char* dcs, char* dss, int dq, int dlo, int dhi, bool lrl) __attribute__((always_inline)) {
 #pragma unroll
         for (int bl = 0; bl < TM * TN; ++bl) {
             const int i = bl / TN, j = bl % TN;
@@ -407,13 +425,18 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_w4a4_kernel(
                 // whose inputs are long complete, so one wave keeps the
                 // matrix pipe and the VALU busy at the same time
                 __builtin_amdgcn_sched_barrier(0);
+                // the two-address VOP2 form issues faster than the VOP3 form
+                // the compiler picks for an fma whose result overwrites its
+                // addend (measured on gfx950)
 #pragma unroll
-                for (int e = 0; e < 16; ++e) acc[pi][pj][e] = __builtin_fmaf(Pp[e], Sp[e], acc[pi][pj][e]);
-                order_point(acc[pi][pj]);
+                for (int e = 0; e < 16; ++e)
+                    asm volatile("v_fmac_f32_e32 %0, %1, %2" : "+v"(acc[pi][pj][e]) : "v"(Pp[e]), "v"(Sp[e]));
             }
             // this block's share of the loads being spread (the last block
-            // takes what is left)
-            if (dhi > dlo) {
+            // takes what is left); or the low-rank chunk in place of them
+            if (lrl) {
+                if (MODE != 2 && bl == 0 && rank > 0) load_lr(0);
+            } else if (dhi > dlo) {
                 if (bl < TM * TN - 1) load_quad(dcs, dss, dq, dlo + bl, dlo + bl + 1);
                 else load_quad(dcs, dss, dq, dlo + bl, dhi);
             }
@@ -439,13 +462,16 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_w4a4_kernel(
     // rounded up to an even number so the loop body has no branches (which
     // would blur the compiler's per-slot tracking of loads into LDS); the
     // extra groups have zero scales.
-    auto step = [&](int q, int par, char* cs, char* ss, char* ncs, char* nss) __attribute__((always_inline)) {
+    // tail 1 (the second-to-last step): the first low-rank chunk replaces
+    // the first half of the quad past the end; tail 2 (the last step): no
+    // loads at all.
+    auto step = [&](int q, int par, char* cs, char* ss, char* ncs, char* nss, int tail) __attribute__((always_inline)) {
         const int g0 = 4 * q;
-        group(g0, 0, par, cs, ss, 1, ncs, nss, q + 1, DSPLIT, NDMA);
-        group(g0 + 1, 1, par, cs, ss, 2, cs, ss, 0, 0, 0);
-        group(g0 + 2, 2, par, cs, ss, 3, cs, ss, 0, 0, 0);
+        group(g0, 0, par, cs, ss, 1, ncs, nss, q + 1, tail == 2 ? 0 : DSPLIT, tail == 2 ? 0 : NDMA, false);
+        group(g0 + 1, 1, par, cs, ss, 2, cs, ss, 0, 0, 0, false);
+        group(g0 + 2, 2, par, cs, ss, 3, cs, ss, 0, 0, 0, false);
         publish();
-        group(g0 + 3, 3, par, ncs, nss, 0, cs, ss, q + 2, 0, DSPLIT);
+        group(g0 + 3, 3, par, ncs, nss, 0, cs, ss, q + 2, 0, tail ? 0 : DSPLIT, tail == 1);
     };
     // ---- the tiles of this workgroup ----------------------------------------
     int t = blockIdx.x;
@@ -458,7 +484,6 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_w4a4_kernel(
 #pragma unroll
                 for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
         S1 = zero;     // the first group's "previous block" adds nothing
-        if (MODE != 2 && rank > 0) low_rank();
         // bias of the lane's columns, fetched now so its latency is hidden
         float bvj[TN];
 #pragma unroll
@@ -468,37 +493,102 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_w4a4_kernel(
         }
         // quad 0 published, quad 1 in flight, group 0's operands and quad 0's
         // scales read
-        publish();
+        publish_first();
         load_quad(cs1, ss1, 1, 0, DSPLIT);
 #pragma unroll
         for (int i = 0; i < TM; ++i) { read_a(cs0, 0, i); read_sa(ss0, 0, i); }
 #pragma unroll
         for (int j = 0; j < TN; ++j) { read_b(cs0, 0, j); read_sb(ss0, 0, j); }
 
-        for (int q = 0; q < NQ; q += 2) {
-            step(q, 0, cs0, ss0, cs1, ss1);
-            step(q + 1, 1, cs1, ss1, cs0, ss0);
+        if constexpr (FMT == 0) {
+            // the last two steps prefetch the first low-rank chunk in place
+            // of the quads past the end of K
+            const int NQE = (NQ + 1) & ~1;   // steps run in pairs
+            for (int q = 0; q < NQE - 2; q += 2) {
+                step(q, 0, cs0, ss0, cs1, ss1, 0);
+                step(q + 1, 1, cs1, ss1, cs0, ss0, 0);
+            }
+            step(NQE - 2, 0, cs0, ss0, cs1, ss1, 1);
+            step(NQE - 1, 1, cs1, ss1, cs0, ss0, 2);
+        } else {
+            // (the MXFP4 form keeps one loop body: a peeled copy of the last
+            // steps no longer fits its accumulators in the register budget)
+            for (int q = 0; q < NQ; q += 2) {
+                step(q, 0, cs0, ss0, cs1, ss1, 0);
+                step(q + 1, 1, cs1, ss1, cs0, ss0, 0);
+            }
         }
         if constexpr (MODE != 2 && FMT == 0) {
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[TM - 1][TN - 1][e] = __builtin_fmaf(P1[e], S1[e], acc[TM - 1][TN - 1][e]);
         }
-        // every load into LDS has landed and every wave is done with the
-        // slots: the next tile's first loads go out before this tile's stores
-        __syncthreads();
+        // INT4: the low-rank chunk in slot 0 was published by the last step.
+        // Afterwards every load into LDS has landed and every wave is past
+        // its last read of both slots.
+        if (MODE != 2 && rank > 0) low_rank();
+        else publish();
+        // ---- outputs -------------------------------------------------------
+        // The next tile's quad 0 goes out first (slot 0 is free), then this
+        // tile's outputs: bias, GELU and the one rounding run in registers.
+        // bf16 outputs leave through LDS: each wave writes its 64 x 64 values
+        // row-major into code slot 1 (free: every wave is past its last read)
+        // and reads them back as 16-byte row chunks, so a store instruction
+        // writes 8 rows x 128 bytes and a wave needs 8 stores, not one per
+        // output element. The next tile's first wait does not wait for them
+        // (publish_first): every workgroup finishes its tiles at about the
+        // same time, and a wait behind the chip-wide burst of output stores
+        // would idle the GPU.
+        static_assert(TM == 2 && TN == 2 && C::NW == 4 && C::CODE_SLOT >= 32768,
+                      "output staging assumes 64 x 64 wave tiles, 4 waves, 32 KB code slots");
         const int64_t em0 = m0, en0 = n0;
         const bool more = t + (int)gridDim.x < tiles;
-        if (more) start_tile(t + (int)gridDim.x);
-
-        if constexpr (MODE != 2) {
-            // bias, GELU and one rounding to the output type in registers, then
-            // buffer stores straight from the MFMA layout: a store instruction
-            // writes two 64-byte row segments (lanes 0..31 row r, lanes 32..63
-            // row r + 4); the row step is the scalar offset, so the stores need
-            // no address arithmetic. Rows past M fall outside the buffer range
-            // and are dropped; columns past N are masked.
-            constexpr int ESZ = (MODE == 0) ? 2 : 4;
-            const rsrc_t ry = make_rsrc(y, M * ldy * ESZ);
+        // INT4: the next tile's loads go out before the output work. (The
+        // MXFP4 form issues them after it: with the output work behind them
+        // its accumulators no longer fit the register budget.)
+        constexpr bool EARLY_NEXT = (FMT == 0 && MODE == 0);
+        if (EARLY_NEXT && more) start_tile(t + (int)gridDim.x);
+        if constexpr (MODE == 0) {
+            constexpr int RB = 128, CPR = 8;                   // bytes and 16-byte chunks per staged row
+            char* stg = cs1 + wave * 8192;
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+                for (int i = 0; i < TM; ++i)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) {
+                        float v = acc[i][j][e] + bvj[j];
+                        if constexpr (ACT == 1) v = gelu_tanh_f32(v);
+                        const int lr = i * 32 + out_row(e, lane), lc = j * 32 + (lane & 31);
+                        *(uint16_t*)(stg + lr * RB + lc * 2) = f32_to_bf16_bits(v);
+                    }
+            // the wave reads back only what it wrote (its own LDS operations
+            // complete in order)
+            uint4 ov[NST];
+#pragma unroll
+            for (int k = 0; k < NST; ++k) {
+                const int q = k * 64 + lane;
+                ov[k] = *(const uint4*)(stg + (q / CPR) * RB + (q % CPR) * 16);
+            }
+            if (!EARLY_NEXT && more) start_tile(t + (int)gridDim.x);
+            // rows past M fall outside the buffer range and are dropped;
+            // chunks past N (a multiple of 8) are masked
+            const rsrc_t ry = make_rsrc(y, M * ldy * 2);
+#pragma unroll
+            for (int k = 0; k < NST; ++k) {
+                const int q = k * 64 + lane;
+                const int64_t row = em0 + wm * 64 + q / CPR;
+                const int64_t col = en0 + wn * 64 + (q % CPR) * 8;
+                if (col < N)
+                    __builtin_amdgcn_raw_buffer_store_b128(v4i{(int)ov[k].x, (int)ov[k].y, (int)ov[k].z, (int)ov[k].w},
+                                                          ry, (int)((row * ldy + col) * 2), 0, 0);
+            }
+            stores_in_flight = more;
+        } else if constexpr (MODE == 1) {
+            // fp32 outputs: straight from the MFMA layout, one store per
+            // element (two row segments per instruction; the row step is the
+            // scalar offset); rows past M are dropped by the buffer range,
+            // columns past N masked. The next tile waits for them.
+            const rsrc_t ry = make_rsrc(y, M * ldy * 4);
 #pragma unroll
             for (int j = 0; j < TN; ++j) {
                 const int64_t col = en0 + wn * 32 * TN + j * 32 + (lane & 31);
@@ -506,20 +596,20 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_w4a4_kernel(
 #pragma unroll
                     for (int i = 0; i < TM; ++i) {
                         const int64_t row0 = em0 + wm * 32 * TM + i * 32 + 4 * (lane >> 5);
-                        const int vo = (int)((row0 * ldy + col) * ESZ);
+                        const int vo = (int)((row0 * ldy + col) * 4);
 #pragma unroll
                         for (int e = 0; e < 16; ++e) {
                             float v = acc[i][j][e] + bvj[j];
                             if constexpr (ACT == 1) v = gelu_tanh_f32(v);
-                            const int so = (8 * (e >> 2) + (e & 3)) * (int)ldy * ESZ;
-                            if constexpr (MODE == 0)
-                                __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_bits(v), ry, vo, so, 0);
-                            else
-                                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), ry, vo, so, 0);
+                            const int so = (8 * (e >> 2) + (e & 3)) * (int)ldy * 4;
+                            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), ry, vo, so, 0);
                         }
                     }
                 }
             }
+            if (more) start_tile(t + (int)gridDim.x);
+        } else {
+            if (more) start_tile(t + (int)gridDim.x);
         }
 
         if (!more) break;
