@@ -37,14 +37,15 @@ PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 # HBM traffic of one GEMM launch on the QKV shape, from two rocprofv3 counter
 # passes over this script (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch),
 # each scaled by the factor that makes the same counter read the known size of
-# the plain device copy this script also runs.  The figures hold only for the
+# the device copies this script also runs (a copy reads what it writes, and
+# WRITE_SIZE counts the written bytes exactly).  The figures hold only for the
 # kernel sources they were taken on (their sha256 below); otherwise the
 # traffic is reported as null.
 GEMM_TRAFFIC = {
-    "source_sha256": "bf40777b0a807bfba2ab9ffcda60dbd0d1b831a18449a5a694cf92fdf741250e",
-    "fetch_kib": 66638.78, "write_kib": 74732.45,        # QKV GEMM, mean of 40 dispatches
-    "fetch_factor": 262144.0 / 131084.49,                 # 256 MiB copy: known bytes / FETCH_SIZE
-    "write_factor": 262144.0 / 262144.0,                  # 256 MiB copy: known bytes / WRITE_SIZE
+    "source_sha256": "41f9ba31119e550f5e673ef4aaf62d6a038a7007ff963915a373192b2817826b",
+    "fetch_kib": 64229.2, "write_kib": 73728.0,          # QKV GEMM, mean of 3196 dispatches
+    "fetch_factor": 137704.0 / 68863.6,                   # device copies: bytes written / FETCH_SIZE
+    "write_factor": 1.0,                                  # WRITE_SIZE reads the bytes written
 }
 
 
