@@ -42,8 +42,10 @@ def jacobi_svd(a: np.ndarray, tol: float = 1e-15, max_sweeps: int = 60):
     a = np.asarray(a, dtype=np.float64)
     m, n = a.shape
     if m < n:
+        # the transpose's right vectors are this matrix's left ones: the
+        # sign convention is applied again, to this matrix's right vectors
         u, s, vt = jacobi_svd(a.T, tol, max_sweeps)
-        return vt.T, s, u.T
+        return _fix_signs(vt.T, s, u.T)
     # Columns of a are kept as contiguous rows of At (and of Vt for V).
     At = np.array(a.T, order="C", copy=True)
     Vt = np.eye(n)
@@ -107,7 +109,7 @@ def randomized_svd(a: np.ndarray, rank: int, omega: np.ndarray, power_iters: int
     b = q.T @ a
     ub, s, vt = jacobi_svd(b)
     u = q @ ub
-    return u[:, :rank], s[:rank], vt[:rank]
+    return _fix_signs(u[:, :rank], s[:rank], vt[:rank])
 
 
 def truncated_svd(a: np.ndarray, rank: int, seed: int = 0, exact_limit: int = 256,

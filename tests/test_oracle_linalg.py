@@ -35,6 +35,36 @@ def test_jacobi_rank_deficient_and_sign_convention():
     assert np.all(vt[np.arange(6), idx] > 0)
 
 
+def _signs_ok(vt, k):
+    idx = np.argmax(np.abs(vt[:k]), axis=1)
+    return bool(np.all(vt[np.arange(k), idx] > 0))
+
+
+@pytest.mark.parametrize("shape", [(30, 70), (70, 30)])
+def test_sign_convention_holds_for_wide_and_tall(shape):
+    """The convention is on the right singular vectors of the matrix given,
+    also when it is wider than tall (decomposed through its transpose)."""
+    a = np.random.default_rng(6).standard_normal(shape)
+    u, s, vt = linalg.jacobi_svd(a)
+    assert _signs_ok(vt, min(shape))
+    assert np.linalg.norm(u * s @ vt - a) <= 1e-12 * np.linalg.norm(a)
+
+
+def test_sign_convention_holds_for_the_range_finder():
+    """The randomised path returns factors under the same convention (it
+    must not depend on the signs the orthonormal bases happened to get)."""
+    rng = np.random.default_rng(7)
+    a = rng.standard_normal((300, 500)) * np.linspace(5.0, 0.1, 300)[:, None]
+    omega = rng.standard_normal((500, 24))
+    u, s, vt = linalg.randomized_svd(a, 8, omega, power_iters=3)
+    assert _signs_ok(vt, 8)
+    # flipping the sign of the test matrix flips the bases, not the result
+    u2, s2, vt2 = linalg.randomized_svd(a, 8, -omega, power_iters=3)
+    assert np.allclose(vt, vt2, atol=1e-10) and np.allclose(u, u2, atol=1e-10)
+    u3, s3, vt3 = linalg.truncated_svd(a, 8, seed=1)
+    assert _signs_ok(vt3, 8)
+
+
 def test_full_rank_reconstruction_of_smoothed_weight():
     """With r = min(K, N), the fp64 factors reproduce the matrix (north-star
     check 'full-rank reconstruction of W')."""
