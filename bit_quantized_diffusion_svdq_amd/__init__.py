@@ -10,7 +10,10 @@ from ._lib import (SvdqError, awq_gemv_w4a16, check_device, library_path, load_l
                    svdq_quantize_act, w4a4_linear, awq_gemv, STATUS_NAMES,
                    svdq_quantize_act_mxfp4, svdq_gemm_mxfp4, quantize_act_mxfp4, mxfp4_linear, pack_l1,
                    LayerDesc, LayerSizes, layer_desc, layer_sizes, svdq_validate_desc, validate_desc,
-                   svdq_probe_clock, svdq_probe_read)
+                   svdq_probe_clock, svdq_probe_read, svdq_calib_absmax, svdq_smoothing,
+                   svdq_smooth_weight, svdq_lowrank_workspace_size, svdq_lowrank, svdq_quantize_residual,
+                   svdq_pack_lowrank)
+from .offline import quantize_layer
 from .fused import column_offsets, column_slice, projection_weights, split_columns
 from .graph import CapturedSequence
 
@@ -19,5 +22,7 @@ __all__ = ["SvdqError", "awq_gemv_w4a16", "check_device", "library_path", "load_
            "svdq_quantize_act", "w4a4_linear", "awq_gemv", "STATUS_NAMES",
            "svdq_quantize_act_mxfp4", "svdq_gemm_mxfp4", "quantize_act_mxfp4", "mxfp4_linear", "pack_l1",
            "LayerDesc", "LayerSizes", "layer_desc", "layer_sizes", "svdq_validate_desc", "validate_desc",
-           "svdq_probe_clock", "svdq_probe_read",
+           "svdq_probe_clock", "svdq_probe_read", "svdq_calib_absmax", "svdq_smoothing",
+           "svdq_smooth_weight", "svdq_lowrank_workspace_size", "svdq_lowrank", "svdq_quantize_residual",
+           "svdq_pack_lowrank", "quantize_layer",
            "column_offsets", "column_slice", "projection_weights", "split_columns", "CapturedSequence"]

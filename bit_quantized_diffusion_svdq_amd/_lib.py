@@ -40,6 +40,13 @@ _SIGS = {
     "awq_gemv_w4a16": [_P, _I64, _I64, _P, _P, _P, _P, _I64, _P, _P, _P],
     "svdq_probe_clock": [_P, _I32, _P],
     "svdq_probe_read": [_P, _I64, _P, _I32, _P],
+    "svdq_calib_absmax": [_P, _I64, _I64, _I64, _I32, _I32, _P, _P],
+    "svdq_smoothing": [_P, _P, _I64, ctypes.c_double, _P, _P],
+    "svdq_smooth_weight": [_P, _I64, _I64, _I64, _P, _P, _P],
+    "svdq_lowrank_workspace_size": [_I64, _I64, _I32, _I32, _P],
+    "svdq_lowrank": [_P, _I64, _I64, _I32, _P, _I32, _I32, _P, _P, _P, _P, _I64, _P],
+    "svdq_quantize_residual": [_P, _I64, _I64, _P, _P, _I32, _P, _P, _P],
+    "svdq_pack_lowrank": [_P, _P, _I64, _I64, _I32, _P, _P, _P],
 }
 
 
@@ -188,6 +195,45 @@ def svdq_probe_clock(ticks, spins, stream=None):
 def svdq_probe_read(buf, nbytes, sink, blocks, stream=None):
     _check(load_library().svdq_probe_read(_ptr(buf), nbytes, _ptr(sink), blocks, _stream(stream)),
            "svdq_probe_read")
+
+
+def svdq_calib_absmax(a, rows, cols, lda, axis, accumulate, out, stream=None):
+    _check(load_library().svdq_calib_absmax(_ptr(a), rows, cols, lda, axis, accumulate, _ptr(out),
+                                            _stream(stream)), "svdq_calib_absmax")
+
+
+def svdq_smoothing(ax, aw, K, alpha, inv_lambda, stream=None):
+    _check(load_library().svdq_smoothing(_ptr(ax), _ptr(aw), K, float(alpha), _ptr(inv_lambda),
+                                         _stream(stream)), "svdq_smoothing")
+
+
+def svdq_smooth_weight(w, K, N, ldw, inv_lambda, w_hat, stream=None):
+    _check(load_library().svdq_smooth_weight(_ptr(w), K, N, ldw, _ptr(inv_lambda), _ptr(w_hat),
+                                             _stream(stream)), "svdq_smooth_weight")
+
+
+def svdq_lowrank_workspace_size(K, N, rank, l) -> int:
+    out = ctypes.c_int64(0)
+    _check(load_library().svdq_lowrank_workspace_size(K, N, rank, l, ctypes.byref(out)),
+           "svdq_lowrank_workspace_size")
+    return out.value
+
+
+def svdq_lowrank(w_hat, K, N, rank, omega, l, power_iters, l1, l2, sigma, workspace, workspace_bytes,
+                 stream=None):
+    _check(load_library().svdq_lowrank(_ptr(w_hat), K, N, rank, _ptr(omega), l, power_iters, _ptr(l1),
+                                       _ptr(l2), _ptr(sigma), _ptr(workspace), workspace_bytes,
+                                       _stream(stream)), "svdq_lowrank")
+
+
+def svdq_quantize_residual(w_hat, K, N, l1, l2, rank, qw, sw, stream=None):
+    _check(load_library().svdq_quantize_residual(_ptr(w_hat), K, N, _ptr(l1), _ptr(l2), rank, _ptr(qw),
+                                                 _ptr(sw), _stream(stream)), "svdq_quantize_residual")
+
+
+def svdq_pack_lowrank(l1, l2, K, N, rank, l1t, l2t, stream=None):
+    _check(load_library().svdq_pack_lowrank(_ptr(l1), _ptr(l2), K, N, rank, _ptr(l1t), _ptr(l2t),
+                                            _stream(stream)), "svdq_pack_lowrank")
 
 
 # ---------------------------------------------------------------- tensor helpers

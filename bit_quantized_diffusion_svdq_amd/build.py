@@ -8,7 +8,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libsvdq.so")
-SOURCES = ["api.hip", "act_quant.hip", "gemm_w4a4.hip", "gemv_w4a16.hip", "probe.hip"]
+SOURCES = ["api.hip", "act_quant.hip", "gemm_w4a4.hip", "gemv_w4a16.hip", "probe.hip", "offline.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

@@ -31,6 +31,7 @@
 // E2M1, E8M0, conversion from FP32). The instruction keeps the sign of values
 // that round to zero; those nibbles get sign 0 afterwards.
 #include "common.h"
+#include "int4_fields.h"
 
 namespace {
 
@@ -39,32 +40,6 @@ constexpr int ROWS = 16;
 // VGPRs (rank <= 32), else 8; more waves with fewer groups in flight each let a
 // SIMD work on whichever wave's data has landed
 __host__ __device__ constexpr int waves_for(int rt) { return rt <= 2 ? 16 : 8; }
-
-// Quantise one value given the group's fp32 reciprocal `inv` (0 when the
-// scale is 0) and return its FP6 E2M3 field: magnitude in bits 0-2, zero
-// exponent, sign in bit 5 (zero is stored with sign 0). Clamping to [-7, 7]
-// before rounding equals clamping after it (the bounds are integers);
-// |a| + 1.5 * 2^23 rounds |a| half-to-even into the low mantissa bits (the
-// spacing there is 1 and the constant is even), and round(a) < 0 exactly
-// when a + 0.5 < 0, which gives the sign without a compare.
-DEV uint32_t code_field(float v, float inv) {
-    const float t = v * inv;                   // one fp32 multiply (no contraction)
-    const float a = __builtin_amdgcn_fmed3f(t, -7.0f, 7.0f);
-    const uint32_t mag = __float_as_uint(fabsf(a) + 12582912.0f) & 7u;
-    const uint32_t sgn = (__float_as_uint(a + 0.5f) >> 26) & 32u;
-    return mag | sgn;
-}
-
-// Sixteen E2M3 fields (code e at bits 6e..6e+5 of a 96-bit stream T) -> the
-// 64-bit storage word: T[0:32) and T[64:96) keep their places, and the bits of
-// T[32:64) go into the zero exponent positions of those two thirds
-// (0x18618618 in the low word, 0x61861861 in the high word).
-DEV uint2 fold_fields(const uint32_t (&f)[16]) {
-    const uint32_t d0 = f[0] | (f[1] << 6) | (f[2] << 12) | (f[3] << 18) | (f[4] << 24) | (f[5] << 30);
-    const uint32_t d1 = (f[5] >> 2) | (f[6] << 4) | (f[7] << 10) | (f[8] << 16) | (f[9] << 22) | (f[10] << 28);
-    const uint32_t d2 = (f[10] >> 4) | (f[11] << 2) | (f[12] << 8) | (f[13] << 14) | (f[14] << 20) | (f[15] << 26);
-    return make_uint2(d0 | (d1 & 0x18618618u), d2 | (d1 & 0x61861861u));
-}
 
 // Eight E2M1 nibbles (t[0] in bits 0-3): round to nearest, ties to mantissa
 // 0, saturating at 6 (the conversion instruction), then the sign of every

@@ -33,6 +33,21 @@ hipError_t launch_gemv_w4a16(const uint16_t* x, int M, int64_t K, const float* i
                              const uint8_t* qwt, const uint16_t* scale, const uint16_t* zero,
                              int64_t N, const uint16_t* bias, uint16_t* y, int cus, hipStream_t stream);
 size_t gemv_smem_bytes(int M, int64_t K);
+hipError_t launch_calib_absmax(const uint16_t* a, int64_t rows, int64_t cols, int64_t lda, int axis,
+                               int accumulate, float* out, hipStream_t stream);
+hipError_t launch_smoothing(const float* ax, const float* aw, int64_t K, double alpha, float* inv_lambda,
+                            hipStream_t stream);
+hipError_t launch_smooth_weight(const uint16_t* w, int64_t K, int64_t N, int64_t ldw, const float* inv_lambda,
+                                double* w_hat, hipStream_t stream);
+int64_t offline_lowrank_ws_bytes(int64_t K, int64_t N, int l);
+int offline_lmax();
+hipError_t launch_lowrank(const double* w_hat, int64_t K, int64_t N, int r, const double* omega, int l,
+                          int power_iters, uint16_t* l1, uint16_t* l2, double* sigma, void* ws,
+                          hipStream_t stream);
+hipError_t launch_quantize_residual(const double* w_hat, int64_t K, int64_t N, const uint16_t* l1,
+                                    const uint16_t* l2, int r, uint8_t* qw, uint16_t* sw, hipStream_t stream);
+hipError_t launch_pack_lowrank(const uint16_t* l1, const uint16_t* l2, int64_t K, int64_t N, int r, uint16_t* l1t,
+                               uint16_t* l2t, hipStream_t stream);
 hipError_t launch_clock_probe(long long* out, int spins, hipStream_t stream);
 hipError_t launch_read_probe(const uint8_t* buf, int64_t bytes, uint32_t* sink, int blocks,
                              hipStream_t stream);
@@ -374,3 +389,143 @@ svdq_status svdq_probe_read(const void* buf, int64_t bytes, uint32_t* sink, int3
 }
 
 }  // extern "C"
+
+/* ------------------------------------------------------------------------ */
+/* offline quantiser                                                         */
+
+namespace {
+
+// element counts the offline kernels index with 64-bit offsets; a product of
+// two sizes must stay far from overflow
+svdq_status check_dims(int64_t a, int64_t b, const char* what) {
+    if (a < 0 || b < 0 || (a > 0 && b > (((int64_t)1 << 46) / a)))
+        return fail(SVDQ_ERR_SHAPE, "%s: %lld x %lld is out of range", what, (long long)a, (long long)b);
+    return SVDQ_OK;
+}
+
+}  // namespace
+
+svdq_status svdq_calib_absmax(const void* a, int64_t rows, int64_t cols, int64_t lda, int32_t axis,
+                              int32_t accumulate, float* out, void* stream) {
+    svdq_status s;
+    if (axis != 0 && axis != 1) return fail(SVDQ_ERR_UNSUPPORTED, "axis %d must be 0 or 1", axis);
+    if (accumulate != 0 && accumulate != 1) return fail(SVDQ_ERR_UNSUPPORTED, "accumulate must be 0 or 1");
+    if ((s = check_dims(rows, cols, "svdq_calib_absmax")) != SVDQ_OK) return s;
+    if (cols % 8) return fail(SVDQ_ERR_SHAPE, "cols = %lld must be a multiple of 8", (long long)cols);
+    if (lda < cols || lda % 8) return fail(SVDQ_ERR_SHAPE, "lda = %lld must be >= cols and a multiple of 8", (long long)lda);
+    const int64_t n = axis == 0 ? cols : rows;
+    if (n == 0) { g_last_error.clear(); return SVDQ_OK; }
+    if (!out || (rows > 0 && cols > 0 && !a)) return fail(SVDQ_ERR_NULL, "a and out are required");
+    if ((a && !aligned(a, 16)) || !aligned(out, 4)) return fail(SVDQ_ERR_ALIGN, "a needs 16-byte alignment, out 4");
+    if ((s = check_current_device()) != SVDQ_OK) return s;
+    return launched(launch_calib_absmax((const uint16_t*)a, rows, cols, lda, axis, accumulate, out,
+                                        (hipStream_t)stream),
+                    "svdq_calib_absmax launch");
+}
+
+svdq_status svdq_smoothing(const float* ax, const float* aw, int64_t K, double alpha, float* inv_lambda,
+                           void* stream) {
+    svdq_status s;
+    if (K < 0) return fail(SVDQ_ERR_SHAPE, "K = %lld must be >= 0", (long long)K);
+    if (!(alpha >= 0.0 && alpha <= 1.0)) return fail(SVDQ_ERR_UNSUPPORTED, "alpha %g must be in [0, 1]", alpha);
+    if (K == 0) { g_last_error.clear(); return SVDQ_OK; }
+    if (!ax || !aw || !inv_lambda) return fail(SVDQ_ERR_NULL, "ax, aw and inv_lambda are required");
+    if (!aligned(ax, 4) || !aligned(aw, 4) || !aligned(inv_lambda, 4)) return fail(SVDQ_ERR_ALIGN, "4-byte alignment");
+    if ((s = check_current_device()) != SVDQ_OK) return s;
+    return launched(launch_smoothing(ax, aw, K, alpha, inv_lambda, (hipStream_t)stream), "svdq_smoothing launch");
+}
+
+svdq_status svdq_smooth_weight(const void* w, int64_t K, int64_t N, int64_t ldw, const float* inv_lambda,
+                               double* w_hat, void* stream) {
+    svdq_status s;
+    if ((s = check_dims(K, N, "svdq_smooth_weight")) != SVDQ_OK) return s;
+    if (K > 65535) return fail(SVDQ_ERR_SHAPE, "K = %lld above 65535", (long long)K);
+    if (N % 8) return fail(SVDQ_ERR_SHAPE, "N = %lld must be a multiple of 8", (long long)N);
+    if (ldw < N || ldw % 8) return fail(SVDQ_ERR_SHAPE, "ldw = %lld must be >= N and a multiple of 8", (long long)ldw);
+    if (K == 0 || N == 0) { g_last_error.clear(); return SVDQ_OK; }
+    if (!w || !w_hat) return fail(SVDQ_ERR_NULL, "w and w_hat are required");
+    if (!aligned(w, 16) || !aligned(w_hat, 16) || (inv_lambda && !aligned(inv_lambda, 4)))
+        return fail(SVDQ_ERR_ALIGN, "w and w_hat need 16-byte alignment");
+    if ((s = check_current_device()) != SVDQ_OK) return s;
+    return launched(launch_smooth_weight((const uint16_t*)w, K, N, ldw, inv_lambda, w_hat, (hipStream_t)stream),
+                    "svdq_smooth_weight launch");
+}
+
+namespace {
+
+svdq_status check_lowrank_shape(int64_t K, int64_t N, int32_t rank, int32_t l) {
+    svdq_status s;
+    if ((s = check_dims(K, N, "svdq_lowrank")) != SVDQ_OK) return s;
+    if (K < 1 || N < 1) return fail(SVDQ_ERR_SHAPE, "K and N must be >= 1");
+    if (rank < 1 || rank > 80 || rank % 16)
+        return fail(SVDQ_ERR_SHAPE, "rank %d must be a multiple of 16 in [16, 80]", rank);
+    const int64_t mn = K < N ? K : N;
+    if (l < rank || l > offline_lmax() || l > mn)
+        return fail(SVDQ_ERR_SHAPE, "block width l = %d must satisfy rank <= l <= min(%d, K, N)", l, offline_lmax());
+    return SVDQ_OK;
+}
+
+}  // namespace
+
+svdq_status svdq_lowrank_workspace_size(int64_t K, int64_t N, int32_t rank, int32_t l, int64_t* bytes) {
+    svdq_status s;
+    if (!bytes) return fail(SVDQ_ERR_NULL, "bytes is required");
+    if ((s = check_lowrank_shape(K, N, rank, l)) != SVDQ_OK) return s;
+    *bytes = offline_lowrank_ws_bytes(K, N, l);
+    g_last_error.clear();
+    return SVDQ_OK;
+}
+
+svdq_status svdq_lowrank(const double* w_hat, int64_t K, int64_t N, int32_t rank, const double* omega, int32_t l,
+                         int32_t power_iters, void* l1, void* l2, double* sigma, void* workspace,
+                         int64_t workspace_bytes, void* stream) {
+    svdq_status s;
+    if ((s = check_lowrank_shape(K, N, rank, l)) != SVDQ_OK) return s;
+    if (power_iters < 0 || power_iters > 64) return fail(SVDQ_ERR_SHAPE, "power_iters %d must be in [0, 64]", power_iters);
+    if (workspace_bytes < offline_lowrank_ws_bytes(K, N, l))
+        return fail(SVDQ_ERR_SHAPE, "workspace of %lld bytes, %lld needed", (long long)workspace_bytes,
+                    (long long)offline_lowrank_ws_bytes(K, N, l));
+    if (!w_hat || !omega || !l1 || !l2 || !workspace) return fail(SVDQ_ERR_NULL, "w_hat, omega, l1, l2, workspace are required");
+    if (!aligned(w_hat, 8) || !aligned(omega, 8) || !aligned(l1, 2) || !aligned(l2, 2) ||
+        (sigma && !aligned(sigma, 8)) || !aligned(workspace, 256))
+        return fail(SVDQ_ERR_ALIGN, "w_hat, omega, sigma 8-byte, l1, l2 2-byte, workspace 256-byte alignment");
+    if ((s = check_current_device()) != SVDQ_OK) return s;
+    return launched(launch_lowrank(w_hat, K, N, rank, omega, l, power_iters, (uint16_t*)l1, (uint16_t*)l2, sigma,
+                                   workspace, (hipStream_t)stream),
+                    "svdq_lowrank launch");
+}
+
+svdq_status svdq_quantize_residual(const double* w_hat, int64_t K, int64_t N, const void* l1, const void* l2,
+                                   int32_t rank, uint8_t* qw, void* sw_f16, void* stream) {
+    svdq_status s;
+    if ((s = check_dims(K, N, "svdq_quantize_residual")) != SVDQ_OK) return s;
+    if ((s = check_k(K)) != SVDQ_OK) return s;
+    if (K / 64 > 65535) return fail(SVDQ_ERR_SHAPE, "K = %lld: more than 65535 groups", (long long)K);
+    if (N < 1) return fail(SVDQ_ERR_SHAPE, "N must be >= 1");
+    if (rank < 0 || rank > 112 || rank % 16) return fail(SVDQ_ERR_SHAPE, "rank %d must be a multiple of 16 in [0, 112]", rank);
+    if (!w_hat || !qw || !sw_f16 || (rank > 0 && (!l1 || !l2)))
+        return fail(SVDQ_ERR_NULL, "w_hat, qw, sw (and l1, l2 when rank > 0) are required");
+    if (!aligned(w_hat, 8) || !aligned(qw, 8) || !aligned(sw_f16, 2) || (l1 && !aligned(l1, 2)) || (l2 && !aligned(l2, 2)))
+        return fail(SVDQ_ERR_ALIGN, "w_hat, qw 8-byte, sw, l1, l2 2-byte alignment");
+    if ((s = check_current_device()) != SVDQ_OK) return s;
+    return launched(launch_quantize_residual(w_hat, K, N, (const uint16_t*)l1, (const uint16_t*)l2, rank, qw,
+                                             (uint16_t*)sw_f16, (hipStream_t)stream),
+                    "svdq_quantize_residual launch");
+}
+
+svdq_status svdq_pack_lowrank(const void* l1, const void* l2, int64_t K, int64_t N, int32_t rank, void* l1t,
+                              void* l2t, void* stream) {
+    svdq_status s;
+    if ((s = check_dims(K, N, "svdq_pack_lowrank")) != SVDQ_OK) return s;
+    if ((s = check_k(K)) != SVDQ_OK) return s;
+    if ((s = check_rank(rank)) != SVDQ_OK) return s;
+    if (N < 1) return fail(SVDQ_ERR_SHAPE, "N must be >= 1");
+    if (rank == 0) { g_last_error.clear(); return SVDQ_OK; }
+    if (!l1 || !l2 || !l1t || !l2t) return fail(SVDQ_ERR_NULL, "l1, l2, l1t, l2t are required");
+    if (!aligned(l1, 2) || !aligned(l2, 2) || !aligned(l1t, 16) || !aligned(l2t, 2))
+        return fail(SVDQ_ERR_ALIGN, "l1t needs 16-byte alignment, the others 2");
+    if ((s = check_current_device()) != SVDQ_OK) return s;
+    return launched(launch_pack_lowrank((const uint16_t*)l1, (const uint16_t*)l2, K, N, rank, (uint16_t*)l1t,
+                                        (uint16_t*)l2t, (hipStream_t)stream),
+                    "svdq_pack_lowrank launch");
+}

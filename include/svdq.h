@@ -308,6 +308,81 @@ svdq_status awq_gemv_w4a16(const void* x, int64_t M, int64_t K, const float* inv
 svdq_status svdq_probe_clock(int64_t* ticks, int32_t spins, void* stream);
 svdq_status svdq_probe_read(const void* buf, int64_t bytes, uint32_t* sink, int32_t blocks, void* stream);
 
+/* ------------------------------------------------------------------------
+ * Offline quantiser: turning a bf16 weight into the arrays above, on the
+ * GPU. This is the Quantize step of the tool chain the donmalab.com page
+ * describes (section on quantising a model yourself: inspect, quantize,
+ * package, validate), with the roles the remio.ai page gives the parts
+ * (section on SVDQuant moving hard values out of 4-bit): calibration
+ * statistics set the smoothing, a 16-bit low-rank branch takes the hardest
+ * part of the smoothed weight, the residual becomes 4-bit. Every call
+ * enqueues on `stream`, allocates nothing and does not synchronise; all
+ * pointers are device memory owned by the caller. Results are
+ * deterministic (no atomics on floating-point sums).
+ *
+ * svdq_calib_absmax -- per-channel absolute maxima of a bf16 matrix
+ *   a [rows][cols] (row stride lda elements, cols and lda multiples of 8,
+ *   a 16-byte aligned). axis 0: out[c] = max_r |a[r][c]| (out [cols]; the
+ *   activation statistic ax[k] over a calibration batch X [M][K]); axis 1:
+ *   out[r] = max_c |a[r][c]| (out [rows]; the weight statistic aw[k] of
+ *   W [K][N]). accumulate 1 folds the result into the maxima already in
+ *   out (calibration over several batches), 0 overwrites them. Inputs are
+ *   finite.
+ */
+svdq_status svdq_calib_absmax(const void* a, int64_t rows, int64_t cols, int64_t lda, int32_t axis,
+                              int32_t accumulate, float* out, void* stream);
+
+/* svdq_smoothing -- lambda[k] = ax[k]^alpha / aw[k]^(1 - alpha) in fp64 (1
+ *   where either maximum is 0; alpha in [0, 1], 0.5 through square roots),
+ *   written as inv_lambda[k] = fp32(1 / lambda[k]) [K]: the online
+ *   activation scale (remio.ai page, same section: outliers move into the
+ *   weights). */
+svdq_status svdq_smoothing(const float* ax, const float* aw, int64_t K, double alpha, float* inv_lambda,
+                           void* stream);
+
+/* svdq_smooth_weight -- w_hat[k][n] = f64(W[k][n]) / f64(inv_lambda[k]),
+ *   fp64 [K][N] (dense, 16-byte aligned) from bf16 W [K][N] (row stride ldw,
+ *   N and ldw multiples of 8, K <= 65535). inv_lambda NULL means 1. */
+svdq_status svdq_smooth_weight(const void* w, int64_t K, int64_t N, int64_t ldw, const float* inv_lambda,
+                               double* w_hat, void* stream);
+
+/* svdq_lowrank -- the rank-r truncated SVD of w_hat [K][N] (fp64) as the
+ *   low-rank branch: L1 = bf16(U_r Sigma_r) [K][r] and L2 = bf16(V_r^T)
+ *   [r][N], each entry rounded once from fp64 to nearest even, the entry of
+ *   largest magnitude of every right singular vector positive; sigma [r]
+ *   (fp64, may be NULL) the singular values, descending. Method: randomised
+ *   range finder with power iterations (Halko, Martinsson and Tropp, SIAM
+ *   Review 2011, algorithms 4.3/4.4 and 5.1) from the caller's random test
+ *   matrix omega [N][l] (fp64, e.g. standard normal), power_iters in
+ *   [0, 64], block width l with rank <= l <= min(88, K, N); the l x N
+ *   projection is decomposed exactly (Jacobi). rank is a multiple of 16 in
+ *   [16, 80]. workspace: device memory of at least
+ *   svdq_lowrank_workspace_size() bytes, 256-byte aligned, contents
+ *   irrelevant; calls sharing it must not overlap.
+ */
+svdq_status svdq_lowrank_workspace_size(int64_t K, int64_t N, int32_t rank, int32_t l, int64_t* bytes);
+svdq_status svdq_lowrank(const double* w_hat, int64_t K, int64_t N, int32_t rank, const double* omega, int32_t l,
+                         int32_t power_iters, void* l1, void* l2, double* sigma, void* workspace,
+                         int64_t workspace_bytes, void* stream);
+
+/* svdq_quantize_residual -- R = fp32(w_hat - f64(L1) f64(L2)) (L1 bf16
+ *   [K][rank], L2 bf16 [rank][N]; rank a multiple of 16 in [0, 112], 0 = no
+ *   branch), then symmetric INT4 per (output column n, group of 64 along
+ *   K): s = fp16(min(amax / 7, 65504)), q = clamp(rtne(R * fp32(1 / s)),
+ *   -7, 7), all codes 0 where s = 0. Writes qw [N][K/2] (codes format v2)
+ *   and sw (scales format v3, [ceil(G/4)][N][4] fp16, padding 0): the
+ *   weight operands of svdq_gemm_w4a4. K a multiple of 64; qw 8-byte
+ *   aligned. */
+svdq_status svdq_quantize_residual(const double* w_hat, int64_t K, int64_t N, const void* l1, const void* l2,
+                                   int32_t rank, uint8_t* qw, void* sw_f16, void* stream);
+
+/* svdq_pack_lowrank -- L1 [K][rank] and L2 [rank][N] (bf16) into the layouts
+ *   the online kernels read: l1t (format v4 tiles, 16-byte aligned) for
+ *   svdq_quantize_act and l2t [N][rank] for svdq_gemm_w4a4. rank 0 writes
+ *   nothing. */
+svdq_status svdq_pack_lowrank(const void* l1, const void* l2, int64_t K, int64_t N, int32_t rank, void* l1t,
+                              void* l2t, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

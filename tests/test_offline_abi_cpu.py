@@ -1,0 +1,137 @@
+"""Host-side checks of the offline quantiser's C ABI (no GPU needed): every
+malformed call returns its documented status before touching the device;
+well-formed calls on a machine without a gfx950 GPU stop at the capability
+check. The workspace query is pure host arithmetic."""
+import ctypes
+
+import pytest
+
+import bit_quantized_diffusion_svdq_amd as svdq
+
+OK, NULL, SHAPE, ALIGN, UNSUP, DEVICE = 0, 1, 2, 3, 4, 5
+A, B, C, D, E = 0x7F0000000000, 0x7F0000100000, 0x7F0000200000, 0x7F0000300000, 0x7F0000400000
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return svdq.load_library()
+
+
+def _no_gpu():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(axis=2), UNSUP), (dict(acc=3), UNSUP), (dict(cols=100), SHAPE), (dict(lda=8), SHAPE),
+    (dict(lda=260), SHAPE), (dict(rows=-1), SHAPE), (dict(out=None), NULL), (dict(a=None), NULL),
+    (dict(a=A + 8), ALIGN), (dict(out=B + 2), ALIGN),
+])
+def test_calib_absmax_rejects(lib, kw, status):
+    a = dict(a=A, rows=64, cols=256, lda=256, axis=0, acc=0, out=B)
+    a.update(kw)
+    assert lib.svdq_calib_absmax(a["a"], a["rows"], a["cols"], a["lda"], a["axis"], a["acc"], a["out"], None) == status
+
+
+def test_calib_absmax_empty_is_ok(lib):
+    assert lib.svdq_calib_absmax(None, 0, 0, 0, 0, 0, None, None) == OK
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(alpha=-0.1), UNSUP), (dict(alpha=1.5), UNSUP), (dict(alpha=float("nan")), UNSUP), (dict(K=-1), SHAPE),
+    (dict(ax=None), NULL), (dict(inv=None), NULL), (dict(aw=B + 2), ALIGN),
+])
+def test_smoothing_rejects(lib, kw, status):
+    a = dict(ax=A, aw=B, K=256, alpha=0.5, inv=C)
+    a.update(kw)
+    assert lib.svdq_smoothing(a["ax"], a["aw"], a["K"], a["alpha"], a["inv"], None) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(N=100), SHAPE), (dict(ldw=8), SHAPE), (dict(K=70000), SHAPE), (dict(w=None), NULL),
+    (dict(w_hat=None), NULL), (dict(w=A + 8), ALIGN), (dict(w_hat=C + 8), ALIGN),
+])
+def test_smooth_weight_rejects(lib, kw, status):
+    a = dict(w=A, K=256, N=512, ldw=512, inv=B, w_hat=C)
+    a.update(kw)
+    assert lib.svdq_smooth_weight(a["w"], a["K"], a["N"], a["ldw"], a["inv"], a["w_hat"], None) == status
+
+
+def _ws(lib, K, N, r, l):
+    out = ctypes.c_int64(0)
+    st = lib.svdq_lowrank_workspace_size(K, N, r, l, ctypes.byref(out))
+    return st, out.value
+
+
+def test_lowrank_workspace_size(lib):
+    st, n = _ws(lib, 3072, 9216, 32, 48)
+    assert st == OK and n >= 8 * (2 * 3072 * 48 + 2 * 9216 * 48)
+    st2, n2 = _ws(lib, 512, 512, 16, 32)
+    assert st2 == OK and 0 < n2 < n
+    assert lib.svdq_lowrank_workspace_size(512, 512, 16, 32, None) == NULL
+
+
+@pytest.mark.parametrize("K,N,r,l", [(512, 512, 0, 16), (512, 512, 24, 32), (512, 512, 96, 96),
+                                     (512, 512, 32, 16), (512, 512, 32, 89), (64, 512, 32, 80),
+                                     (512, 40, 32, 48), (0, 512, 16, 16)])
+def test_lowrank_shape_rejects(lib, K, N, r, l):
+    assert _ws(lib, K, N, r, l)[0] == SHAPE
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(iters=-1), SHAPE), (dict(iters=65), SHAPE), (dict(wsb=1024), SHAPE), (dict(w_hat=None), NULL),
+    (dict(omega=None), NULL), (dict(l1=None), NULL), (dict(ws=None), NULL), (dict(ws=E + 8), ALIGN),
+    (dict(omega=B + 4), ALIGN),
+])
+def test_lowrank_rejects(lib, kw, status):
+    a = dict(w_hat=A, K=512, N=512, r=16, omega=B, l=32, iters=4, l1=C, l2=D, sigma=None, ws=E, wsb=1 << 30)
+    a.update(kw)
+    assert lib.svdq_lowrank(a["w_hat"], a["K"], a["N"], a["r"], a["omega"], a["l"], a["iters"], a["l1"], a["l2"],
+                            a["sigma"], a["ws"], a["wsb"], None) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(K=96), SHAPE), (dict(N=0), SHAPE), (dict(r=128), SHAPE), (dict(r=8), SHAPE), (dict(qw=None), NULL),
+    (dict(l1=None), NULL), (dict(sw=None), NULL), (dict(qw=C + 4), ALIGN), (dict(w_hat=A + 4), ALIGN),
+])
+def test_quantize_residual_rejects(lib, kw, status):
+    a = dict(w_hat=A, K=256, N=64, l1=B, l2=E, r=16, qw=C, sw=D)
+    a.update(kw)
+    assert lib.svdq_quantize_residual(a["w_hat"], a["K"], a["N"], a["l1"], a["l2"], a["r"], a["qw"], a["sw"],
+                                      None) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(K=96), SHAPE), (dict(r=20), SHAPE), (dict(N=0), SHAPE), (dict(l1t=None), NULL), (dict(l1t=C + 2), ALIGN),
+])
+def test_pack_lowrank_rejects(lib, kw, status):
+    a = dict(l1=A, l2=B, K=256, N=64, r=16, l1t=C, l2t=D)
+    a.update(kw)
+    assert lib.svdq_pack_lowrank(a["l1"], a["l2"], a["K"], a["N"], a["r"], a["l1t"], a["l2t"], None) == status
+
+
+def test_rank_zero_residual_and_pack_need_no_factors(lib):
+    _no_gpu()
+    assert lib.svdq_pack_lowrank(None, None, 256, 64, 0, None, None, None) == OK
+    assert lib.svdq_quantize_residual(A, 256, 64, None, None, 0, C, D, None) == DEVICE
+
+
+def test_valid_offline_calls_without_gpu_report_device_error(lib):
+    _no_gpu()
+    assert lib.svdq_calib_absmax(A, 64, 256, 256, 1, 0, B, None) == DEVICE
+    assert lib.svdq_smoothing(A, B, 256, 0.5, C, None) == DEVICE
+    assert lib.svdq_smooth_weight(A, 256, 512, 512, B, C, None) == DEVICE
+    assert lib.svdq_lowrank(A, 512, 512, 16, B, 32, 4, C, D, None, E, 1 << 30, None) == DEVICE
+    assert lib.svdq_pack_lowrank(A, B, 256, 64, 16, C, D, None) == DEVICE
+
+
+def test_quantize_layer_rejects_host_tensors():
+    import torch
+    w = torch.zeros((256, 64), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        svdq.quantize_layer(w, w.T.contiguous(), 16)            # calibration batch of the wrong width
+    with pytest.raises(ValueError, match="rank"):
+        svdq.quantize_layer(w, None, 24, smooth=False)
+    with pytest.raises(ValueError, match="GPU"):
+        svdq.quantize_layer(w, torch.zeros((8, 256), dtype=torch.bfloat16), 16)
