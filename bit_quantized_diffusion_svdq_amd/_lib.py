@@ -47,6 +47,9 @@ _SIGS = {
     "svdq_lowrank": [_P, _I64, _I64, _I32, _P, _I32, _I32, _P, _P, _P, _P, _I64, _P],
     "svdq_quantize_residual": [_P, _I64, _I64, _P, _P, _I32, _P, _P, _P],
     "svdq_pack_lowrank": [_P, _P, _I64, _I64, _I32, _P, _P, _P],
+    "svdq_gemm_w4a4_quant_next_workspace_size": [_I64, _I64, _I32, _P],
+    "svdq_gemm_w4a4_quant_next": [_P, _P, _I64, _I64, _P, _P, _I64, _P, _P, _I32, _P, _I32,
+                                  _P, _P, _I32, _P, _P, _P, _P, _I64, _P],
 }
 
 
@@ -236,6 +239,21 @@ def svdq_pack_lowrank(l1, l2, K, N, rank, l1t, l2t, stream=None):
                                             _stream(stream)), "svdq_pack_lowrank")
 
 
+def svdq_gemm_w4a4_quant_next_workspace_size(M, N, rank_next) -> int:
+    out = ctypes.c_int64(0)
+    _check(load_library().svdq_gemm_w4a4_quant_next_workspace_size(M, N, rank_next, ctypes.byref(out)),
+           "svdq_gemm_w4a4_quant_next_workspace_size")
+    return out.value
+
+
+def svdq_gemm_w4a4_quant_next(qx, sx, M, K, qw, sw, N, xl1, l2t, rank, bias, act, inv_next, l1t_next,
+                              rank_next, qx_next, sx_next, xl1_next, workspace, workspace_bytes, stream=None):
+    _check(load_library().svdq_gemm_w4a4_quant_next(
+        _ptr(qx), _ptr(sx), M, K, _ptr(qw), _ptr(sw), N, _ptr(xl1), _ptr(l2t), rank, _ptr(bias), act,
+        _ptr(inv_next), _ptr(l1t_next), rank_next, _ptr(qx_next), _ptr(sx_next), _ptr(xl1_next),
+        _ptr(workspace), workspace_bytes, _stream(stream)), "svdq_gemm_w4a4_quant_next")
+
+
 # ---------------------------------------------------------------- tensor helpers
 # (allocate outputs with torch, then call the entry points above)
 
@@ -394,3 +412,41 @@ def mxfp4_linear(qx, sx, xl1, qw, sw, l2t, bias, rank: int, act: str = "none",
     svdq_gemm_mxfp4(qx, sx, M, K, qw, sw, N, xl1 if rank else None, l2t if rank else None, rank,
                     bias, ACT[act], y, y_dt, y.stride(0), stream)
     return y
+
+
+def w4a4_linear_quant_next(qx, sx, xl1, qw, sw, l2t, bias, rank: int, act: str, inv_next, l1t_next,
+                           rank_next: int, out=None, workspace=None, stream=None):
+    """The W4A4 layer whose bf16 output H = bf16(act(Y)) feeds the next
+    layer: instead of H, returns the next layer's activation-pass results
+    (qx_next uint8 [M, N/2], sx_next fp16 [ceil(N/256), M, 4], xl1_next fp32
+    [M, rank_next]), as svdq_quantize_act(H, inv_next, l1t_next, rank_next)
+    would. ``out`` may give those three tensors, ``workspace`` the partials
+    buffer (svdq_gemm_w4a4_quant_next_workspace_size bytes)."""
+    M, K, N = _check_gemm_inputs(qx, sx, xl1, qw, sw, l2t, bias, rank, None, 4, torch.float16)
+    _require(N % 128 == 0, f"N = {N} must be a multiple of 128")
+    _require(inv_next is not None and inv_next.dtype == torch.float32 and inv_next.numel() == N
+             and inv_next.is_contiguous(), f"inv_next must be a contiguous fp32 vector of N = {N} values")
+    if rank_next:
+        _require(l1t_next is not None and l1t_next.dtype == torch.bfloat16 and l1t_next.numel() == N * rank_next
+                 and l1t_next.is_contiguous(), f"l1t_next must hold {N} x {rank_next} bf16 values (tile layout)")
+    _check_same_device(qx, inv_next=inv_next, l1t_next=l1t_next if rank_next else None)
+    dev = qx.device
+    G4 = (N // 64 + 3) // 4
+    if out is None:
+        out = (torch.empty((M, N // 2), dtype=torch.uint8, device=dev),
+               torch.empty((G4, M, 4), dtype=torch.float16, device=dev),
+               torch.empty((M, rank_next), dtype=torch.float32, device=dev) if rank_next else None)
+    qn, sn, xn = out
+    _require(tuple(qn.shape) == (M, N // 2) and qn.dtype == torch.uint8 and qn.is_contiguous(), "qx_next shape")
+    _require(tuple(sn.shape) == (G4, M, 4) and sn.dtype == torch.float16 and sn.is_contiguous(), "sx_next shape")
+    if rank_next:
+        _require(xn is not None and tuple(xn.shape) == (M, rank_next) and xn.dtype == torch.float32
+                 and xn.is_contiguous(), "xl1_next shape")
+    nbytes = svdq_gemm_w4a4_quant_next_workspace_size(M, N, rank_next)
+    if workspace is None and nbytes:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    svdq_gemm_w4a4_quant_next(qx, sx, M, K, qw, sw, N, xl1 if rank else None, l2t if rank else None, rank,
+                              bias, ACT[act], inv_next, l1t_next if rank_next else None, rank_next, qn, sn,
+                              xn if rank_next else None, workspace, workspace.numel() if workspace is not None else 0,
+                              stream)
+    return qn, sn, xn

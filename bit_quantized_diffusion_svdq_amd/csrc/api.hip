@@ -48,6 +48,13 @@ hipError_t launch_quantize_residual(const double* w_hat, int64_t K, int64_t N, c
                                     const uint16_t* l2, int r, uint8_t* qw, uint16_t* sw, hipStream_t stream);
 hipError_t launch_pack_lowrank(const uint16_t* l1, const uint16_t* l2, int64_t K, int64_t N, int r, uint16_t* l1t,
                                uint16_t* l2t, hipStream_t stream);
+int64_t gemm_next_partial_bytes(int64_t M, int64_t N, int rank_next);
+hipError_t launch_gemm_w4a4_next(const uint8_t* qx, const uint16_t* sx, const uint8_t* qw,
+                                 const uint16_t* sw, const float* xl1, const uint16_t* l2t, int rank,
+                                 const uint16_t* bias, int act, int64_t M, int64_t N, int64_t K,
+                                 const float* inv_next, const uint16_t* l1t_next, int rank_next,
+                                 uint8_t* qx_next, uint16_t* sx_next, float* xl1_next, float* part,
+                                 hipStream_t stream);
 hipError_t launch_clock_probe(long long* out, int spins, hipStream_t stream);
 hipError_t launch_read_probe(const uint8_t* buf, int64_t bytes, uint32_t* sink, int blocks,
                              hipStream_t stream);
@@ -528,4 +535,68 @@ svdq_status svdq_pack_lowrank(const void* l1, const void* l2, int64_t K, int64_t
     return launched(launch_pack_lowrank((const uint16_t*)l1, (const uint16_t*)l2, K, N, rank, (uint16_t*)l1t,
                                         (uint16_t*)l2t, (hipStream_t)stream),
                     "svdq_pack_lowrank launch");
+}
+
+/* ------------------------------------------------------------------------ */
+/* GEMM with the next layer's activation pass in its epilogue                 */
+
+namespace {
+
+svdq_status check_next_shape(int64_t M, int64_t N, int32_t rank_next) {
+    if (M < 0) return fail(SVDQ_ERR_SHAPE, "M = %lld must be >= 0", (long long)M);
+    if (N <= 0 || N % 128) return fail(SVDQ_ERR_SHAPE, "N = %lld must be a positive multiple of 128 (whole tiles)", (long long)N);
+    if (rank_next < 0 || rank_next > 64 || rank_next % 16)
+        return fail(SVDQ_ERR_SHAPE, "rank_next %d must be a multiple of 16 in [0, 64]", rank_next);
+    if ((N / 128) * M * rank_next * 4 >= ((int64_t)1 << 40)) return fail(SVDQ_ERR_SHAPE, "partials too large");
+    return SVDQ_OK;
+}
+
+}  // namespace
+
+svdq_status svdq_gemm_w4a4_quant_next_workspace_size(int64_t M, int64_t N, int32_t rank_next, int64_t* bytes) {
+    svdq_status s;
+    if (!bytes) return fail(SVDQ_ERR_NULL, "bytes is required");
+    if ((s = check_next_shape(M, N, rank_next)) != SVDQ_OK) return s;
+    *bytes = gemm_next_partial_bytes(M, N, rank_next);
+    g_last_error.clear();
+    return SVDQ_OK;
+}
+
+svdq_status svdq_gemm_w4a4_quant_next(const uint8_t* qx, const void* sx_f16, int64_t M, int64_t K,
+                                      const uint8_t* qw, const void* sw_f16, int64_t N,
+                                      const float* xl1, const void* l2t, int32_t rank,
+                                      const void* bias, int32_t act,
+                                      const float* inv_lambda_next, const void* l1t_next, int32_t rank_next,
+                                      uint8_t* qx_next, void* sx_next_f16, float* xl1_next,
+                                      void* workspace, int64_t workspace_bytes, void* stream) {
+    svdq_status s;
+    if ((s = check_k(K)) != SVDQ_OK) return s;
+    if ((s = check_rank(rank)) != SVDQ_OK) return s;
+    if ((s = check_act(act)) != SVDQ_OK) return s;
+    if ((s = check_next_shape(M, N, rank_next)) != SVDQ_OK) return s;
+    if ((s = check_gemm_bytes(M, N, K)) != SVDQ_OK) return s;
+    if ((M + 256) * rank * 4 >= ((int64_t)1 << 31) || (N + 256) * rank * 2 >= ((int64_t)1 << 31))
+        return fail(SVDQ_ERR_SHAPE, "(M + 256) * rank * 4 and (N + 256) * rank * 2 must stay below 2^31 bytes");
+    if (M * (N / 2) >= ((int64_t)1 << 31) || rank_next * N * 2 >= ((int64_t)1 << 31))
+        return fail(SVDQ_ERR_SHAPE, "the next layer's codes or L1 exceed 2 GiB");
+    if (M == 0) { g_last_error.clear(); return SVDQ_OK; }
+    if (!qx || !sx_f16 || !qw || !sw_f16 || !inv_lambda_next || !qx_next || !sx_next_f16)
+        return fail(SVDQ_ERR_NULL, "qx, sx, qw, sw, inv_lambda_next, qx_next and sx_next are required");
+    if (rank > 0 && (!xl1 || !l2t)) return fail(SVDQ_ERR_NULL, "xl1 and l2t are required when rank > 0");
+    if (rank_next > 0 && (!l1t_next || !xl1_next || !workspace))
+        return fail(SVDQ_ERR_NULL, "l1t_next, xl1_next and workspace are required when rank_next > 0");
+    if (rank_next > 0 && workspace_bytes < gemm_next_partial_bytes(M, N, rank_next))
+        return fail(SVDQ_ERR_SHAPE, "workspace of %lld bytes, %lld needed", (long long)workspace_bytes,
+                    (long long)gemm_next_partial_bytes(M, N, rank_next));
+    if (!aligned(qx, 16) || !aligned(qw, 16) || !aligned(sx_f16, 16) || !aligned(sw_f16, 16) ||
+        (xl1 && !aligned(xl1, 16)) || (l2t && !aligned(l2t, 16)) || (bias && !aligned(bias, 2)) ||
+        !aligned(inv_lambda_next, 16) || (l1t_next && !aligned(l1t_next, 16)) || !aligned(qx_next, 16) ||
+        !aligned(sx_next_f16, 2) || (xl1_next && !aligned(xl1_next, 4)) || (workspace && !aligned(workspace, 16)))
+        return fail(SVDQ_ERR_ALIGN, "vector operands need 16-byte alignment (sx_next and bias 2, xl1_next 4)");
+    if ((s = check_current_device()) != SVDQ_OK) return s;
+    return launched(launch_gemm_w4a4_next(qx, (const uint16_t*)sx_f16, qw, (const uint16_t*)sw_f16, xl1,
+                                          (const uint16_t*)l2t, rank, (const uint16_t*)bias, act, M, N, K,
+                                          inv_lambda_next, (const uint16_t*)l1t_next, rank_next, qx_next,
+                                          (uint16_t*)sx_next_f16, xl1_next, (float*)workspace, (hipStream_t)stream),
+                    "svdq_gemm_w4a4_quant_next launch");
 }

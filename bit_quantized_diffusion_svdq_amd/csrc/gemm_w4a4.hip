@@ -35,6 +35,7 @@
 //    the fp32 xl1); bias and GELU run in fp32 before the single rounding of
 //    the output, which is stored straight from the MFMA layout.
 #include "common.h"
+#include "int4_fields.h"
 
 namespace {
 
@@ -108,7 +109,23 @@ DEV v6i unfold_frag(const uint4& raw) {
     return v6i{(int)d[0], (int)d[1], (int)d[2], (int)d[3], (int)d[4], (int)d[5]};
 }
 
-// MODE 0: bf16 out, 1: fp32 out, 2: integer partials dump (INT4 only).
+// The next layer's activation pass, done by MODE 3 on this layer's output
+// H = bf16(act(Y)) (which is not stored): smoothing multiplier inv [N],
+// its down-projection L1 [N][rank] in the tile layout of the activation
+// kernel (format v4) lt, codes qx [M][N/2]
+// (format v2) and scales sx (format v3) of H * inv, and per 128-column
+// tile of H the partial down-projection part [N/128][M][rank] (fp32).
+struct NextAct {
+    const float* inv;
+    const uint16_t* lt;
+    int rank;
+    uint8_t* qx;
+    uint16_t* sx;
+    float* part;
+};
+
+// MODE 0: bf16 out, 1: fp32 out, 2: integer partials dump (INT4 only),
+// 3: the next layer's activation pass on the bf16 output (INT4 only).
 // FMT 0: INT4 g64 with fp16 scales; 1: MXFP4 (E2M1 codes, E8M0 per 32).
 template <class C, int MODE, int ACT, int FMT = 0>
 __global__ __launch_bounds__(C::NT, C::MINB) void gemm_w4a4_kernel(
@@ -117,8 +134,9 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_w4a4_kernel(
     const float* __restrict__ xl1, const uint16_t* __restrict__ l2t, int rank,
     const uint16_t* __restrict__ bias,
     void* __restrict__ y, int64_t ldy, int64_t M, int64_t N, int64_t K,
-    int64_t pm0, int64_t pmc, int64_t pn0, int64_t pnc, int32_t* __restrict__ part)
+    int64_t pm0, int64_t pmc, int64_t pn0, int64_t pnc, int32_t* __restrict__ part, NextAct nx)
 {
+    static_assert(MODE != 3 || FMT == 0, "the fused next-layer pass is INT4 only");
     constexpr int BM = C::BM, BN = C::BN, TM = C::TM, TN = C::TN, NT = C::NT;
     // two quad slots of codes and two of scales, all separate objects: the
     // compiler then tracks each one's outstanding LDS-destination loads on
@@ -473,6 +491,152 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_w4a4_kernel(
         publish();
         group(g0 + 3, 3, par, ncs, nss, 0, cs, ss, q + 2, 0, tail ? 0 : DSPLIT, tail == 1);
     };
+    // ---- MODE 3: the next layer's activation pass on this tile's output --------
+    // H = bf16(act(Y + bias)) of the tile goes row-major into code slot 1
+    // (each wave its 64 x 64 block, the 16-byte chunks of row r XOR-swizzled
+    // by r % 8). Then lane l owns row l of its wave's block, whose 64 columns
+    // are exactly one group of the next layer's K: x = f32(h) * inv, the
+    // group maximum, scale and codes are the lane's own (the same steps as
+    // the activation kernel), and the 64 codes leave as four stored words.
+    // The next layer's down-projection of these 64 columns runs on the bf16
+    // MFMA (x split into bf16 hi + lo) as D[j][row] = L1^T[j][k] x[row][k];
+    // the B operand wants lanes l and l + 32 to hold the two 8-column halves
+    // of one row, so half of each lane's packs trade places with lane l ^ 32.
+    // The two waves of a tile row (wn = 0, 1) hold the tile's two 64-column
+    // halves: wn = 1 hands its D to wn = 0 through code slot 0 and wn = 0
+    // stores the sum (its half first) as the tile's partial.
+    auto next_act = [&](int64_t tm0, int64_t tn0, const float (&bv)[TN]) __attribute__((always_inline)) {
+        char* stg = cs1 + wave * 8192;
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    float v = acc[i][j][e] + bv[j];
+                    if constexpr (ACT == 1) v = gelu_tanh_f32(v);
+                    const int lr = i * 32 + out_row(e, lane), lc = j * 32 + (lane & 31);
+                    *(uint16_t*)(stg + lr * 128 + (((lc >> 3) ^ (lr & 7)) << 4) + (lc & 7) * 2) = f32_to_bf16_bits(v);
+                }
+        const int64_t col0 = tn0 + wn * 64;                 // the lane's group of the next layer
+        const int64_t row = tm0 + wm * 64 + lane;
+        const int g2 = (int)(col0 >> 6);
+        float xh[64];
+        float amax = 0.0f;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            const uint4 hv = *(const uint4*)(stg + lane * 128 + ((c ^ (lane & 7)) << 4));
+            const float4 i0 = *(const float4*)(nx.inv + col0 + 8 * c);
+            const float4 i1 = *(const float4*)(nx.inv + col0 + 8 * c + 4);
+            const float iv[8] = {i0.x, i0.y, i0.z, i0.w, i1.x, i1.y, i1.z, i1.w};
+            const uint32_t hw[4] = {hv.x, hv.y, hv.z, hv.w};
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const float h = (k & 1) ? bf16_hi_to_f32(hw[k >> 1]) : bf16_lo_to_f32(hw[k >> 1]);
+                xh[8 * c + k] = h * iv[k];
+                amax = fmaxf(amax, fabsf(xh[8 * c + k]));
+            }
+        }
+        {
+            const float s32 = fminf(amax / 7.0f, 65504.0f);
+            const _Float16 s16 = (_Float16)s32;
+            const float sf = (float)s16;
+            const float invs = (sf > 0.0f) ? 1.0f / sf : 0.0f;
+            uint2 wd[4];
+#pragma unroll
+            for (int w4 = 0; w4 < 4; ++w4) {
+                uint32_t f[16];
+#pragma unroll
+                for (int k = 0; k < 16; ++k) f[k] = code_field(xh[16 * w4 + k], invs);
+                wd[w4] = fold_fields(f);
+            }
+            // rows past M fall outside the buffer ranges and are dropped
+            const rsrc_t rq = make_rsrc(nx.qx, M * (N / 2));
+            const int qo = (int)(row * (N / 2) + col0 / 2);
+            __builtin_amdgcn_raw_buffer_store_b128(v4i{(int)wd[0].x, (int)wd[0].y, (int)wd[1].x, (int)wd[1].y},
+                                                  rq, qo, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b128(v4i{(int)wd[2].x, (int)wd[2].y, (int)wd[3].x, (int)wd[3].y},
+                                                  rq, qo + 16, 0, 0);
+            // (the scale array's rows past M belong to the next quad: masked)
+            if (row < M) nx.sx[((int64_t)(g2 >> 2) * M + row) * 4 + (g2 & 3)] = __builtin_bit_cast(uint16_t, s16);
+        }
+        // the B operand packs: step s covers columns 16 s .. 16 s + 15
+        v8bf bh[2][4], bl[2][4];            // [block of 32 rows][step]
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+            v8bf oh_lo, ol_lo, oh_hi, ol_hi;          // own row, columns 16 s + 0..7 / 8..15
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const __bf16 a = (__bf16)xh[16 * st + k], b = (__bf16)xh[16 * st + 8 + k];
+                oh_lo[k] = a;
+                ol_lo[k] = (__bf16)(xh[16 * st + k] - (float)a);
+                oh_hi[k] = b;
+                ol_hi[k] = (__bf16)(xh[16 * st + 8 + k] - (float)b);
+            }
+            // lanes < 32 send their upper halves, lanes >= 32 their lower ones
+            const bool lowlane = lane < 32;
+            uint4 sh = __builtin_bit_cast(uint4, lowlane ? oh_hi : oh_lo);
+            uint4 sl = __builtin_bit_cast(uint4, lowlane ? ol_hi : ol_lo);
+            uint4 rh, rl;
+            rh.x = __shfl_xor(sh.x, 32); rh.y = __shfl_xor(sh.y, 32); rh.z = __shfl_xor(sh.z, 32); rh.w = __shfl_xor(sh.w, 32);
+            rl.x = __shfl_xor(sl.x, 32); rl.y = __shfl_xor(sl.y, 32); rl.z = __shfl_xor(sl.z, 32); rl.w = __shfl_xor(sl.w, 32);
+            const v8bf gh = __builtin_bit_cast(v8bf, rh), gl = __builtin_bit_cast(v8bf, rl);
+            bh[0][st] = lowlane ? oh_lo : gh;           // rows 0..31 of the block
+            bl[0][st] = lowlane ? ol_lo : gl;
+            bh[1][st] = lowlane ? gh : oh_hi;           // rows 32..63
+            bl[1][st] = lowlane ? gl : ol_hi;
+        }
+        const int r2 = nx.rank;
+        const rsrc_t rlt = make_rsrc(nx.lt, (int64_t)r2 * N * 2);
+        const int lt_half = lane >> 5;
+        char* xch = cs0 + wm * 16384;                 // wn = 1's D for wn = 0, per tile row
+        float* pp = nx.part + ((tn0 / 128) * M) * (int64_t)r2;
+        for (int jb = 0; jb < r2; jb += 32) {
+            v16f d[2] = {zero, zero};
+#pragma unroll
+            for (int st = 0; st < 4; ++st) {
+                // A: L1[col0 + 16 st + 8 (l / 32) + 0..7][jr], jr = jb + l % 32,
+                // one 16-byte chunk of the tile layout (group g2, 16-rank
+                // tile jr / 16, step l / 32, tile lane 16 st + jr % 16);
+                // ranks past r2 are zero
+                const int jr = jb + (lane & 31);
+                const int64_t chunk = (((int64_t)g2 * (r2 / 16) + (jr >> 4)) * 2 + lt_half) * 64 + 16 * st + (jr & 15);
+                uint4 araw = make_uint4(0u, 0u, 0u, 0u);
+                if (jr < r2) araw = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rlt, (int)(chunk * 16), 0, 0));
+                const v8bf a = __builtin_bit_cast(v8bf, araw);
+#pragma unroll
+                for (int mb = 0; mb < 2; ++mb) {
+                    d[mb] = mfma_bf16_32x32x16(a, bh[mb][st], d[mb]);
+                    d[mb] = mfma_bf16_32x32x16(a, bl[mb][st], d[mb]);
+                }
+            }
+            if (wn == 1) {
+#pragma unroll
+                for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        *(float4*)(xch + ((mb * 4 + q) * 64 + lane) * 16) =
+                            make_float4(d[mb][4 * q], d[mb][4 * q + 1], d[mb][4 * q + 2], d[mb][4 * q + 3]);
+            }
+            lds_barrier();
+            if (wn == 0) {
+#pragma unroll
+                for (int mb = 0; mb < 2; ++mb) {
+                    const int64_t prow = tm0 + wm * 64 + mb * 32 + (lane & 31);
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const float4 o = *(const float4*)(xch + ((mb * 4 + q) * 64 + lane) * 16);
+                        const int j = jb + 8 * q + 4 * (lane >> 5);
+                        if (prow < M && j < r2)
+                            *(float4*)(pp + prow * r2 + j) = make_float4(d[mb][4 * q] + o.x, d[mb][4 * q + 1] + o.y,
+                                                                       d[mb][4 * q + 2] + o.z, d[mb][4 * q + 3] + o.w);
+                    }
+                }
+            }
+            lds_barrier();       // slot 0 is free again before the next chunk or tile loads into it
+        }
+    };
+
     // ---- the tiles of this workgroup ----------------------------------------
     int t = blockIdx.x;
     start_tile(t);
@@ -608,6 +772,9 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_w4a4_kernel(
                 }
             }
             if (more) start_tile(t + (int)gridDim.x);
+        } else if constexpr (MODE == 3) {
+            next_act(em0, en0, bvj);
+            if (more) start_tile(t + (int)gridDim.x);
         } else {
             if (more) start_tile(t + (int)gridDim.x);
         }
@@ -634,7 +801,8 @@ template <class C, int MODE, int ACT, int FMT = 0>
 void launch_mode(hipStream_t stream, const uint8_t* qx, const uint16_t* sx,
                  const uint8_t* qw, const uint16_t* sw, const float* xl1, const uint16_t* l2t,
                  int rank, const uint16_t* bias, void* y, int64_t ldy, int64_t M, int64_t N,
-                 int64_t K, int64_t pm0, int64_t pmc, int64_t pn0, int64_t pnc, int32_t* p) {
+                 int64_t K, int64_t pm0, int64_t pmc, int64_t pn0, int64_t pnc, int32_t* p,
+                 NextAct nx = NextAct{nullptr, nullptr, 0, nullptr, nullptr, nullptr}) {
     const int64_t mext = (MODE == 2) ? pmc : M, next = (MODE == 2) ? pnc : N;
     const int64_t tiles = ((next + C::BN - 1) / C::BN) * ((mext + C::BM - 1) / C::BM);
     // persistent workgroups: MINB per CU
@@ -642,7 +810,7 @@ void launch_mode(hipStream_t stream, const uint8_t* qx, const uint16_t* sx,
     const int64_t grid = tiles < slots ? tiles : slots;
     hipLaunchKernelGGL((gemm_w4a4_kernel<C, MODE, ACT, FMT>), dim3((unsigned)grid), dim3(C::NT),
                        0, stream, qx, sx, qw, sw, xl1, l2t, rank, bias, y, ldy, M, N, K,
-                       pm0, pmc, pn0, pnc, p);
+                       pm0, pmc, pn0, pnc, p, nx);
 }
 
 }  // namespace
@@ -687,5 +855,40 @@ hipError_t launch_gemm_w4a4_partials(const uint8_t* qx, const uint8_t* qw, int64
 {
     launch_mode<MainCfg, 2, 0>(stream, qx, nullptr, qw, nullptr, nullptr, nullptr, 0, nullptr,
                                nullptr, 0, M, N, K, m0, mc, n0, nc, p);
+    return hipGetLastError();
+}
+
+namespace {
+
+// xl1[m][j] = sum over the 128-column tiles t = 0, 1, ... of part[t][m][j]
+__global__ void sum_tile_partials_kernel(const float* __restrict__ part, int T, int64_t M, int r,
+                                         float* __restrict__ xl1) {
+    const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (e >= M * r) return;
+    float v = 0.0f;
+    for (int t = 0; t < T; ++t) v += part[(int64_t)t * M * r + e];
+    xl1[e] = v;
+}
+
+}  // namespace
+
+int64_t gemm_next_partial_bytes(int64_t M, int64_t N, int rank_next) { return (N / 128) * M * rank_next * 4; }
+
+hipError_t launch_gemm_w4a4_next(const uint8_t* qx, const uint16_t* sx, const uint8_t* qw,
+                                 const uint16_t* sw, const float* xl1, const uint16_t* l2t, int rank,
+                                 const uint16_t* bias, int act, int64_t M, int64_t N, int64_t K,
+                                 const float* inv_next, const uint16_t* l1t_next, int rank_next,
+                                 uint8_t* qx_next, uint16_t* sx_next, float* xl1_next, float* part,
+                                 hipStream_t stream)
+{
+    using C = MainCfg;
+    const NextAct nx{inv_next, l1t_next, rank_next, qx_next, sx_next, part};
+    if (act) launch_mode<C, 3, 1>(stream, qx, sx, qw, sw, xl1, l2t, rank, bias, nullptr, 0, M, N, K, 0, 0, 0, 0, nullptr, nx);
+    else launch_mode<C, 3, 0>(stream, qx, sx, qw, sw, xl1, l2t, rank, bias, nullptr, 0, M, N, K, 0, 0, 0, 0, nullptr, nx);
+    if (rank_next > 0) {
+        const int64_t n = M * rank_next;
+        hipLaunchKernelGGL(sum_tile_partials_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, part,
+                           (int)(N / 128), M, rank_next, xl1_next);
+    }
     return hipGetLastError();
 }

@@ -308,6 +308,42 @@ svdq_status awq_gemv_w4a16(const void* x, int64_t M, int64_t K, const float* inv
 svdq_status svdq_probe_clock(int64_t* ticks, int32_t spins, void* stream);
 svdq_status svdq_probe_read(const void* buf, int64_t bytes, uint32_t* sink, int32_t blocks, void* stream);
 
+/* svdq_gemm_w4a4_quant_next -- svdq_gemm_w4a4 whose output is not stored
+ * but quantised for the next layer in the same kernel: H = bf16(act(Y))
+ * (act as for svdq_gemm_w4a4; the GELU of an MLP's first linear) is the
+ * next layer's input, and the epilogue runs that layer's activation pass
+ * on it, with results identical to svdq_quantize_act(H, inv_lambda_next,
+ * l1t_next, rank_next) up to the summation order of xl1_next. This is the
+ * fusion the remio.ai page names for the original engine (section on
+ * SVDQuant moving hard values out of 4-bit: the down-projection fused into
+ * input quantisation, so the 16-bit branch adds no separate pass), taken
+ * one step further: the 16-bit H of an MLP (113 MB at 4608 x 12288) never
+ * goes to memory. The donmalab.com page (section on squeezing out more
+ * performance) credits removing such overhead with most of the gain.
+ *
+ *  this layer   qx, sx_f16, M, K, qw, sw_f16, N, xl1, l2t, rank, bias, act:
+ *               as svdq_gemm_w4a4; N a multiple of 128 (whole tiles).
+ *  next layer   inv_lambda_next fp32 [N] (16-byte aligned; its input
+ *               channels are this layer's outputs), l1t_next its L1 in the
+ *               tile layout (format v4, K = N), rank_next a multiple of 16
+ *               in [0, 64].
+ *  outputs      qx_next [M][N/2] (format v2), sx_next [ceil(N/256)][M][4]
+ *               fp16 (format v3, the padding groups of a last partial quad
+ *               are not written), xl1_next fp32 [M][rank_next].
+ *  workspace    svdq_gemm_w4a4_quant_next_workspace_size() bytes (16-byte
+ *               aligned, contents irrelevant): every 128-column tile's
+ *               share of xl1_next, summed afterwards in tile order (so the
+ *               result is deterministic). Calls sharing it must not overlap.
+ */
+svdq_status svdq_gemm_w4a4_quant_next_workspace_size(int64_t M, int64_t N, int32_t rank_next, int64_t* bytes);
+svdq_status svdq_gemm_w4a4_quant_next(const uint8_t* qx, const void* sx_f16, int64_t M, int64_t K,
+                                      const uint8_t* qw, const void* sw_f16, int64_t N,
+                                      const float* xl1, const void* l2t, int32_t rank,
+                                      const void* bias, int32_t act,
+                                      const float* inv_lambda_next, const void* l1t_next, int32_t rank_next,
+                                      uint8_t* qx_next, void* sx_next_f16, float* xl1_next,
+                                      void* workspace, int64_t workspace_bytes, void* stream);
+
 /* ------------------------------------------------------------------------
  * Offline quantiser: turning a bf16 weight into the arrays above, on the
  * GPU. This is the Quantize step of the tool chain the donmalab.com page
