@@ -188,6 +188,37 @@ def gemm_traffic_bytes():
     return int(round(1024 * (t["fetch_kib"] * t["fetch_factor"] + t["write_kib"] * t["write_factor"])))
 
 
+def offline_quantize_timing(lib, dev, reps=5):
+    """The GPU offline quantiser on the QKV weight (3072 x 9216, bf16) with a
+    4096-token calibration batch: calibration maxima, smoothing, W_hat, the
+    rank-32 range finder (4 power iterations) and residual packing. Time per
+    layer by HIP events around quantize_layer (its host work included)."""
+    import statistics
+
+    import numpy as np
+    import torch
+
+    import synth
+    li = synth.make_layer(synth.CONFIGS["qkv"])
+    bf = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+    w, x = bf(li.w), bf(li.x)
+    l = min(32 + 16, 3072)
+    omega = torch.from_numpy(np.random.default_rng(0).standard_normal((9216, l))).to(dev)
+    run = lambda: lib.quantize_layer(w, x, 32, omega=omega)
+    run()
+    torch.cuda.synchronize()
+    ms = []
+    for _ in range(reps):
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        run()
+        e.record()
+        e.synchronize()
+        ms.append(s.elapsed_time(e))
+    return {"median_ms": round(statistics.median(ms), 3), "min_ms": round(min(ms), 3),
+            "reps_ms": [round(v, 3) for v in ms]}
+
+
 def mxfp4_block(lib, dev, iters=50):
     """The MXFP4 form on a transformer block's four linears at 4608 tokens
     (4096 image + 512 text): QKV 3072->9216, out 3072->3072, fc1 3072->12288
@@ -522,7 +553,28 @@ def main():
         extra.update({"mlp_pair": summary_us(mlp_ms),
                       "mlp_pair_TOPS": round(mlp_flops / (mm * 1e-3) / 1e12, 1)})
         log(f"gemv {gmed * 1e3:.2f} us (read floor {fmed * 1e3:.2f}), mlp pair {mm * 1e3:.1f} us")
-        del fc1, fc2, h, y2
+        # the same MLP with fc2's activation pass fused into fc1's epilogue
+        # (the bf16 hidden state never stored), eager and as one graph; and
+        # the unfused pair as a graph
+        from bit_quantized_diffusion_svdq_amd import SvdqLinear, SvdqMLP
+        lin = lambda o: SvdqLinear(o["inv_lambda"], o["l1t"], o["l2t"], o["qw"], o["sw"], o["bias"], 32)
+        blk = SvdqMLP(lin(fc1), lin(fc2), Mm)
+        blk.x.copy_(fc1["x"])
+        fused = lambda: blk.forward(blk.x)
+        for _ in range(5):
+            fused()
+        fused_ms, _ = time_reps(fused, 20, 5)
+        fused_graph = [time_graph(blk._launches, 10) for _ in range(5)]
+        pair_graph = [time_graph(mlp, 10) for _ in range(5)]
+        fm = statistics.median(fused_ms)
+        extra.update({"mlp_fused": summary_us(fused_ms), "mlp_fused_graph": summary_us(fused_graph),
+                      "mlp_pair_graph": summary_us(pair_graph),
+                      "mlp_fused_TOPS": round(mlp_flops / (fm * 1e-3) / 1e12, 1)})
+        log(f"mlp fused {fm * 1e3:.1f} us (graph {statistics.median(fused_graph) * 1e3:.1f}, "
+            f"unfused graph {statistics.median(pair_graph) * 1e3:.1f})")
+        del fc1, fc2, h, y2, blk
+        extra["offline_quantize_qkv"] = offline_quantize_timing(lib, dev)
+        log(f"offline quantiser, QKV layer: {extra['offline_quantize_qkv']['median_ms']} ms")
         extra["mxfp4_block"] = mxfp4_block(lib, dev)
         log(f"mxfp4 block {extra['mxfp4_block']['block_us']} us")
 

@@ -591,8 +591,8 @@ svdq_status svdq_gemm_w4a4_quant_next(const uint8_t* qx, const void* sx_f16, int
     if (!aligned(qx, 16) || !aligned(qw, 16) || !aligned(sx_f16, 16) || !aligned(sw_f16, 16) ||
         (xl1 && !aligned(xl1, 16)) || (l2t && !aligned(l2t, 16)) || (bias && !aligned(bias, 2)) ||
         !aligned(inv_lambda_next, 16) || (l1t_next && !aligned(l1t_next, 16)) || !aligned(qx_next, 16) ||
-        !aligned(sx_next_f16, 2) || (xl1_next && !aligned(xl1_next, 4)) || (workspace && !aligned(workspace, 16)))
-        return fail(SVDQ_ERR_ALIGN, "vector operands need 16-byte alignment (sx_next and bias 2, xl1_next 4)");
+        !aligned(sx_next_f16, 2) || (xl1_next && !aligned(xl1_next, 16)) || (workspace && !aligned(workspace, 16)))
+        return fail(SVDQ_ERR_ALIGN, "vector operands need 16-byte alignment (sx_next and bias 2)");
     if ((s = check_current_device()) != SVDQ_OK) return s;
     return launched(launch_gemm_w4a4_next(qx, (const uint16_t*)sx_f16, qw, (const uint16_t*)sw_f16, xl1,
                                           (const uint16_t*)l2t, rank, (const uint16_t*)bias, act, M, N, K,

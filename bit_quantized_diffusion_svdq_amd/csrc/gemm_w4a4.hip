@@ -503,8 +503,10 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_w4a4_kernel(
     // the B operand wants lanes l and l + 32 to hold the two 8-column halves
     // of one row, so half of each lane's packs trade places with lane l ^ 32.
     // The two waves of a tile row (wn = 0, 1) hold the tile's two 64-column
-    // halves: wn = 1 hands its D to wn = 0 through code slot 0 and wn = 0
-    // stores the sum (its half first) as the tile's partial.
+    // halves: wn = 1 hands its D to wn = 0 through LDS and wn = 0 stores
+    // the sum (its half first) as the tile's partial. (Issuing the next
+    // tile's first loads before this work measured no faster, and its
+    // registers no longer fit.)
     auto next_act = [&](int64_t tm0, int64_t tn0, const float (&bv)[TN]) __attribute__((always_inline)) {
         char* stg = cs1 + wave * 8192;
 #pragma unroll
@@ -560,41 +562,44 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_w4a4_kernel(
             // (the scale array's rows past M belong to the next quad: masked)
             if (row < M) nx.sx[((int64_t)(g2 >> 2) * M + row) * 4 + (g2 & 3)] = __builtin_bit_cast(uint16_t, s16);
         }
-        // the B operand packs: step s covers columns 16 s .. 16 s + 15
-        v8bf bh[2][4], bl[2][4];            // [block of 32 rows][step]
-#pragma unroll
-        for (int st = 0; st < 4; ++st) {
-            v8bf oh_lo, ol_lo, oh_hi, ol_hi;          // own row, columns 16 s + 0..7 / 8..15
-#pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                const __bf16 a = (__bf16)xh[16 * st + k], b = (__bf16)xh[16 * st + 8 + k];
-                oh_lo[k] = a;
-                ol_lo[k] = (__bf16)(xh[16 * st + k] - (float)a);
-                oh_hi[k] = b;
-                ol_hi[k] = (__bf16)(xh[16 * st + 8 + k] - (float)b);
-            }
-            // lanes < 32 send their upper halves, lanes >= 32 their lower ones
-            const bool lowlane = lane < 32;
-            uint4 sh = __builtin_bit_cast(uint4, lowlane ? oh_hi : oh_lo);
-            uint4 sl = __builtin_bit_cast(uint4, lowlane ? ol_hi : ol_lo);
-            uint4 rh, rl;
-            rh.x = __shfl_xor(sh.x, 32); rh.y = __shfl_xor(sh.y, 32); rh.z = __shfl_xor(sh.z, 32); rh.w = __shfl_xor(sh.w, 32);
-            rl.x = __shfl_xor(sl.x, 32); rl.y = __shfl_xor(sl.y, 32); rl.z = __shfl_xor(sl.z, 32); rl.w = __shfl_xor(sl.w, 32);
-            const v8bf gh = __builtin_bit_cast(v8bf, rh), gl = __builtin_bit_cast(v8bf, rl);
-            bh[0][st] = lowlane ? oh_lo : gh;           // rows 0..31 of the block
-            bl[0][st] = lowlane ? ol_lo : gl;
-            bh[1][st] = lowlane ? gh : oh_hi;           // rows 32..63
-            bl[1][st] = lowlane ? gl : ol_hi;
-        }
         const int r2 = nx.rank;
         const rsrc_t rlt = make_rsrc(nx.lt, (int64_t)r2 * N * 2);
         const int lt_half = lane >> 5;
-        char* xch = cs0 + wm * 16384;                 // wn = 1's D for wn = 0, per tile row
+        // wn = 1 hands its D over in its own staging block (it has read its
+        // rows of H already: a wave's LDS operations complete in order)
+        char* xch = cs1 + (wm * C::WGN + 1) * 8192;
         float* pp = nx.part + ((tn0 / 128) * M) * (int64_t)r2;
         for (int jb = 0; jb < r2; jb += 32) {
             v16f d[2] = {zero, zero};
 #pragma unroll
             for (int st = 0; st < 4; ++st) {
+                // B: x of step st (columns 16 st .. 16 st + 15) as bf16 hi and
+                // lo packs of 8 columns; lane l and lane l ^ 32 trade halves
+                // so that the 32-row block mb has rows l % 32 + 32 mb with
+                // columns 8 (l / 32) + 0..7 of the step
+                v8bf bh[2], bl[2];
+                {
+                    v8bf oh_lo, ol_lo, oh_hi, ol_hi;          // own row, columns + 0..7 / + 8..15
+#pragma unroll
+                    for (int k = 0; k < 8; ++k) {
+                        const __bf16 a0 = (__bf16)xh[16 * st + k], b0 = (__bf16)xh[16 * st + 8 + k];
+                        oh_lo[k] = a0;
+                        ol_lo[k] = (__bf16)(xh[16 * st + k] - (float)a0);
+                        oh_hi[k] = b0;
+                        ol_hi[k] = (__bf16)(xh[16 * st + 8 + k] - (float)b0);
+                    }
+                    const bool lowlane = lane < 32;          // sends its upper half, keeps its lower
+                    const uint4 sh = __builtin_bit_cast(uint4, lowlane ? oh_hi : oh_lo);
+                    const uint4 sl = __builtin_bit_cast(uint4, lowlane ? ol_hi : ol_lo);
+                    uint4 rh, rl;
+                    rh.x = __shfl_xor(sh.x, 32); rh.y = __shfl_xor(sh.y, 32); rh.z = __shfl_xor(sh.z, 32); rh.w = __shfl_xor(sh.w, 32);
+                    rl.x = __shfl_xor(sl.x, 32); rl.y = __shfl_xor(sl.y, 32); rl.z = __shfl_xor(sl.z, 32); rl.w = __shfl_xor(sl.w, 32);
+                    const v8bf gh = __builtin_bit_cast(v8bf, rh), gl = __builtin_bit_cast(v8bf, rl);
+                    bh[0] = lowlane ? oh_lo : gh;
+                    bl[0] = lowlane ? ol_lo : gl;
+                    bh[1] = lowlane ? gh : oh_hi;
+                    bl[1] = lowlane ? gl : ol_hi;
+                }
                 // A: L1[col0 + 16 st + 8 (l / 32) + 0..7][jr], jr = jb + l % 32,
                 // one 16-byte chunk of the tile layout (group g2, 16-rank
                 // tile jr / 16, step l / 32, tile lane 16 st + jr % 16);
@@ -606,8 +611,8 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_w4a4_kernel(
                 const v8bf a = __builtin_bit_cast(v8bf, araw);
 #pragma unroll
                 for (int mb = 0; mb < 2; ++mb) {
-                    d[mb] = mfma_bf16_32x32x16(a, bh[mb][st], d[mb]);
-                    d[mb] = mfma_bf16_32x32x16(a, bl[mb][st], d[mb]);
+                    d[mb] = mfma_bf16_32x32x16(a, bh[mb], d[mb]);
+                    d[mb] = mfma_bf16_32x32x16(a, bl[mb], d[mb]);
                 }
             }
             if (wn == 1) {
@@ -633,7 +638,7 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_w4a4_kernel(
                     }
                 }
             }
-            lds_barrier();       // slot 0 is free again before the next chunk or tile loads into it
+            lds_barrier();       // the hand-over block is free again for the next chunk
         }
     };
 
@@ -860,14 +865,41 @@ hipError_t launch_gemm_w4a4_partials(const uint8_t* qx, const uint8_t* qw, int64
 
 namespace {
 
-// xl1[m][j] = sum over the 128-column tiles t = 0, 1, ... of part[t][m][j]
-__global__ void sum_tile_partials_kernel(const float* __restrict__ part, int T, int64_t M, int r,
-                                         float* __restrict__ xl1) {
-    const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (e >= M * r) return;
-    float v = 0.0f;
-    for (int t = 0; t < T; ++t) v += part[(int64_t)t * M * r + e];
-    xl1[e] = v;
+// xl1[m][j] = the sum of part[t][m][j] over the 128-column tiles t, in a
+// fixed order: the tiles split into four consecutive ranges, each summed in
+// tile order by its own thread (8 loads of 16 bytes in flight), and the four
+// range sums added first to last. A workgroup covers 64 groups of four
+// consecutive elements (M r is a multiple of 16).
+__global__ __launch_bounds__(256) void sum_tile_partials_kernel(const float* __restrict__ part, int T, int64_t n4,
+                                                                float* __restrict__ xl1) {
+    __shared__ float4 red[4][64];
+    const int c = threadIdx.x >> 6, gl = threadIdx.x & 63;
+    const int64_t g = (int64_t)blockIdx.x * 64 + gl;
+    const int t0 = c * T / 4, t1 = (c + 1) * T / 4;
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (g < n4) {
+        const float4* p = (const float4*)part + g;
+        int t = t0;
+        for (; t + 8 <= t1; t += 8) {
+            float4 b[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) b[u] = p[(int64_t)(t + u) * n4];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) { v.x += b[u].x; v.y += b[u].y; v.z += b[u].z; v.w += b[u].w; }
+        }
+        for (; t < t1; ++t) {
+            const float4 b = p[(int64_t)t * n4];
+            v.x += b.x; v.y += b.y; v.z += b.z; v.w += b.w;
+        }
+    }
+    red[c][gl] = v;
+    __syncthreads();
+    if (c == 0 && g < n4) {
+        float4 r = red[0][gl];
+#pragma unroll
+        for (int k = 1; k < 4; ++k) { r.x += red[k][gl].x; r.y += red[k][gl].y; r.z += red[k][gl].z; r.w += red[k][gl].w; }
+        ((float4*)xl1)[g] = r;
+    }
 }
 
 }  // namespace
@@ -886,9 +918,9 @@ hipError_t launch_gemm_w4a4_next(const uint8_t* qx, const uint16_t* sx, const ui
     if (act) launch_mode<C, 3, 1>(stream, qx, sx, qw, sw, xl1, l2t, rank, bias, nullptr, 0, M, N, K, 0, 0, 0, 0, nullptr, nx);
     else launch_mode<C, 3, 0>(stream, qx, sx, qw, sw, xl1, l2t, rank, bias, nullptr, 0, M, N, K, 0, 0, 0, 0, nullptr, nx);
     if (rank_next > 0) {
-        const int64_t n = M * rank_next;
-        hipLaunchKernelGGL(sum_tile_partials_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, part,
-                           (int)(N / 128), M, rank_next, xl1_next);
+        const int64_t n4 = M * rank_next / 4;
+        hipLaunchKernelGGL(sum_tile_partials_kernel, dim3((unsigned)((n4 + 63) / 64)), dim3(256), 0, stream, part,
+                           (int)(N / 128), n4, xl1_next);
     }
     return hipGetLastError();
 }

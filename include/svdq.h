@@ -329,7 +329,8 @@ svdq_status svdq_probe_read(const void* buf, int64_t bytes, uint32_t* sink, int3
  *               in [0, 64].
  *  outputs      qx_next [M][N/2] (format v2), sx_next [ceil(N/256)][M][4]
  *               fp16 (format v3, the padding groups of a last partial quad
- *               are not written), xl1_next fp32 [M][rank_next].
+ *               are not written), xl1_next fp32 [M][rank_next] (16-byte
+ *               aligned).
  *  workspace    svdq_gemm_w4a4_quant_next_workspace_size() bytes (16-byte
  *               aligned, contents irrelevant): every 128-column tile's
  *               share of xl1_next, summed afterwards in tile order (so the
