@@ -50,6 +50,8 @@ _SIGS = {
     "svdq_gemm_w4a4_quant_next_workspace_size": [_I64, _I64, _I32, _P],
     "svdq_gemm_w4a4_quant_next": [_P, _P, _I64, _I64, _P, _P, _I64, _P, _P, _I32, _P, _I32,
                                   _P, _P, _I32, _P, _P, _P, _P, _I64, _P],
+    "svdq_gemm_w4a4_quant_next_noalloc": [_P, _P, _I64, _I64, _P, _P, _I64, _P, _P, _I32, _P, _I32,
+                                          _P, _P, _I32, _P, _P, _P, _P],
 }
 
 
@@ -252,6 +254,14 @@ def svdq_gemm_w4a4_quant_next(qx, sx, M, K, qw, sw, N, xl1, l2t, rank, bias, act
         _ptr(qx), _ptr(sx), M, K, _ptr(qw), _ptr(sw), N, _ptr(xl1), _ptr(l2t), rank, _ptr(bias), act,
         _ptr(inv_next), _ptr(l1t_next), rank_next, _ptr(qx_next), _ptr(sx_next), _ptr(xl1_next),
         _ptr(workspace), workspace_bytes, _stream(stream)), "svdq_gemm_w4a4_quant_next")
+
+
+def svdq_gemm_w4a4_quant_next_noalloc(qx, sx, M, K, qw, sw, N, xl1, l2t, rank, bias, act, inv_next, l1t_next,
+                                      rank_next, qx_next, sx_next, xl1_next, stream=None):
+    _check(load_library().svdq_gemm_w4a4_quant_next_noalloc(
+        _ptr(qx), _ptr(sx), M, K, _ptr(qw), _ptr(sw), N, _ptr(xl1), _ptr(l2t), rank, _ptr(bias), act,
+        _ptr(inv_next), _ptr(l1t_next), rank_next, _ptr(qx_next), _ptr(sx_next), _ptr(xl1_next),
+        _stream(stream)), "svdq_gemm_w4a4_quant_next_noalloc")
 
 
 # ---------------------------------------------------------------- tensor helpers

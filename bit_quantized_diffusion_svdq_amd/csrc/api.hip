@@ -600,3 +600,63 @@ svdq_status svdq_gemm_w4a4_quant_next(const uint8_t* qx, const void* sx_f16, int
                                           (uint16_t*)sx_next_f16, xl1_next, (float*)workspace, (hipStream_t)stream),
                     "svdq_gemm_w4a4_quant_next launch");
 }
+
+/* ------------------------------------------------------------------------ */
+/* allocation-free form of svdq_gemm_w4a4_quant_next                          */
+
+namespace {
+
+// The tile partials of svdq_gemm_w4a4_quant_next_noalloc live here: one copy
+// per GPU, held until the process ends. Host code never uses the array's
+// name as an address (on the host it is only a stand-in for the symbol);
+// every use goes through the device address fetched per device below.
+constexpr int64_t kNoAllocScratchBytes = (int64_t)64 << 20;
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
+
+void* g_scratch_ptr[kMaxDev];
+std::mutex g_scratch_mu;
+
+// this device's address of `scratch` (fetched once, with the device current)
+svdq_status scratch_address(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) {
+        (void)hipGetLastError();
+        return fail(SVDQ_ERR_DEVICE, "no current HIP device");
+    }
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p) {
+            (void)hipGetLastError();
+            return fail(SVDQ_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+        }
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return SVDQ_OK;
+}
+
+}  // namespace
+
+svdq_status svdq_gemm_w4a4_quant_next_noalloc(const uint8_t* qx, const void* sx_f16, int64_t M, int64_t K,
+                                              const uint8_t* qw, const void* sw_f16, int64_t N,
+                                              const float* xl1, const void* l2t, int32_t rank,
+                                              const void* bias, int32_t act,
+                                              const float* inv_lambda_next, const void* l1t_next, int32_t rank_next,
+                                              uint8_t* qx_next, void* sx_next_f16, float* xl1_next, void* stream) {
+    svdq_status s;
+    if ((s = check_next_shape(M, N, rank_next)) != SVDQ_OK) return s;
+    const int64_t need = gemm_next_partial_bytes(M, N, rank_next);
+    if (need > kNoAllocScratchBytes)
+        return fail(SVDQ_ERR_SHAPE, "the tile partials take %lld bytes, above the %lld bytes of the built-in scratch "
+                    "(use svdq_gemm_w4a4_quant_next with a workspace)", (long long)need,
+                    (long long)kNoAllocScratchBytes);
+    void* ws = nullptr;
+    if (rank_next > 0 && M > 0) {
+        if ((s = check_current_device()) != SVDQ_OK) return s;
+        if ((s = scratch_address(&ws)) != SVDQ_OK) return s;
+    }
+    return svdq_gemm_w4a4_quant_next(qx, sx_f16, M, K, qw, sw_f16, N, xl1, l2t, rank, bias, act, inv_lambda_next,
+                                     l1t_next, rank_next, qx_next, sx_next_f16, xl1_next, ws, need, stream);
+}

@@ -345,6 +345,25 @@ svdq_status svdq_gemm_w4a4_quant_next(const uint8_t* qx, const void* sx_f16, int
                                       uint8_t* qx_next, void* sx_next_f16, float* xl1_next,
                                       void* workspace, int64_t workspace_bytes, void* stream);
 
+/* svdq_gemm_w4a4_quant_next_noalloc -- svdq_gemm_w4a4_quant_next for callers
+ * that cannot allocate device memory: code recorded under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc. Same arguments
+ * without the workspace: the tile partials go to a scratch array built into
+ * the library (64 MiB per GPU, held until the process ends; the MLP's fc1 at
+ * 4608 tokens, N 12288, rank_next 32, takes 56.6 MB). A call whose partials
+ * (N / 128) * M * rank_next * 4 bytes exceed it returns SVDQ_ERR_SHAPE and
+ * launches nothing. Nothing in the array needs to start at zero (every call
+ * writes all it reads). Every call on one GPU shares that GPU's array:
+ * calls that overlap on one GPU (other streams, other threads) race; order
+ * them on one stream. Allocates nothing (no hipMalloc, no allocating
+ * library routine). */
+svdq_status svdq_gemm_w4a4_quant_next_noalloc(const uint8_t* qx, const void* sx_f16, int64_t M, int64_t K,
+                                              const uint8_t* qw, const void* sw_f16, int64_t N,
+                                              const float* xl1, const void* l2t, int32_t rank,
+                                              const void* bias, int32_t act,
+                                              const float* inv_lambda_next, const void* l1t_next, int32_t rank_next,
+                                              uint8_t* qx_next, void* sx_next_f16, float* xl1_next, void* stream);
+
 /* ------------------------------------------------------------------------
  * Offline quantiser: turning a bf16 weight into the arrays above, on the
  * GPU. This is the Quantize step of the tool chain the donmalab.com page

@@ -172,3 +172,14 @@ def test_quant_next_workspace_and_empty(lib):
 def test_quant_next_without_gpu_reports_device_error(lib):
     _no_gpu()
     assert _next(lib) == DEVICE
+
+
+def test_noalloc_refuses_beyond_scratch_on_the_host(lib):
+    """The allocation-free fused GEMM checks its partials against the built-in
+    64 MiB before touching any device."""
+    st = lib.svdq_gemm_w4a4_quant_next_noalloc(A, B, 8192, 256, C, D, 12288, E, E + 0x10000, 16, None, 1,
+                                               A + 0x20000, B + 0x20000, 64, C + 0x20000, D + 0x20000, E + 0x20000,
+                                               None)
+    assert st == SHAPE and b"scratch" in lib.svdq_last_error()
+    assert lib.svdq_gemm_w4a4_quant_next_noalloc(A, B, 128, 256, C, D, 200, E, E, 16, None, 1, A, B, 32,
+                                                 C, D, E, None) == SHAPE
