@@ -6,10 +6,20 @@ quantisation) followed by svdq_gemm_w4a4 (group GEMM + low-rank up-projection
 + bias, bf16 out), M=4096 tokens, K=3072, N=9216, rank 32. `value` is the
 effective TOPS of that linear, 2*M*N*K / step time.
 
+Protocol: the first step is timed alone (first_run); the shader clock is read
+idle, after the timed steps and after each GEMM repetition set; one second of
+steps runs before anything is timed (clock and power ramp); then the K timed
+steps, the GEMM alone (5 x 50 launches hot, and over 4 rotated operand sets),
+the activation kernel over 12 rotated copies of X, a 256 MiB device copy.
+
 In the same run (separate timed loops, reported under "extra"): the AWQ W4A16
 adaLN GEMV (4 x 3072 -> 18432, weights rotated through more buffers than the
-256 MB Infinity Cache holds, so every launch reads HBM) and the MLP pair
-(fc1 3072 -> 12288 with the GELU epilogue, then fc2 12288 -> 3072, 4608 tokens).
+256 MB Infinity Cache holds, so every launch reads HBM; a read-only probe of
+the same bytes beside it), the MLP pair (fc1 3072 -> 12288 with the GELU
+epilogue, then fc2 12288 -> 3072, 4608 tokens) unfused and with fc2's
+activation pass fused into fc1 (eager and as one HIP graph), the MXFP4
+transformer block, the GPU offline quantiser on the QKV weight, and the CPU
+oracle (one and all host threads).
 
 Inputs are seeded synthetic tensors resident in HBM before timing starts:
 activations with the workload's outlier channels; packed weights are uniform
