@@ -5,7 +5,9 @@
 // one the remio.ai page attributes to the original Nunchaku engine (section
 // "SVDQuant moves hard values out of 4-bit"); here it is re-derived for CDNA4:
 //  - one workgroup owns 16 token rows; its waves (16 for ranks up to 32,
-//    else 8, as registers allow) take the 64-wide groups of K round-robin, so
+//    else 8, as registers allow; also 8 when there are more row blocks than
+//    CUs, so that two workgroups share a CU and a launch of 4608 tokens has
+//    no second round of workgroups) take the 64-wide groups of K round-robin, so
 //    every row is read from HBM exactly once with 128-byte contiguous row
 //    segments per group; each wave issues the loads of two (with 16 waves)
 //    or six of its groups at once (and the L1 fragments one group ahead)
@@ -38,7 +40,8 @@ namespace {
 constexpr int ROWS = 16;
 // waves per workgroup: 16 (four per SIMD) while the rank leaves room in 128
 // VGPRs (rank <= 32), else 8; more waves with fewer groups in flight each let a
-// SIMD work on whichever wave's data has landed
+// SIMD work on whichever wave's data has landed. With more row blocks than
+// CUs, 8 waves of at most 128 VGPRs let two workgroups share a CU.
 __host__ __device__ constexpr int waves_for(int rt) { return rt <= 2 ? 16 : 8; }
 
 // Eight E2M1 nibbles (t[0] in bits 0-3): round to nearest, ties to mantissa
@@ -55,15 +58,15 @@ DEV uint32_t e2m1_x8(const float* t) {
 }
 
 // RT = rank / 16 (0..8); FMT 0: INT4 g64, 1: MXFP4; CHT: groups each wave
-// keeps in flight (0: the default for the wave count)
-template <int RT, int FMT, int CHT>
-__global__ __launch_bounds__(waves_for(RT) * 64) void act_quant_kernel(
+// keeps in flight (0: the default for the wave count); WV: waves per workgroup
+template <int RT, int FMT, int CHT, int WV>
+__global__ __launch_bounds__(WV * 64) void act_quant_kernel(
     const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t ldx,
     const float* __restrict__ inv_lambda, const uint16_t* __restrict__ l1t,
     uint8_t* __restrict__ qx, uint16_t* __restrict__ sx, float* __restrict__ xl1)
 {
     constexpr int RTX = RT > 0 ? RT : 1;
-    constexpr int WAVES = waves_for(RT), NTH = WAVES * 64;
+    constexpr int WAVES = WV, NTH = WAVES * 64;
     extern __shared__ float smem[];
     const int G = (int)(K / 64);
     float* s_inv = smem;                                   // [K]
@@ -178,7 +181,7 @@ __global__ __launch_bounds__(waves_for(RT) * 64) void act_quant_kernel(
     // the X loads of up to CH groups are all issued before any is processed
     // (by default 16 waves x 2 groups or 8 x 6: 32 or 48 KB per CU in flight);
     // L1 fragments run one group ahead
-    constexpr int CH = CHT ? CHT : (WAVES == 16 ? 2 : 6);
+    constexpr int CH = CHT ? CHT : (WAVES == 16 || RT <= 2 ? 2 : 6);
     static_assert(CH % 2 == 0, "groups are processed in pairs");
     v8bf la[RTX][2], lb[RTX][2];
     for (int c0 = 0; c0 < ((n + CH - 1) / CH) * CH || c0 == 0; c0 += CH) {
@@ -253,43 +256,56 @@ __global__ __launch_bounds__(waves_for(RT) * 64) void act_quant_kernel(
 
 }  // namespace
 
-size_t act_quant_smem_bytes(int64_t K, int rank) {
+// LDS of a launch with `waves` waves; act_quant_smem_bytes is the largest
+// any launch of (K, rank) uses
+size_t act_quant_smem_bytes_w(int64_t K, int rank, int waves) {
     const int64_t G = K / 64;
-    return sizeof(float) * (K + (ROWS * G + 1) / 2 + (size_t)waves_for(rank / 16) * ROWS * rank);
+    return sizeof(float) * (K + (ROWS * G + 1) / 2 + (size_t)waves * ROWS * rank);
 }
+
+size_t act_quant_smem_bytes(int64_t K, int rank) { return act_quant_smem_bytes_w(K, rank, waves_for(rank / 16)); }
 
 namespace {
 
-template <int RT, int FMT, int CHT>
-void launch_one(dim3 grid, size_t smem, hipStream_t stream, const uint16_t* x, int64_t M, int64_t K,
+template <int RT, int FMT, int CHT, int WV>
+void launch_one(dim3 grid, hipStream_t stream, const uint16_t* x, int64_t M, int64_t K,
                 int64_t ldx, const float* inv_lambda, const uint16_t* l1t, uint8_t* qx, uint16_t* sx,
                 float* xl1)
 {
+    const size_t smem = act_quant_smem_bytes_w(K, RT * 16, WV);
     if (smem > 65536)
-        (void)hipFuncSetAttribute((const void*)act_quant_kernel<RT, FMT, CHT>,
+        (void)hipFuncSetAttribute((const void*)act_quant_kernel<RT, FMT, CHT, WV>,
                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-    hipLaunchKernelGGL((act_quant_kernel<RT, FMT, CHT>), grid, dim3(waves_for(RT) * 64), smem, stream,
+    hipLaunchKernelGGL((act_quant_kernel<RT, FMT, CHT, WV>), grid, dim3(WV * 64), smem, stream,
                        x, M, K, ldx, inv_lambda, l1t, qx, sx, xl1);
 }
 
 template <int FMT>
 hipError_t launch_fmt(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
                       const float* inv_lambda, const uint16_t* l1t, int rank,
-                      uint8_t* qx, uint16_t* sx, float* xl1, hipStream_t stream)
+                      uint8_t* qx, uint16_t* sx, float* xl1, int cus, hipStream_t stream)
 {
-    const dim3 grid((unsigned)((M + ROWS - 1) / ROWS));
-    const size_t smem = act_quant_smem_bytes(K, rank);
+    const int64_t blocks = (M + ROWS - 1) / ROWS;
+    const dim3 grid((unsigned)blocks);
+    const bool shared_cu = blocks > cus;          // more row blocks than CUs: 8-wave workgroups, two per CU
     switch (rank / 16) {
     // the MXFP4 form with 16 waves and at least 8 groups per wave (K >= 8192)
-    // runs faster with four groups in flight; the INT4 form does not
+    // runs faster with four groups in flight; the INT4 form does not.
+    // (a row-block count above the CU count takes 8-wave workgroups first)
 #define CASE(RTV) case RTV: \
-        if constexpr (FMT == 1 && waves_for(RTV) == 16) { \
-            if (K >= 8192) { \
-                launch_one<RTV, FMT, 4>(grid, smem, stream, x, M, K, ldx, inv_lambda, l1t, qx, sx, xl1); \
+        if constexpr (waves_for(RTV) == 16) { \
+            if (shared_cu) { \
+                launch_one<RTV, FMT, 0, 8>(grid, stream, x, M, K, ldx, inv_lambda, l1t, qx, sx, xl1); \
                 break; \
             } \
+            if constexpr (FMT == 1) { \
+                if (K >= 8192) { \
+                    launch_one<RTV, FMT, 4, 16>(grid, stream, x, M, K, ldx, inv_lambda, l1t, qx, sx, xl1); \
+                    break; \
+                } \
+            } \
         } \
-        launch_one<RTV, FMT, 0>(grid, smem, stream, x, M, K, ldx, inv_lambda, l1t, qx, sx, xl1); break;
+        launch_one<RTV, FMT, 0, waves_for(RTV)>(grid, stream, x, M, K, ldx, inv_lambda, l1t, qx, sx, xl1); break;
         CASE(0) CASE(1) CASE(2) CASE(3) CASE(4) CASE(5) CASE(6) CASE(7) CASE(8)
 #undef CASE
         default: return hipErrorInvalidValue;
@@ -301,14 +317,14 @@ hipError_t launch_fmt(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
 
 hipError_t launch_act_quant(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
                             const float* inv_lambda, const uint16_t* l1t, int rank,
-                            uint8_t* qx, uint16_t* sx, float* xl1, hipStream_t stream)
+                            uint8_t* qx, uint16_t* sx, float* xl1, int cus, hipStream_t stream)
 {
-    return launch_fmt<0>(x, M, K, ldx, inv_lambda, l1t, rank, qx, sx, xl1, stream);
+    return launch_fmt<0>(x, M, K, ldx, inv_lambda, l1t, rank, qx, sx, xl1, cus, stream);
 }
 
 hipError_t launch_act_quant_mxfp4(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
                                   const float* inv_lambda, const uint16_t* l1t, int rank,
-                                  uint8_t* qx, uint8_t* sx, float* xl1, hipStream_t stream)
+                                  uint8_t* qx, uint8_t* sx, float* xl1, int cus, hipStream_t stream)
 {
-    return launch_fmt<1>(x, M, K, ldx, inv_lambda, l1t, rank, qx, (uint16_t*)sx, xl1, stream);
+    return launch_fmt<1>(x, M, K, ldx, inv_lambda, l1t, rank, qx, (uint16_t*)sx, xl1, cus, stream);
 }

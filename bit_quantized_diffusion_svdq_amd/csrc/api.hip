@@ -13,7 +13,7 @@
 
 hipError_t launch_act_quant(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
                             const float* inv_lambda, const uint16_t* l1t, int rank,
-                            uint8_t* qx, uint16_t* sx, float* xl1, hipStream_t stream);
+                            uint8_t* qx, uint16_t* sx, float* xl1, int cus, hipStream_t stream);
 size_t act_quant_smem_bytes(int64_t K, int rank);
 hipError_t launch_gemm_w4a4(const uint8_t* qx, const uint16_t* sx, const uint8_t* qw,
                             const uint16_t* sw, const float* xl1, const uint16_t* l2t, int rank,
@@ -21,7 +21,7 @@ hipError_t launch_gemm_w4a4(const uint8_t* qx, const uint16_t* sx, const uint8_t
                             int64_t M, int64_t N, int64_t K, hipStream_t stream);
 hipError_t launch_act_quant_mxfp4(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
                                   const float* inv_lambda, const uint16_t* l1t, int rank,
-                                  uint8_t* qx, uint8_t* sx, float* xl1, hipStream_t stream);
+                                  uint8_t* qx, uint8_t* sx, float* xl1, int cus, hipStream_t stream);
 hipError_t launch_gemm_mxfp4(const uint8_t* qx, const uint8_t* sx, const uint8_t* qw,
                              const uint8_t* sw, const float* xl1, const uint16_t* l2t, int rank,
                              const uint16_t* bias, int act, void* y, int y_f32, int64_t ldy,
@@ -184,15 +184,16 @@ svdq_status quantize_act_impl(int mxfp4, const void* x, int64_t M, int64_t K, in
         (inv_lambda && !aligned(inv_lambda, 16)) ||
         (rank > 0 && (!aligned(l1t, 16) || !aligned(xl1, 16))))
         return fail(SVDQ_ERR_ALIGN, "x, inv_lambda, l1t, qx, sx_f16, xl1 need 16-byte alignment");
-    if ((s = check_current_device()) != SVDQ_OK) return s;
+    int cus = 0;
+    if ((s = check_current_device(&cus)) != SVDQ_OK) return s;
     const uint16_t* l1 = rank > 0 ? (const uint16_t*)l1t : nullptr;
     float* xo = rank > 0 ? xl1 : nullptr;
     if (mxfp4)
         return launched(launch_act_quant_mxfp4((const uint16_t*)x, M, K, ldx, inv_lambda, l1, rank, qx,
-                                               (uint8_t*)sx_f16, xo, (hipStream_t)stream),
+                                               (uint8_t*)sx_f16, xo, cus, (hipStream_t)stream),
                         "svdq_quantize_act_mxfp4 launch");
     return launched(launch_act_quant((const uint16_t*)x, M, K, ldx, inv_lambda, l1, rank, qx,
-                                     (uint16_t*)sx_f16, xo, (hipStream_t)stream),
+                                     (uint16_t*)sx_f16, xo, cus, (hipStream_t)stream),
                     "svdq_quantize_act launch");
 }
 
