@@ -235,6 +235,8 @@ def mxfp4_block(lib, dev, iters=50):
     with GELU, fc2 12288->3072 on fc1's output; rank 32. One step = activation
     quantisation + GEMM for each. Weights are random codes with E8M0
     exponents of a realistic range (kernel time does not depend on values)."""
+    import statistics
+
     import torch
 
     from bit_quantized_diffusion_svdq_amd import pack_l1
@@ -290,7 +292,43 @@ def mxfp4_block(lib, dev, iters=50):
     graph_ms = time_graph(step, 5, replays=10)
     ops = 2.0 * M * sum(l["K"] * l["N"] for l in L)
     gsum = sum(gemm_ms)
+    # the same block with fc2's activation pass fused into fc1's epilogue
+    # (svdq_gemm_mxfp4_quant_next: the bf16 hidden state is never stored)
+    from bit_quantized_diffusion_svdq_amd import SvdqLinear, SvdqMLP
+    lin = lambda l: SvdqLinear(l["inv"], l["l1t"], l["l2t"], l["qw"], l["sw"], l["bias"], R, fmt="mxfp4")
+    mlp = SvdqMLP(lin(L[2]), lin(L[3]), M)
+    mlp.x.copy_(xf)
+
+    def step_fused():
+        run(0, xq, "none", ys[0], None)
+        run(1, xo, "none", ys[1], None)
+        mlp._launches()
+
+    for _ in range(10):
+        step_fused()
+    torch.cuda.synchronize()
+    fused_ms, _ = time_reps(step_fused, 10, 5)
+    fused_graph_ms = [time_graph(step_fused, 5, replays=10) for _ in range(3)]
+    fmed, fgmed = statistics.median(fused_ms), statistics.median(fused_graph_ms)
+    # the MXFP4 GEMM alone at the QKV shape of the headline (4096 tokens)
+    Mq = 4096
+    lq = L[0]
+    xq4 = xq[:Mq].contiguous()
+    qx4, sx4, xl4 = lib.quantize_act_mxfp4(xq4, lq["inv"], lq["l1t"], R)
+    yq4 = torch.empty((Mq, lq["N"]), dtype=torch.bfloat16, device=dev)
+    gq = lambda: lib.mxfp4_linear(qx4, sx4, xl4, lq["qw"], lq["sw"], lq["l2t"], lq["bias"], R, y=yq4)
+    for _ in range(20):
+        gq()
+    qkv_ms, _ = time_reps(gq, 50, 5)
+    qmed = statistics.median(qkv_ms)
+    qkv_ops = 2.0 * Mq * lq["K"] * lq["N"]
     return {"M": M, "ops": ops, "block_us": round(block_ms * 1e3, 2),
+            "block_fused_mlp_us": summary_us(fused_ms), "block_fused_mlp_graph_us": summary_us(fused_graph_ms),
+            "block_fused_mlp_TOPS": round(ops / (fmed * 1e-3) / 1e12, 1),
+            "block_fused_mlp_graph_TOPS": round(ops / (fgmed * 1e-3) / 1e12, 1),
+            "qkv_gemm_M4096": {**summary_us(qkv_ms), "TOPS": round(qkv_ops / (qmed * 1e-3) / 1e12, 1),
+                               "frac_of_fp4_peak": round(qkv_ops / (qmed * 1e-3) / 1e12 / PEAK_FP4_TFLOPS, 4),
+                               "frac_of_int8_peak": round(qkv_ops / (qmed * 1e-3) / 1e12 / PEAK_INT8_TOPS, 4)},
             "block_TOPS": round(ops / (block_ms * 1e-3) / 1e12, 1),
             "block_graph_us": round(graph_ms * 1e3, 2),
             "block_graph_TOPS": round(ops / (graph_ms * 1e-3) / 1e12, 1),
@@ -586,7 +624,8 @@ def main():
         extra["offline_quantize_qkv"] = offline_quantize_timing(lib, dev)
         log(f"offline quantiser, QKV layer: {extra['offline_quantize_qkv']['median_ms']} ms")
         extra["mxfp4_block"] = mxfp4_block(lib, dev)
-        log(f"mxfp4 block {extra['mxfp4_block']['block_us']} us")
+        log(f"mxfp4 block {extra['mxfp4_block']['block_us']} us, with the fused MLP "
+            f"{extra['mxfp4_block']['block_fused_mlp_us']['median_us']} us")
 
     out = {
         "metric": "W4A4 linear effective TOPS (M4096 K3072 N9216 r32) + % of MI355X MFMA peak",

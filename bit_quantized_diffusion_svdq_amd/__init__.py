@@ -13,7 +13,7 @@ from ._lib import (SvdqError, awq_gemv_w4a16, check_device, library_path, load_l
                    svdq_probe_clock, svdq_probe_read, svdq_calib_absmax, svdq_smoothing,
                    svdq_smooth_weight, svdq_lowrank_workspace_size, svdq_lowrank, svdq_quantize_residual,
                    svdq_pack_lowrank, svdq_gemm_w4a4_quant_next, svdq_gemm_w4a4_quant_next_workspace_size,
-                   w4a4_linear_quant_next)
+                   w4a4_linear_quant_next, svdq_gemm_mxfp4_quant_next, mxfp4_linear_quant_next)
 from .offline import quantize_layer
 from .fused import column_offsets, column_slice, projection_weights, split_columns
 from .graph import CapturedSequence
@@ -27,5 +27,6 @@ __all__ = ["SvdqError", "awq_gemv_w4a16", "check_device", "library_path", "load_
            "svdq_probe_clock", "svdq_probe_read", "svdq_calib_absmax", "svdq_smoothing",
            "svdq_smooth_weight", "svdq_lowrank_workspace_size", "svdq_lowrank", "svdq_quantize_residual",
            "svdq_pack_lowrank", "quantize_layer", "svdq_gemm_w4a4_quant_next",
-           "svdq_gemm_w4a4_quant_next_workspace_size", "w4a4_linear_quant_next", "SvdqLinear", "SvdqMLP",
+           "svdq_gemm_w4a4_quant_next_workspace_size", "w4a4_linear_quant_next", "svdq_gemm_mxfp4_quant_next",
+           "mxfp4_linear_quant_next", "SvdqLinear", "SvdqMLP",
            "column_offsets", "column_slice", "projection_weights", "split_columns", "CapturedSequence"]

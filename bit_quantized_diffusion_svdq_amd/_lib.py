@@ -50,6 +50,8 @@ _SIGS = {
     "svdq_gemm_w4a4_quant_next_workspace_size": [_I64, _I64, _I32, _P],
     "svdq_gemm_w4a4_quant_next": [_P, _P, _I64, _I64, _P, _P, _I64, _P, _P, _I32, _P, _I32,
                                   _P, _P, _I32, _P, _P, _P, _P, _I64, _P],
+    "svdq_gemm_mxfp4_quant_next": [_P, _P, _I64, _I64, _P, _P, _I64, _P, _P, _I32, _P, _I32,
+                                   _P, _P, _I32, _P, _P, _P, _P, _I64, _P],
     "svdq_gemm_w4a4_quant_next_noalloc": [_P, _P, _I64, _I64, _P, _P, _I64, _P, _P, _I32, _P, _I32,
                                           _P, _P, _I32, _P, _P, _P, _P],
 }
@@ -256,6 +258,14 @@ def svdq_gemm_w4a4_quant_next(qx, sx, M, K, qw, sw, N, xl1, l2t, rank, bias, act
         _ptr(workspace), workspace_bytes, _stream(stream)), "svdq_gemm_w4a4_quant_next")
 
 
+def svdq_gemm_mxfp4_quant_next(qx, sx, M, K, qw, sw, N, xl1, l2t, rank, bias, act, inv_next, l1t_next,
+                               rank_next, qx_next, sx_next, xl1_next, workspace, workspace_bytes, stream=None):
+    _check(load_library().svdq_gemm_mxfp4_quant_next(
+        _ptr(qx), _ptr(sx), M, K, _ptr(qw), _ptr(sw), N, _ptr(xl1), _ptr(l2t), rank, _ptr(bias), act,
+        _ptr(inv_next), _ptr(l1t_next), rank_next, _ptr(qx_next), _ptr(sx_next), _ptr(xl1_next),
+        _ptr(workspace), workspace_bytes, _stream(stream)), "svdq_gemm_mxfp4_quant_next")
+
+
 def svdq_gemm_w4a4_quant_next_noalloc(qx, sx, M, K, qw, sw, N, xl1, l2t, rank, bias, act, inv_next, l1t_next,
                                       rank_next, qx_next, sx_next, xl1_next, stream=None):
     _check(load_library().svdq_gemm_w4a4_quant_next_noalloc(
@@ -425,14 +435,18 @@ def mxfp4_linear(qx, sx, xl1, qw, sw, l2t, bias, rank: int, act: str = "none",
 
 
 def w4a4_linear_quant_next(qx, sx, xl1, qw, sw, l2t, bias, rank: int, act: str, inv_next, l1t_next,
-                           rank_next: int, out=None, workspace=None, stream=None):
+                           rank_next: int, out=None, workspace=None, stream=None, fmt: str = "int4"):
     """The W4A4 layer whose bf16 output H = bf16(act(Y)) feeds the next
     layer: instead of H, returns the next layer's activation-pass results
-    (qx_next uint8 [M, N/2], sx_next fp16 [ceil(N/256), M, 4], xl1_next fp32
-    [M, rank_next]), as svdq_quantize_act(H, inv_next, l1t_next, rank_next)
-    would. ``out`` may give those three tensors, ``workspace`` the partials
-    buffer (svdq_gemm_w4a4_quant_next_workspace_size bytes)."""
-    M, K, N = _check_gemm_inputs(qx, sx, xl1, qw, sw, l2t, bias, rank, None, 4, torch.float16)
+    (qx_next uint8 [M, N/2], sx_next [ceil(N/256), M, 4] fp16 (INT4) or
+    [ceil(N/256), M, 8] uint8 E8M0 (MXFP4), xl1_next fp32 [M, rank_next]),
+    as svdq_quantize_act(H, ...) (or svdq_quantize_act_mxfp4) would.
+    ``out`` may give those three tensors, ``workspace`` the partials buffer
+    (svdq_gemm_w4a4_quant_next_workspace_size bytes)."""
+    _require(fmt in FMT, f"fmt must be one of {sorted(FMT)}")
+    mx = fmt == "mxfp4"
+    sx_last, sx_dt = (8, torch.uint8) if mx else (4, torch.float16)
+    M, K, N = _check_gemm_inputs(qx, sx, xl1, qw, sw, l2t, bias, rank, None, sx_last, sx_dt)
     _require(N % 128 == 0, f"N = {N} must be a multiple of 128")
     _require(inv_next is not None and inv_next.dtype == torch.float32 and inv_next.numel() == N
              and inv_next.is_contiguous(), f"inv_next must be a contiguous fp32 vector of N = {N} values")
@@ -444,19 +458,27 @@ def w4a4_linear_quant_next(qx, sx, xl1, qw, sw, l2t, bias, rank: int, act: str, 
     G4 = (N // 64 + 3) // 4
     if out is None:
         out = (torch.empty((M, N // 2), dtype=torch.uint8, device=dev),
-               torch.empty((G4, M, 4), dtype=torch.float16, device=dev),
+               torch.empty((G4, M, sx_last), dtype=sx_dt, device=dev),
                torch.empty((M, rank_next), dtype=torch.float32, device=dev) if rank_next else None)
     qn, sn, xn = out
     _require(tuple(qn.shape) == (M, N // 2) and qn.dtype == torch.uint8 and qn.is_contiguous(), "qx_next shape")
-    _require(tuple(sn.shape) == (G4, M, 4) and sn.dtype == torch.float16 and sn.is_contiguous(), "sx_next shape")
+    _require(tuple(sn.shape) == (G4, M, sx_last) and sn.dtype == sx_dt and sn.is_contiguous(), "sx_next shape")
     if rank_next:
         _require(xn is not None and tuple(xn.shape) == (M, rank_next) and xn.dtype == torch.float32
                  and xn.is_contiguous(), "xl1_next shape")
     nbytes = svdq_gemm_w4a4_quant_next_workspace_size(M, N, rank_next)
     if workspace is None and nbytes:
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
-    svdq_gemm_w4a4_quant_next(qx, sx, M, K, qw, sw, N, xl1 if rank else None, l2t if rank else None, rank,
-                              bias, ACT[act], inv_next, l1t_next if rank_next else None, rank_next, qn, sn,
-                              xn if rank_next else None, workspace, workspace.numel() if workspace is not None else 0,
-                              stream)
+    entry = svdq_gemm_mxfp4_quant_next if mx else svdq_gemm_w4a4_quant_next
+    entry(qx, sx, M, K, qw, sw, N, xl1 if rank else None, l2t if rank else None, rank,
+          bias, ACT[act], inv_next, l1t_next if rank_next else None, rank_next, qn, sn,
+          xn if rank_next else None, workspace, workspace.numel() if workspace is not None else 0,
+          stream)
     return qn, sn, xn
+
+
+def mxfp4_linear_quant_next(qx, sx, xl1, qw, sw, l2t, bias, rank: int, act: str, inv_next, l1t_next,
+                            rank_next: int, out=None, workspace=None, stream=None):
+    """w4a4_linear_quant_next for MXFP4 layers (svdq_gemm_mxfp4_quant_next)."""
+    return w4a4_linear_quant_next(qx, sx, xl1, qw, sw, l2t, bias, rank, act, inv_next, l1t_next, rank_next,
+                                  out=out, workspace=workspace, stream=stream, fmt="mxfp4")

@@ -31,9 +31,10 @@ class SvdqLinear:
     l1t: torch.Tensor | None        # bf16, L1 tile layout (K * rank values)
     l2t: torch.Tensor | None        # bf16 [N, rank]
     qw: torch.Tensor                # uint8 [N, K/2]
-    sw: torch.Tensor                # fp16 [ceil(K/256), N, 4]
+    sw: torch.Tensor                # fp16 [ceil(K/256), N, 4] (INT4) or uint8 [ceil(K/256), N, 8] (MXFP4)
     bias: torch.Tensor | None       # bf16 [N]
     rank: int
+    fmt: str = "int4"               # "int4" (group 64, fp16 scales) or "mxfp4" (E2M1, E8M0 per 32)
 
     @property
     def K(self) -> int:
@@ -52,12 +53,15 @@ class SvdqLinear:
 
 
 class SvdqMLP:
-    """fc1 (GELU) -> fc2 on M tokens. ``forward(x)`` copies x into the
-    block's input buffer and runs the three launches; ``capture()`` records
-    them once into a graph, after which ``replay(x)`` does the same with one
-    graph launch. Outputs land in ``self.y`` (bf16 [M, fc2.N])."""
+    """fc1 (GELU) -> fc2 on M tokens, both INT4 or both MXFP4. ``forward(x)``
+    copies x into the block's input buffer and runs the three launches;
+    ``capture()`` records them once into a graph, after which ``replay(x)``
+    does the same with one graph launch. Outputs land in ``self.y`` (bf16
+    [M, fc2.N])."""
 
     def __init__(self, fc1: SvdqLinear, fc2: SvdqLinear, M: int):
+        _lib._require(fc1.fmt == fc2.fmt and fc1.fmt in ("int4", "mxfp4"),
+                      f"fc1 and fc2 must share a format (int4 or mxfp4), got {fc1.fmt} and {fc2.fmt}")
         _lib._require(fc2.K == fc1.N, f"fc2 takes K = {fc2.K}, fc1 gives N = {fc1.N}")
         _lib._require(fc1.N % 128 == 0, "fc1's N must be a multiple of 128 for the fused activation pass")
         _lib._require(fc2.rank <= 64, "fc2's rank must be at most 64 for the fused activation pass")
@@ -65,11 +69,13 @@ class SvdqMLP:
         dev = fc1.qw.device
         K1, N1, N2 = fc1.K, fc1.N, fc2.N
         self.x = torch.empty((M, K1), dtype=torch.bfloat16, device=dev)
+        self.mx = fc1.fmt == "mxfp4"
+        sl, sdt = (8, torch.uint8) if self.mx else (4, torch.float16)
         self.qx1 = torch.empty((M, K1 // 2), dtype=torch.uint8, device=dev)
-        self.sx1 = torch.empty(((K1 // 64 + 3) // 4, M, 4), dtype=torch.float16, device=dev)
+        self.sx1 = torch.empty(((K1 // 64 + 3) // 4, M, sl), dtype=sdt, device=dev)
         self.xl1_1 = torch.empty((M, fc1.rank), dtype=torch.float32, device=dev) if fc1.rank else None
         self.qx2 = torch.empty((M, N1 // 2), dtype=torch.uint8, device=dev)
-        self.sx2 = torch.empty(((N1 // 64 + 3) // 4, M, 4), dtype=torch.float16, device=dev)
+        self.sx2 = torch.empty(((N1 // 64 + 3) // 4, M, sl), dtype=sdt, device=dev)
         self.xl1_2 = torch.empty((M, fc2.rank), dtype=torch.float32, device=dev) if fc2.rank else None
         nb = _lib.svdq_gemm_w4a4_quant_next_workspace_size(M, N1, fc2.rank)
         self.ws = torch.empty(max(nb, 16), dtype=torch.uint8, device=dev)
@@ -79,14 +85,15 @@ class SvdqMLP:
 
     def _launches(self):
         f1, f2, M = self.fc1, self.fc2, self.M
-        _lib.svdq_quantize_act(self.x, M, f1.K, f1.K, f1.inv_lambda, f1.l1t, f1.rank, self.qx1, self.sx1,
-                               self.xl1_1)
-        _lib.svdq_gemm_w4a4_quant_next(self.qx1, self.sx1, M, f1.K, f1.qw, f1.sw, f1.N, self.xl1_1, f1.l2t,
-                                       f1.rank, f1.bias, _lib.ACT["gelu_tanh"], f2.inv_lambda, f2.l1t, f2.rank,
-                                       self.qx2, self.sx2, self.xl1_2, self.ws if self.ws_bytes else None,
-                                       self.ws_bytes)
-        _lib.svdq_gemm_w4a4(self.qx2, self.sx2, M, f2.K, f2.qw, f2.sw, f2.N, self.xl1_2, f2.l2t, f2.rank,
-                            f2.bias, _lib.ACT["none"], self.y, 0, f2.N)
+        act_pass = _lib.svdq_quantize_act_mxfp4 if self.mx else _lib.svdq_quantize_act
+        fused = _lib.svdq_gemm_mxfp4_quant_next if self.mx else _lib.svdq_gemm_w4a4_quant_next
+        gemm = _lib.svdq_gemm_mxfp4 if self.mx else _lib.svdq_gemm_w4a4
+        act_pass(self.x, M, f1.K, f1.K, f1.inv_lambda, f1.l1t, f1.rank, self.qx1, self.sx1, self.xl1_1)
+        fused(self.qx1, self.sx1, M, f1.K, f1.qw, f1.sw, f1.N, self.xl1_1, f1.l2t, f1.rank, f1.bias,
+              _lib.ACT["gelu_tanh"], f2.inv_lambda, f2.l1t, f2.rank, self.qx2, self.sx2, self.xl1_2,
+              self.ws if self.ws_bytes else None, self.ws_bytes)
+        gemm(self.qx2, self.sx2, M, f2.K, f2.qw, f2.sw, f2.N, self.xl1_2, f2.l2t, f2.rank, f2.bias,
+             _lib.ACT["none"], self.y, 0, f2.N)
 
     def _load(self, x):
         _lib._check_rows(x, "x", torch.bfloat16)

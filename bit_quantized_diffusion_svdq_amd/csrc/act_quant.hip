@@ -44,19 +44,6 @@ constexpr int ROWS = 16;
 // CUs, 8 waves of at most 128 VGPRs let two workgroups share a CU.
 __host__ __device__ constexpr int waves_for(int rt) { return rt <= 2 ? 16 : 8; }
 
-// Eight E2M1 nibbles (t[0] in bits 0-3): round to nearest, ties to mantissa
-// 0, saturating at 6 (the conversion instruction), then the sign of every
-// zero nibble cleared: (mag + 7) carries into bit 3 exactly when mag != 0.
-DEV uint32_t e2m1_x8(const float* t) {
-    uint32_t w = 0u;
-    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, t[0], t[1], 1.0f, 0);
-    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, t[2], t[3], 1.0f, 1);
-    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, t[4], t[5], 1.0f, 2);
-    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, t[6], t[7], 1.0f, 3);
-    const uint32_t nonzero = ((w & 0x77777777u) + 0x77777777u) & 0x88888888u;
-    return w & (0x77777777u | nonzero);
-}
-
 // RT = rank / 16 (0..8); FMT 0: INT4 g64, 1: MXFP4; CHT: groups each wave
 // keeps in flight (0: the default for the wave count); WV: waves per workgroup
 template <int RT, int FMT, int CHT, int WV>
@@ -143,9 +130,8 @@ __global__ __launch_bounds__(WV * 64) void act_quant_kernel(
         } else {
             // block 2g + (p >> 1) of the row; e = floor(log2 amax) - 2 from the
             // exponent field (a zero or subnormal amax clamps to -127)
-            const int ebits = (int)((__float_as_uint(amax) >> 23) & 0xffu);
-            const int e = ebits - 129 < -127 ? -127 : ebits - 129;
-            const float sc = __uint_as_float((uint32_t)(127 - e) << 23);   // 2^-e, exact
+            const int e = mx_block_exponent(amax);
+            const float sc = mx_inv_scale(e);                              // 2^-e, exact
             float t[16];
 #pragma unroll
             for (int j = 0; j < 16; ++j) t[j] = v[j] * sc;

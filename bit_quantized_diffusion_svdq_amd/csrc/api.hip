@@ -54,7 +54,7 @@ hipError_t launch_gemm_w4a4_next(const uint8_t* qx, const uint16_t* sx, const ui
                                  const uint16_t* bias, int act, int64_t M, int64_t N, int64_t K,
                                  const float* inv_next, const uint16_t* l1t_next, int rank_next,
                                  uint8_t* qx_next, uint16_t* sx_next, float* xl1_next, float* part,
-                                 hipStream_t stream);
+                                 hipStream_t stream, int fmt);
 hipError_t launch_clock_probe(long long* out, int spins, hipStream_t stream);
 hipError_t launch_read_probe(const uint8_t* buf, int64_t bytes, uint32_t* sink, int blocks,
                              hipStream_t stream);
@@ -563,7 +563,10 @@ svdq_status svdq_gemm_w4a4_quant_next_workspace_size(int64_t M, int64_t N, int32
     return SVDQ_OK;
 }
 
-svdq_status svdq_gemm_w4a4_quant_next(const uint8_t* qx, const void* sx_f16, int64_t M, int64_t K,
+namespace {
+
+// both formats: the checks, then the launch (fmt 0 INT4, 1 MXFP4)
+svdq_status gemm_quant_next(const char* fn, int fmt, const uint8_t* qx, const void* sx_f16, int64_t M, int64_t K,
                                       const uint8_t* qw, const void* sw_f16, int64_t N,
                                       const float* xl1, const void* l2t, int32_t rank,
                                       const void* bias, int32_t act,
@@ -592,14 +595,42 @@ svdq_status svdq_gemm_w4a4_quant_next(const uint8_t* qx, const void* sx_f16, int
     if (!aligned(qx, 16) || !aligned(qw, 16) || !aligned(sx_f16, 16) || !aligned(sw_f16, 16) ||
         (xl1 && !aligned(xl1, 16)) || (l2t && !aligned(l2t, 16)) || (bias && !aligned(bias, 2)) ||
         !aligned(inv_lambda_next, 16) || (l1t_next && !aligned(l1t_next, 16)) || !aligned(qx_next, 16) ||
-        !aligned(sx_next_f16, 2) || (xl1_next && !aligned(xl1_next, 16)) || (workspace && !aligned(workspace, 16)))
-        return fail(SVDQ_ERR_ALIGN, "vector operands need 16-byte alignment (sx_next and bias 2)");
+        !aligned(sx_next_f16, fmt == 1 ? 1 : 2) || (xl1_next && !aligned(xl1_next, 16)) ||
+        (workspace && !aligned(workspace, 16)))
+        return fail(SVDQ_ERR_ALIGN, "vector operands need 16-byte alignment (sx_next %d, bias 2)", fmt == 1 ? 1 : 2);
     if ((s = check_current_device()) != SVDQ_OK) return s;
     return launched(launch_gemm_w4a4_next(qx, (const uint16_t*)sx_f16, qw, (const uint16_t*)sw_f16, xl1,
                                           (const uint16_t*)l2t, rank, (const uint16_t*)bias, act, M, N, K,
                                           inv_lambda_next, (const uint16_t*)l1t_next, rank_next, qx_next,
-                                          (uint16_t*)sx_next_f16, xl1_next, (float*)workspace, (hipStream_t)stream),
-                    "svdq_gemm_w4a4_quant_next launch");
+                                          (uint16_t*)sx_next_f16, xl1_next, (float*)workspace, (hipStream_t)stream,
+                                          fmt),
+                    fn);
+}
+
+}  // namespace
+
+svdq_status svdq_gemm_w4a4_quant_next(const uint8_t* qx, const void* sx_f16, int64_t M, int64_t K,
+                                      const uint8_t* qw, const void* sw_f16, int64_t N,
+                                      const float* xl1, const void* l2t, int32_t rank,
+                                      const void* bias, int32_t act,
+                                      const float* inv_lambda_next, const void* l1t_next, int32_t rank_next,
+                                      uint8_t* qx_next, void* sx_next_f16, float* xl1_next,
+                                      void* workspace, int64_t workspace_bytes, void* stream) {
+    return gemm_quant_next("svdq_gemm_w4a4_quant_next launch", 0, qx, sx_f16, M, K, qw, sw_f16, N, xl1, l2t, rank,
+                           bias, act, inv_lambda_next, l1t_next, rank_next, qx_next, sx_next_f16, xl1_next,
+                           workspace, workspace_bytes, stream);
+}
+
+svdq_status svdq_gemm_mxfp4_quant_next(const uint8_t* qx, const void* sx, int64_t M, int64_t K,
+                                       const uint8_t* qw, const void* sw, int64_t N,
+                                       const float* xl1, const void* l2t, int32_t rank,
+                                       const void* bias, int32_t act,
+                                       const float* inv_lambda_next, const void* l1t_next, int32_t rank_next,
+                                       uint8_t* qx_next, void* sx_next, float* xl1_next,
+                                       void* workspace, int64_t workspace_bytes, void* stream) {
+    return gemm_quant_next("svdq_gemm_mxfp4_quant_next launch", 1, qx, sx, M, K, qw, sw, N, xl1, l2t, rank,
+                           bias, act, inv_lambda_next, l1t_next, rank_next, qx_next, sx_next, xl1_next,
+                           workspace, workspace_bytes, stream);
 }
 
 /* ------------------------------------------------------------------------ */

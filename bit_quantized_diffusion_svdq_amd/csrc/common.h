@@ -113,3 +113,27 @@ DEV float gelu_tanh_f32(float y) {
     const float t = y * __builtin_fmaf(c2, y * y, c1);
     return y * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(t));
 }
+
+// Eight E2M1 nibbles (t[0] in bits 0-3): round to nearest, ties to mantissa
+// 0, saturating at 6 (the conversion instruction), then the sign of every
+// zero nibble cleared: (mag + 7) carries into bit 3 exactly when mag != 0.
+DEV uint32_t e2m1_x8(const float* t) {
+    uint32_t w = 0u;
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, t[0], t[1], 1.0f, 0);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, t[2], t[3], 1.0f, 1);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, t[4], t[5], 1.0f, 2);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, t[6], t[7], 1.0f, 3);
+    const uint32_t nonzero = ((w & 0x77777777u) + 0x77777777u) & 0x88888888u;
+    return w & (0x77777777u | nonzero);
+}
+
+// E8M0 block exponent of an MX block with absolute maximum amax (OCP
+// Microscaling Formats v1.0: floor(log2 amax) minus the E2M1 emax of 2),
+// read off the exponent field; a zero or subnormal amax clamps to -127.
+DEV int mx_block_exponent(float amax) {
+    const int ebits = (int)((__float_as_uint(amax) >> 23) & 0xffu);
+    return ebits - 129 < -127 ? -127 : ebits - 129;
+}
+
+// 2^-e for an E8M0 exponent e in [-127, 127], exact
+DEV float mx_inv_scale(int e) { return __uint_as_float((uint32_t)(127 - e) << 23); }

@@ -112,9 +112,10 @@ DEV v6i unfold_frag(const uint4& raw) {
 // The next layer's activation pass, done by MODE 3 on this layer's output
 // H = bf16(act(Y)) (which is not stored): smoothing multiplier inv [N],
 // its down-projection L1 [N][rank] in the tile layout of the activation
-// kernel (format v4) lt, codes qx [M][N/2]
-// (format v2) and scales sx (format v3) of H * inv, and per 128-column
-// tile of H the partial down-projection part [N/128][M][rank] (fp32).
+// kernel (format v4) lt, codes qx [M][N/2] and scales sx of H * inv (INT4:
+// format v2 codes, format v3 fp16 scales; MXFP4: E2M1 nibbles and the E8M0
+// exponent records of the MXFP4 activation kernel), and per 128-column tile
+// of H the partial down-projection part [N/128][M][rank] (fp32).
 struct NextAct {
     const float* inv;
     const uint16_t* lt;
@@ -125,7 +126,7 @@ struct NextAct {
 };
 
 // MODE 0: bf16 out, 1: fp32 out, 2: integer partials dump (INT4 only),
-// 3: the next layer's activation pass on the bf16 output (INT4 only).
+// 3: the next layer's activation pass on the bf16 output (same FMT).
 // FMT 0: INT4 g64 with fp16 scales; 1: MXFP4 (E2M1 codes, E8M0 per 32).
 template <class C, int MODE, int ACT, int FMT = 0>
 __global__ __launch_bounds__(C::NT, C::MINB) void gemm_w4a4_kernel(
@@ -136,7 +137,6 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_w4a4_kernel(
     void* __restrict__ y, int64_t ldy, int64_t M, int64_t N, int64_t K,
     int64_t pm0, int64_t pmc, int64_t pn0, int64_t pnc, int32_t* __restrict__ part, NextAct nx)
 {
-    static_assert(MODE != 3 || FMT == 0, "the fused next-layer pass is INT4 only");
     constexpr int BM = C::BM, BN = C::BN, TM = C::TM, TN = C::TN, NT = C::NT;
     // two quad slots of codes and two of scales, all separate objects: the
     // compiler then tracks each one's outstanding LDS-destination loads on
@@ -524,7 +524,7 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_w4a4_kernel(
         const int64_t row = tm0 + wm * 64 + lane;
         const int g2 = (int)(col0 >> 6);
         float xh[64];
-        float amax = 0.0f;
+        float amh[2] = {0.0f, 0.0f};                       // maxima of columns 0-31 and 32-63
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
             const uint4 hv = *(const uint4*)(stg + lane * 128 + ((c ^ (lane & 7)) << 4));
@@ -536,10 +536,34 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_w4a4_kernel(
             for (int k = 0; k < 8; ++k) {
                 const float h = (k & 1) ? bf16_hi_to_f32(hw[k >> 1]) : bf16_lo_to_f32(hw[k >> 1]);
                 xh[8 * c + k] = h * iv[k];
-                amax = fmaxf(amax, fabsf(xh[8 * c + k]));
+                amh[c >> 2] = fmaxf(amh[c >> 2], fabsf(xh[8 * c + k]));
             }
         }
-        {
+        // rows past M fall outside the buffer ranges and are dropped
+        const rsrc_t rq = make_rsrc(nx.qx, M * (N / 2));
+        const int qo = (int)(row * (N / 2) + col0 / 2);
+        if constexpr (FMT == 1) {
+            // MXFP4: the row's two 32-column blocks, each with its own E8M0
+            // exponent (the activation kernel's per-block step); nibble k of
+            // the 32 stored bytes is column col0 + k
+            uint32_t wd[8];
+#pragma unroll
+            for (int b = 0; b < 2; ++b) {
+                const int e = mx_block_exponent(amh[b]);
+                const float sc = mx_inv_scale(e);
+                float t[32];
+#pragma unroll
+                for (int k = 0; k < 32; ++k) t[k] = xh[32 * b + k] * sc;
+#pragma unroll
+                for (int w8 = 0; w8 < 4; ++w8) wd[4 * b + w8] = e2m1_x8(t + 8 * w8);
+                // exponent records [G/4][M][8]: even blocks of the quad in bytes
+                // 0-3, odd blocks in bytes 4-7
+                if (row < M) ((uint8_t*)nx.sx)[((int64_t)(g2 >> 2) * M + row) * 8 + 4 * b + (g2 & 3)] = (uint8_t)(e + 127);
+            }
+            __builtin_amdgcn_raw_buffer_store_b128(v4i{(int)wd[0], (int)wd[1], (int)wd[2], (int)wd[3]}, rq, qo, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b128(v4i{(int)wd[4], (int)wd[5], (int)wd[6], (int)wd[7]}, rq, qo + 16, 0, 0);
+        } else {
+            const float amax = fmaxf(amh[0], amh[1]);
             const float s32 = fminf(amax / 7.0f, 65504.0f);
             const _Float16 s16 = (_Float16)s32;
             const float sf = (float)s16;
@@ -552,9 +576,6 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_w4a4_kernel(
                 for (int k = 0; k < 16; ++k) f[k] = code_field(xh[16 * w4 + k], invs);
                 wd[w4] = fold_fields(f);
             }
-            // rows past M fall outside the buffer ranges and are dropped
-            const rsrc_t rq = make_rsrc(nx.qx, M * (N / 2));
-            const int qo = (int)(row * (N / 2) + col0 / 2);
             __builtin_amdgcn_raw_buffer_store_b128(v4i{(int)wd[0].x, (int)wd[0].y, (int)wd[1].x, (int)wd[1].y},
                                                   rq, qo, 0, 0);
             __builtin_amdgcn_raw_buffer_store_b128(v4i{(int)wd[2].x, (int)wd[2].y, (int)wd[3].x, (int)wd[3].y},
@@ -911,12 +932,17 @@ hipError_t launch_gemm_w4a4_next(const uint8_t* qx, const uint16_t* sx, const ui
                                  const uint16_t* bias, int act, int64_t M, int64_t N, int64_t K,
                                  const float* inv_next, const uint16_t* l1t_next, int rank_next,
                                  uint8_t* qx_next, uint16_t* sx_next, float* xl1_next, float* part,
-                                 hipStream_t stream)
+                                 hipStream_t stream, int fmt)
 {
     using C = MainCfg;
     const NextAct nx{inv_next, l1t_next, rank_next, qx_next, sx_next, part};
-    if (act) launch_mode<C, 3, 1>(stream, qx, sx, qw, sw, xl1, l2t, rank, bias, nullptr, 0, M, N, K, 0, 0, 0, 0, nullptr, nx);
-    else launch_mode<C, 3, 0>(stream, qx, sx, qw, sw, xl1, l2t, rank, bias, nullptr, 0, M, N, K, 0, 0, 0, 0, nullptr, nx);
+    if (fmt == 1) {
+        if (act) launch_mode<C, 3, 1, 1>(stream, qx, sx, qw, sw, xl1, l2t, rank, bias, nullptr, 0, M, N, K, 0, 0, 0, 0, nullptr, nx);
+        else launch_mode<C, 3, 0, 1>(stream, qx, sx, qw, sw, xl1, l2t, rank, bias, nullptr, 0, M, N, K, 0, 0, 0, 0, nullptr, nx);
+    } else {
+        if (act) launch_mode<C, 3, 1>(stream, qx, sx, qw, sw, xl1, l2t, rank, bias, nullptr, 0, M, N, K, 0, 0, 0, 0, nullptr, nx);
+        else launch_mode<C, 3, 0>(stream, qx, sx, qw, sw, xl1, l2t, rank, bias, nullptr, 0, M, N, K, 0, 0, 0, 0, nullptr, nx);
+    }
     if (rank_next > 0) {
         const int64_t n4 = M * rank_next / 4;
         hipLaunchKernelGGL(sum_tile_partials_kernel, dim3((unsigned)((n4 + 63) / 64)), dim3(256), 0, stream, part,

@@ -345,6 +345,29 @@ svdq_status svdq_gemm_w4a4_quant_next(const uint8_t* qx, const void* sx_f16, int
                                       uint8_t* qx_next, void* sx_next_f16, float* xl1_next,
                                       void* workspace, int64_t workspace_bytes, void* stream);
 
+/* svdq_gemm_mxfp4_quant_next -- the MXFP4 form of svdq_gemm_w4a4_quant_next:
+ * svdq_gemm_mxfp4 whose bf16 output H = bf16(act(Y)) is not stored but
+ * quantised for the next MXFP4 layer in the same kernel, with results
+ * identical to svdq_quantize_act_mxfp4(H, inv_lambda_next, l1t_next,
+ * rank_next) up to the summation order of xl1_next. Arguments, shapes,
+ * workspace (svdq_gemm_w4a4_quant_next_workspace_size) and errors as for
+ * svdq_gemm_w4a4_quant_next, except the formats: qx, sx, qw, sw as for
+ * svdq_gemm_mxfp4; qx_next [M][N/2] E2M1 nibbles and sx_next the E8M0
+ * exponent records [ceil(N/256)][M][8] of svdq_quantize_act_mxfp4 (the
+ * records' bytes for padding blocks of a last partial quad are not
+ * written). A block-level MXFP4 MLP then needs no activation pass for its
+ * second linear (the 4-bit floating-point path the remio.ai page names the
+ * fastest, section on hardware support dividing the fastest and the widest
+ * paths; the fusion as above).
+ */
+svdq_status svdq_gemm_mxfp4_quant_next(const uint8_t* qx, const void* sx, int64_t M, int64_t K,
+                                       const uint8_t* qw, const void* sw, int64_t N,
+                                       const float* xl1, const void* l2t, int32_t rank,
+                                       const void* bias, int32_t act,
+                                       const float* inv_lambda_next, const void* l1t_next, int32_t rank_next,
+                                       uint8_t* qx_next, void* sx_next, float* xl1_next,
+                                       void* workspace, int64_t workspace_bytes, void* stream);
+
 /* svdq_gemm_w4a4_quant_next_noalloc -- svdq_gemm_w4a4_quant_next for callers
  * that cannot allocate device memory: code recorded under HIP graph capture,
  * tight serving loops, harnesses that forbid hipMalloc. Same arguments

@@ -139,24 +139,34 @@ def test_quantize_layer_rejects_host_tensors():
 
 # ---------------------------------------------------------------- fused next-layer pass
 
-def _next(lib, **kw):
+def _next(lib, entry="svdq_gemm_w4a4_quant_next", **kw):
     a = dict(qx=A, sx=B, M=128, K=256, qw=C, sw=D, N=256, xl1=E, l2t=E + 0x10000, rank=16, bias=None, act=1,
              inv=A + 0x20000, l1t=B + 0x20000, r2=32, qxn=C + 0x20000, sxn=D + 0x20000, xl1n=E + 0x20000,
              ws=A + 0x80000, wsb=1 << 30)
     a.update(kw)
-    return lib.svdq_gemm_w4a4_quant_next(a["qx"], a["sx"], a["M"], a["K"], a["qw"], a["sw"], a["N"], a["xl1"],
-                                         a["l2t"], a["rank"], a["bias"], a["act"], a["inv"], a["l1t"], a["r2"],
-                                         a["qxn"], a["sxn"], a["xl1n"], a["ws"], a["wsb"], None)
+    return getattr(lib, entry)(a["qx"], a["sx"], a["M"], a["K"], a["qw"], a["sw"], a["N"], a["xl1"],
+                               a["l2t"], a["rank"], a["bias"], a["act"], a["inv"], a["l1t"], a["r2"],
+                               a["qxn"], a["sxn"], a["xl1n"], a["ws"], a["wsb"], None)
 
 
+NEXT_ENTRIES = ["svdq_gemm_w4a4_quant_next", "svdq_gemm_mxfp4_quant_next"]
+
+
+@pytest.mark.parametrize("entry", NEXT_ENTRIES)
 @pytest.mark.parametrize("kw,status", [
     (dict(N=200), SHAPE), (dict(N=192), SHAPE), (dict(K=96), SHAPE), (dict(r2=80), SHAPE), (dict(r2=8), SHAPE),
     (dict(rank=20), SHAPE), (dict(act=5), UNSUP), (dict(wsb=100), SHAPE), (dict(inv=None), NULL),
     (dict(l1t=None), NULL), (dict(ws=None), NULL), (dict(qxn=None), NULL), (dict(xl1=None), NULL),
     (dict(inv=A + 4), ALIGN), (dict(l1t=B + 2), ALIGN), (dict(qxn=C + 8), ALIGN), (dict(M=-1), SHAPE),
 ])
-def test_quant_next_rejects(lib, kw, status):
-    assert _next(lib, **kw) == status
+def test_quant_next_rejects(lib, entry, kw, status):
+    assert _next(lib, entry, **kw) == status
+
+
+def test_quant_next_scale_alignment_by_format(lib):
+    """INT4 scales are fp16 (2-byte aligned); MXFP4 exponents are bytes."""
+    assert _next(lib, "svdq_gemm_w4a4_quant_next", sxn=D + 0x20001) == ALIGN
+    assert _next(lib, "svdq_gemm_mxfp4_quant_next", sxn=D + 0x20001) in (OK, DEVICE)
 
 
 def test_quant_next_workspace_and_empty(lib):
@@ -169,9 +179,10 @@ def test_quant_next_workspace_and_empty(lib):
     assert _next(lib, r2=0, l1t=None, xl1n=None, ws=None, wsb=0) in (OK, DEVICE)
 
 
-def test_quant_next_without_gpu_reports_device_error(lib):
+@pytest.mark.parametrize("entry", NEXT_ENTRIES)
+def test_quant_next_without_gpu_reports_device_error(lib, entry):
     _no_gpu()
-    assert _next(lib) == DEVICE
+    assert _next(lib, entry) == DEVICE
 
 
 def test_noalloc_refuses_beyond_scratch_on_the_host(lib):
