@@ -31,9 +31,16 @@ def build(verbose: bool = False) -> str:
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
+    # The feature flag is meant for the device pass; the host pass also sees
+    # it and prints a notice that it does not know it (one line per source),
+    # which carries no information: drop exactly that line.
+    out = "".join(l for l in (r.stdout + r.stderr).splitlines(keepends=True)
+                  if "'-packed-fp32-ops' is not a recognized feature" not in l)
     if r.returncode != 0:
-        sys.stderr.write(r.stdout + r.stderr)
+        sys.stderr.write(out)
         raise RuntimeError("hipcc failed building libsvdq.so")
+    if verbose and out.strip():
+        sys.stderr.write(out)
     os.replace(tmp, LIB)
     return LIB
 
