@@ -84,3 +84,17 @@ def test_column_slice_rejects_bad_ranges():
             lib.column_slice(qw, sw, None, None, n0, n1)
     with pytest.raises(ValueError):
         lib.column_slice(qw, torch.zeros((32, 4), dtype=torch.float16), None, None, 0, 8)
+
+
+def test_mlp_block_needs_one_format():
+    """SvdqMLP runs both layers in one format (the fused epilogue quantises H
+    for a next layer of the same format); a mixed pair is refused before any
+    buffer is allocated."""
+    z = torch.zeros(1)
+    fc1 = lib.SvdqLinear(z, None, None, torch.zeros((256, 64), dtype=torch.uint8), z, None, 0, fmt="int4")
+    fc2 = lib.SvdqLinear(z, None, None, torch.zeros((64, 128), dtype=torch.uint8), z, None, 0, fmt="mxfp4")
+    with pytest.raises(ValueError, match="format"):
+        lib.SvdqMLP(fc1, fc2, 64)
+    fc3 = lib.SvdqLinear(z, None, None, torch.zeros((64, 128), dtype=torch.uint8), z, None, 0, fmt="nvfp4")
+    with pytest.raises(ValueError, match="format"):
+        lib.SvdqMLP(fc3, fc3, 64)
