@@ -292,7 +292,7 @@ const char* svdq_status_string(svdq_status s) {
 
 const char* svdq_last_error(void) { return g_last_error.c_str(); }
 
-int svdq_version(void) { return 401; }
+int svdq_version(void) { return 402; }
 
 svdq_status svdq_check_device(int device) {
     svdq_status s = check_device_id(device);

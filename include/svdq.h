@@ -147,7 +147,8 @@ const char* svdq_status_string(svdq_status s);
 /* Detail of the last failure on the calling thread ("" if none). */
 const char* svdq_last_error(void);
 
-/* Library version: format version * 100 + revision. */
+/* Library version: format version * 100 + revision (402: format 4, revision 2,
+ * which adds svdq_gemm_mxfp4_quant_next; the formats are unchanged). */
 int svdq_version(void);
 
 /*
