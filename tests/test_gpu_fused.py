@@ -43,7 +43,8 @@ def _sentinel(n):
 
 
 @pytest.mark.parametrize("M,K,N,r,r2", [(200, 512, 1024, 16, 32), (64, 256, 384, 0, 16), (130, 320, 256, 32, 0),
-                                        (128, 192, 512, 32, 64), (257, 3072, 12288, 32, 32)],
+                                        (128, 192, 512, 32, 64), (257, 3072, 12288, 32, 32), (1, 128, 128, 16, 16),
+                                        (33, 64, 640, 0, 48)],
                          ids=lambda v: str(v))
 def test_fused_activation_pass_matches_unfused(M, K, N, r, r2):
     note(f"fused next act M={M} K={K} N={N} r={r} r2={r2}")
@@ -178,7 +179,8 @@ def _check_mx_scales(sf, sa, N):
 
 
 @pytest.mark.parametrize("M,K,N,r,r2", [(200, 512, 1024, 16, 32), (64, 256, 384, 0, 16), (130, 320, 256, 32, 0),
-                                        (128, 192, 512, 32, 64), (257, 3072, 12288, 32, 32)],
+                                        (128, 192, 512, 32, 64), (257, 3072, 12288, 32, 32), (1, 128, 128, 16, 16),
+                                        (33, 64, 640, 0, 48)],
                          ids=lambda v: str(v))
 def test_fused_mxfp4_activation_pass_matches_unfused(M, K, N, r, r2):
     from oracle import mxfp4 as omx
