@@ -570,12 +570,7 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_w4a4_kernel(
             const float invs = (sf > 0.0f) ? 1.0f / sf : 0.0f;
             uint2 wd[4];
 #pragma unroll
-            for (int w4 = 0; w4 < 4; ++w4) {
-                uint32_t f[16];
-#pragma unroll
-                for (int k = 0; k < 16; ++k) f[k] = code_field(xh[16 * w4 + k], invs);
-                wd[w4] = fold_fields(f);
-            }
+            for (int w4 = 0; w4 < 4; ++w4) wd[w4] = codes16_fp6(xh + 16 * w4, invs);
             __builtin_amdgcn_raw_buffer_store_b128(v4i{(int)wd[0].x, (int)wd[0].y, (int)wd[1].x, (int)wd[1].y},
                                                   rq, qo, 0, 0);
             __builtin_amdgcn_raw_buffer_store_b128(v4i{(int)wd[2].x, (int)wd[2].y, (int)wd[3].x, (int)wd[3].y},
