@@ -52,9 +52,9 @@ PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 # kernel sources they were taken on (their sha256 below); otherwise the
 # traffic is reported as null.
 GEMM_TRAFFIC = {
-    "source_sha256": "9ab9fc9dd2d87cd962d8f31e845f6392b36d621c40660661402b549740ca7bf1",
-    "fetch_kib": 64092.6, "write_kib": 73728.0,          # QKV GEMM, mean of 3276 / 3596 dispatches
-    "fetch_factor": 128134.0 / 64078.9,                   # device copies: bytes written / FETCH_SIZE
+    "source_sha256": "1ea68aef412184ed85ff3f62452ab3ef0c8a6a3872eee4c84e684c0e7d328026",
+    "fetch_kib": 64092.7, "write_kib": 73728.0,          # QKV GEMM, mean of 3236 / 3556 dispatches
+    "fetch_factor": 128134.0 / 64078.7,                   # device copies: bytes written / FETCH_SIZE
     "write_factor": 1.0,                                  # WRITE_SIZE reads the bytes written
 }
 
