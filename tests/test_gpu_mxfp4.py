@@ -87,6 +87,22 @@ def test_mx_act_parity(name, M):
     check_act(qa, qx, sx, xl1, cfg.rank)
 
 
+@pytest.mark.parametrize("M,K,rank", [(300, 12800, 32), (50, 3200, 16), (4645, 3072, 32)], ids=lambda v: str(v))
+def test_mx_act_ring_paths(M, K, rank):
+    """The launch shapes of the LDS-staged kernel (ring loop with uneven
+    group counts per wave, conditional last-round requests, more row blocks
+    than CUs with a ragged last block)."""
+    note(f"mxfp4 act ring M={M} K={K} rank={rank}")
+    x = synth.make_matrix_bf16(M, K, seed=K + rank + 1, std=1.5)
+    rng = np.random.default_rng(K + 1)
+    inv = rng.uniform(0.3, 2.5, K).astype(np.float32)
+    l1 = numfmt.f32_to_bf16_bits((rng.standard_normal((K, rank)) * 0.05).astype(np.float32))
+    qx, sx, xl1 = lib.quantize_act_mxfp4(dev_u16(x), dev(inv), dev_u16(osv.pack_l1_tiles(l1)), rank)
+    torch.cuda.synchronize()
+    qa = omx.quantize_act(x, inv, l1)
+    check_act(qa, qx, sx, xl1, rank)
+
+
 def test_mx_act_edge_values():
     """Exact E2M1 ties, saturation, zero blocks, tiny and clamped exponents."""
     note("mxfp4 act edge values")

@@ -72,6 +72,27 @@ def test_act_quant_ranks_and_no_smoothing(rank, use_inv):
     check_act(qa, qx, sx, xl1, rank)
 
 
+# Launch shapes of the LDS-staged activation kernel: K = 12800 (200 groups:
+# waves with 13 and with 12 groups in the steady ring loop, 16 waves with two
+# slots), K = 3200 (50 groups: a fourth group requested in the last round for
+# two waves only), and 4645 rows (more row blocks than CUs: 8 waves, three
+# slots, two workgroups per CU; a ragged last block).
+RING_SHAPES = [(300, 12800, 32), (50, 3200, 16), (4645, 3072, 32)]
+
+
+@pytest.mark.parametrize("M,K,rank", RING_SHAPES, ids=lambda v: str(v))
+def test_act_quant_ring_paths(M, K, rank):
+    note(f"act_quant ring M={M} K={K} rank={rank}")
+    x = synth.make_matrix_bf16(M, K, seed=K + rank, std=1.5)
+    rng = np.random.default_rng(K)
+    inv = rng.uniform(0.3, 2.5, K).astype(np.float32)
+    l1 = numfmt.f32_to_bf16_bits((rng.standard_normal((K, rank)) * 0.05).astype(np.float32))
+    qx, sx, xl1 = lib.quantize_act(dev_u16(x), dev(inv), dev_u16(osv.pack_l1_tiles(l1)), rank)
+    torch.cuda.synchronize()
+    qa = osv.quantize_act(x, inv, l1)
+    check_act(qa, qx, sx, xl1, rank)
+
+
 def test_act_quant_edge_values():
     """Zero rows, tiny (fp16-subnormal scale) groups, huge groups (saturated
     scale) and exact ties, against the oracle bit for bit."""
