@@ -4,15 +4,11 @@
 // The fusion of the low-rank down-projection with input quantisation is the
 // one the remio.ai page attributes to the original Nunchaku engine (section
 // "SVDQuant moves hard values out of 4-bit"); here it is re-derived for CDNA4:
-//  - one workgroup owns 16 token rows; its waves (16 for ranks up to 32,
-//    else 8, as registers allow; also 8 when there are more row blocks than
-//    CUs, so that two workgroups share a CU and a launch of 4608 tokens has
-//    no second round of workgroups) take the 64-wide groups of K round-robin, so
-//    every row is read from HBM exactly once with 128-byte contiguous row
-//    segments per group; each wave issues the loads of two (with 16 waves)
-//    or six of its groups at once (and the L1 fragments one group ahead)
-//    before it quantises them, to keep enough bytes in flight for HBM while
-//    a SIMD always has some wave whose data has landed;
+//  - one workgroup owns 16 token rows; its waves take the 64-wide groups of
+//    K round-robin, so every row is read from HBM exactly once with 128-byte
+//    contiguous row segments per group; in this register form (8 waves) each
+//    wave issues the loads of six of its groups at once (and the L1
+//    fragments one group ahead) before it quantises them;
 //  - a lane holds 16 consecutive channels of one row (two dwordx4 loads);
 //    the four lanes of a row (lanes l, l^16, l^32, l^48) reduce the group
 //    absmax with two cross-lane max steps;
@@ -40,14 +36,9 @@
 namespace {
 
 constexpr int ROWS = 16;
-// waves per workgroup: 16 (four per SIMD) while the rank leaves room in 128
-// VGPRs (rank <= 32), else 8; more waves with fewer groups in flight each let a
-// SIMD work on whichever wave's data has landed. With more row blocks than
-// CUs, 8 waves of at most 128 VGPRs let two workgroups share a CU.
-__host__ __device__ constexpr int waves_for(int rt) { return rt <= 2 ? 16 : 8; }
 
-// RT = rank / 16 (0..8); FMT 0: INT4 g64, 1: MXFP4; CHT: groups each wave
-// keeps in flight (0: the default for the wave count); WV: waves per workgroup
+// RT = rank / 16 (3..8 here); FMT 0: INT4 g64, 1: MXFP4; CHT: groups each
+// wave keeps in flight (0: six); WV: waves per workgroup
 template <int RT, int FMT, int CHT, int WV>
 __global__ __launch_bounds__(WV * 64) void act_quant_kernel(
     const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t ldx,
@@ -166,7 +157,7 @@ __global__ __launch_bounds__(WV * 64) void act_quant_kernel(
     // the X loads of up to CH groups are all issued before any is processed
     // (by default 16 waves x 2 groups or 8 x 6: 32 or 48 KB per CU in flight);
     // L1 fragments run one group ahead
-    constexpr int CH = CHT ? CHT : (WAVES == 16 || RT <= 2 ? 2 : 6);
+    constexpr int CH = CHT ? CHT : 6;
     static_assert(CH % 2 == 0, "groups are processed in pairs");
     v8bf la[RTX][2], lb[RTX][2];
     for (int c0 = 0; c0 < ((n + CH - 1) / CH) * CH || c0 == 0; c0 += CH) {
@@ -490,14 +481,18 @@ __global__ __launch_bounds__(WV * 64) void act_quant_lds_kernel(
 
 }  // namespace
 
-// LDS of a launch with `waves` waves; act_quant_smem_bytes is the largest
-// any launch of (K, rank) uses
+// LDS of a register-form launch with `waves` waves
 size_t act_quant_smem_bytes_w(int64_t K, int rank, int waves) {
     const int64_t G = K / 64;
     return sizeof(float) * (K + (ROWS * G + 1) / 2 + (size_t)waves * ROWS * rank);
 }
 
-size_t act_quant_smem_bytes(int64_t K, int rank) { return act_quant_smem_bytes_w(K, rank, waves_for(rank / 16)); }
+// LDS a launch of (K, rank) needs: the LDS-staged form (ranks up to 32)
+// uses a fixed amount, at most 16 waves x 3 slots; the register form (8
+// waves) holds K reciprocals and the per-wave partials
+size_t act_quant_smem_bytes(int64_t K, int rank) {
+    return rank <= 32 ? (size_t)16 * 3 * SLOT : act_quant_smem_bytes_w(K, rank, 8);
+}
 
 namespace {
 
@@ -564,10 +559,10 @@ hipError_t launch_fmt(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
 {
     const int64_t blocks = (M + ROWS - 1) / ROWS;
     const dim3 grid((unsigned)blocks);
-    const bool shared_cu = blocks > cus;          // more row blocks than CUs: 8-wave workgroups, two per CU
+    const bool shared_cu = blocks > cus;          // more row blocks than CUs: (8, 3), two workgroups per CU
     // ranks up to 32 with 16 rows of X addressable by 31-bit byte offsets
-    const int cfg = lds_config<FMT>(shared_cu, K);
-    if (cfg >= 0 && rank <= 32 && ldx < ((int64_t)1 << 26) && K < ((int64_t)1 << 26)) {
+    if (rank <= 32) {
+        const int cfg = lds_config<FMT>(shared_cu, K);
         switch (rank / 16) {
         case 0: launch_lds_rank<0, FMT>(cfg, grid, stream, x, M, K, ldx, inv_lambda, l1t, qx, sx, xl1); break;
         case 1: launch_lds_rank<1, FMT>(cfg, grid, stream, x, M, K, ldx, inv_lambda, l1t, qx, sx, xl1); break;
@@ -575,25 +570,11 @@ hipError_t launch_fmt(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
         }
         return hipGetLastError();
     }
+    // ranks 48-128: the register form, 8 waves with six groups in flight each
     switch (rank / 16) {
-    // the MXFP4 form with 16 waves and at least 8 groups per wave (K >= 8192)
-    // runs faster with four groups in flight; the INT4 form does not.
-    // (a row-block count above the CU count takes 8-wave workgroups first)
 #define CASE(RTV) case RTV: \
-        if constexpr (waves_for(RTV) == 16) { \
-            if (shared_cu) { \
-                launch_one<RTV, FMT, 0, 8>(grid, stream, x, M, K, ldx, inv_lambda, l1t, qx, sx, xl1); \
-                break; \
-            } \
-            if constexpr (FMT == 1) { \
-                if (K >= 8192) { \
-                    launch_one<RTV, FMT, 4, 16>(grid, stream, x, M, K, ldx, inv_lambda, l1t, qx, sx, xl1); \
-                    break; \
-                } \
-            } \
-        } \
-        launch_one<RTV, FMT, 0, waves_for(RTV)>(grid, stream, x, M, K, ldx, inv_lambda, l1t, qx, sx, xl1); break;
-        CASE(0) CASE(1) CASE(2) CASE(3) CASE(4) CASE(5) CASE(6) CASE(7) CASE(8)
+        launch_one<RTV, FMT, 0, 8>(grid, stream, x, M, K, ldx, inv_lambda, l1t, qx, sx, xl1); break;
+        CASE(3) CASE(4) CASE(5) CASE(6) CASE(7) CASE(8)
 #undef CASE
         default: return hipErrorInvalidValue;
     }

@@ -175,6 +175,9 @@ svdq_status quantize_act_impl(int mxfp4, const void* x, int64_t M, int64_t K, in
     if ((s = check_rank(rank)) != SVDQ_OK) return s;
     if (ldx < K) return fail(SVDQ_ERR_SHAPE, "ldx = %lld < K = %lld", (long long)ldx, (long long)K);
     if (ldx % 8) return fail(SVDQ_ERR_ALIGN, "ldx = %lld must be a multiple of 8", (long long)ldx);
+    if (ldx >= ((int64_t)1 << 26))
+        return fail(SVDQ_ERR_SHAPE, "ldx = %lld must be below 2^26 (16 rows addressed with 31-bit offsets)",
+                    (long long)ldx);
     if (act_quant_smem_bytes(K, rank) > kMaxLds)
         return fail(SVDQ_ERR_SHAPE, "K = %lld with rank %d exceeds the LDS budget", (long long)K, rank);
     if (M == 0) { g_last_error.clear(); return SVDQ_OK; }   // empty batch: nothing to read or write

@@ -156,7 +156,8 @@ int svdq_version(void);
  * group-64 activation quantisation (the remio.ai page, same section: the
  * original engine fused the low-rank down-projection with input quantisation).
  *
- *  x          bf16 [M][ldx], row m's K values contiguous (ldx >= K, ldx % 8 == 0)
+ *  x          bf16 [M][ldx], row m's K values contiguous (K <= ldx < 2^26,
+ *             ldx % 8 == 0)
  *  inv_lambda fp32 [K] smoothing reciprocals, or NULL for lambda == 1
  *  l1t        the down-projection L1 (K x rank, bf16) in the L1 tile layout
  *             (format v4): an array [K/64][rank/16][2][64][8] whose element
@@ -176,6 +177,9 @@ int svdq_version(void);
  * qx and sx are bit-exact with that definition. xl1 is accumulated in fp32
  * (relative error about 1e-6).
  * Alignment: x, inv_lambda, l1t, qx, sx_f16, xl1 16-byte aligned.
+ * LDS: ranks up to 32 take any K; ranks 48-128 keep K fp32 reciprocals and
+ * per-wave partials in LDS, 4 (K + K/8 + 128 rank) bytes of the 160 KB
+ * (K <= 21824 at rank 128), SVDQ_ERR_SHAPE beyond.
  */
 svdq_status svdq_quantize_act(const void* x, int64_t M, int64_t K, int64_t ldx,
                               const float* inv_lambda, const void* l1t, int32_t rank,

@@ -69,6 +69,20 @@ def test_quantize_act_rejects(lib, kw, status):
     assert lib.svdq_last_error()
 
 
+def test_quantize_act_stride_and_lds_limits(lib):
+    """Row strides from 2^26 elements are refused; ranks up to 32 take any K
+    (the LDS-staged form's LDS does not grow with K), the register form for
+    larger ranks is bounded by its LDS."""
+    big = 1 << 26
+    assert _act(lib, ldx=big) == SHAPE and b"2^26" in lib.svdq_last_error()
+    assert _act(lib, K=21888, ldx=21888, rank=128) == SHAPE
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present: well-formed calls on these placeholder pointers would launch")
+    assert _act(lib, K=40000, ldx=40000, rank=32) == DEVICE
+    assert _act(lib, K=21824, ldx=21824, rank=128) == DEVICE
+
+
 def _gemm(lib, **kw):
     a = dict(qx=A, sx=B, M=64, K=256, qw=C, sw=D, N=128, xl1=E, l2t=E + 4096, rank=16,
              bias=None, act=0, y=E + 65536, ydt=0, ldy=128)
