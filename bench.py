@@ -9,7 +9,8 @@ effective TOPS of that linear, 2*M*N*K / step time.
 Protocol: the first step is timed alone (first_run); the shader clock is read
 idle, after the timed steps and after each GEMM repetition set; one second of
 steps runs before anything is timed (clock and power ramp); then the K timed
-steps, the GEMM alone (5 x 50 launches hot, and over 4 rotated operand sets),
+steps (no events inside them), the same K steps with HIP events around each
+GEMM (the GEMM's duration inside the step: the roofline figure), the GEMM alone (5 x 50 launches hot, and over 4 rotated operand sets),
 the activation kernel over 12 rotated copies of X, a 256 MiB device copy.
 
 In the same run (separate timed loops, reported under "extra"): the AWQ W4A16
@@ -464,15 +465,24 @@ def main():
         step()
     torch.cuda.synchronize()
     log(f"timing {args.steps} steps")
+    # the timed steps carry no events: an event pair around each GEMM adds
+    # 4-10 us of command-processor work per step that is no part of the layer
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(i)
+    for _ in range(args.steps):
+        step()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     mhz_timed = clock()
     ms = wall * 1e3 / args.steps
     flops = 2.0 * M * N * K
     value = flops / (ms * 1e-3) / 1e12
+    # the same K steps again, each GEMM bracketed by HIP events on its stream:
+    # the GEMM's average launch duration inside the step (the roofline figure)
+    t1 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    steps_ev_ms = (time.perf_counter() - t1) * 1e3 / args.steps
     gemm_ms = sum(a.elapsed_time(b) for a, b in marks[:args.steps]) / args.steps
     gemm_tflops = flops / (gemm_ms * 1e-3) / 1e12
     log(f"step {ms:.4f} ms, gemm {gemm_ms * 1e3:.1f} us ({gemm_tflops:.0f} TFLOP/s) at {mhz_timed} MHz")
@@ -520,6 +530,7 @@ def main():
     act_med = statistics.median(act_rot_ms)
     extra = {
         "gemm_us": round(gemm_ms * 1e3, 2),
+        "step_with_gemm_events_us": round(steps_ev_ms * 1e3, 2),
         "gemm_frac_of_int8_peak": round(gemm_tflops / PEAK_INT8_TOPS, 4),
         "sclk_MHz": {"idle_before": mhz_idle, "after_timed_steps": mhz_timed,
                      "after_gemm_reps": mhz_hot},

@@ -26,8 +26,11 @@
 //    folds its own rows.
 //  - About one workgroup per CU: workgroup i owns TPW consecutive column
 //    tiles (TPW = 1, 2, 4, 5 or 8, template; 5 at 4 x 3072 -> 18432 on 256
-//    CUs). Its 8 waves split the group pairs into 8 parts; wave w streams
-//    part w of every tile of the workgroup, pair-major with the tile index a
+//    CUs). Its NW waves (12 for up to 4 token rows and 5 tiles: three per
+//    SIMD, two group pairs each at K = 3072, every load of a wave in flight
+//    at once; 8 otherwise) split the group pairs into NW parts; wave w streams
+//    part w of every tile of the workgroup,
+//    pair-major with the tile index a
 //    compile-time constant, so each tile keeps its own accumulator in
 //    registers and the task stream has no branch. Each wave prepares, in its
 //    own LDS region, exactly what it reads: x~ = x inv_s (bf16 hi/lo in the
@@ -43,9 +46,13 @@
 
 namespace {
 
-constexpr int NT = 512;
-constexpr int NW = NT / 64;       // waves = K parts
-constexpr int BTMAX = 16;         // (pair, tile) tasks per weight batch (rounded down to whole pairs)
+// Waves per workgroup (= K parts) and (pair, tile) tasks per weight batch
+// (rounded down to whole pairs), by token quads: one quad (M <= 4) runs 12
+// waves of two pairs each at K = 3072 (three waves per SIMD fit its
+// registers); more quads, or more than 5 tiles per workgroup, keep more
+// accumulators and run 8 waves.
+__host__ __device__ constexpr int nw_of(int NQ, int TPW) { return (NQ == 1 && TPW <= 5) ? 12 : 8; }
+__host__ __device__ constexpr int btmax_of(int NQ, int TPW) { return nw_of(NQ, TPW) == 12 ? 10 : 16; }
 constexpr int ABLK = 528;         // A block per (quad, pair, step): 32 slots x 16 B + zero slot
 constexpr int MAXT = 8;           // largest tiles-per-workgroup instantiation
 constexpr int LDS_BUDGET = 147456;
@@ -53,7 +60,7 @@ constexpr int LDS_BUDGET = 147456;
 __host__ __device__ inline int quads(int M) { return M <= 4 ? 1 : (M <= 8 ? 2 : 4); }
 
 // reduction buffer: [TPW tiles][NW parts][NQ][4 rows][16 columns] floats
-__host__ __device__ inline int red_bytes(int NQ, int TPW) { return TPW * NW * NQ * 4 * 16 * 4; }
+__host__ __device__ inline int red_bytes(int NQ, int TPW) { return TPW * nw_of(NQ, TPW) * NQ * 4 * 16 * 4; }
 
 // group pairs held in LDS per chunk: A blocks 4 * ABLK per quad, and
 // (scale, offset) pairs 2 groups x 16 TPW columns x 8 B, beside the reduction buffer
@@ -100,13 +107,14 @@ DEV uint4 ld128_stream(rsrc_t r, int off, int soff) {
 DEV uint32_t pk(uint16_t a, uint16_t b) { return (uint32_t)a | ((uint32_t)b << 16); }
 
 template <int NQ, int TPW>
-__global__ __launch_bounds__(NT, 2) void gemv_w4a16_kernel(
+__global__ __launch_bounds__(64 * nw_of(NQ, TPW), nw_of(NQ, TPW) == 12 ? 1 : 2) void gemv_w4a16_kernel(
     const uint16_t* __restrict__ x, int M, int K, const float* __restrict__ inv_s,
     const uint8_t* __restrict__ qwt, const uint16_t* __restrict__ scale_t,
     const uint16_t* __restrict__ zero_t, int N, const uint16_t* __restrict__ bias,
     uint16_t* __restrict__ y)
 {
     constexpr int LNQ = NQ == 1 ? 0 : (NQ == 2 ? 1 : 2);
+    constexpr int NW = nw_of(NQ, TPW), NT = 64 * NW, BTMAX = btmax_of(NQ, TPW);
     constexpr int PB = ((BTMAX / NQ) / TPW > 0) ? (BTMAX / NQ) / TPW : 1;   // pairs per batch
     constexpr int BT = PB * TPW;                                           // tasks per batch
     constexpr int TC = TPW * 16;                                           // columns per workgroup
@@ -396,7 +404,7 @@ void launch(const uint16_t* x, int M, int K, const float* inv_s, const uint8_t* 
     (void)hipFuncSetAttribute((const void*)gemv_w4a16_kernel<NQ, TPW>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BUDGET);
     const int T = N / 16;
-    hipLaunchKernelGGL((gemv_w4a16_kernel<NQ, TPW>), dim3((unsigned)((T + TPW - 1) / TPW)), dim3(NT),
+    hipLaunchKernelGGL((gemv_w4a16_kernel<NQ, TPW>), dim3((unsigned)((T + TPW - 1) / TPW)), dim3(64 * nw_of(NQ, TPW)),
                        LDS_BUDGET, stream, x, M, K, inv_s, qwt, scale, zero, N, bias, y);
 }
 

@@ -45,13 +45,17 @@ def test_awq_full_size():
     check(y, li.x, w)
 
 
-# row quads 1, 2 and 4; an odd number of group pairs (uneven K halves); more
-# than 24 pairs per K half (the batch loop); two LDS chunks (16 rows, K 3072);
-# partial workgroups (N not a multiple of 64)
+# row quads 1, 2 and 4; an odd number of group pairs (uneven K parts); waves
+# without pairs (K 128, 256); more pairs per wave than one batch holds (the
+# batch loop: 1 row at K 16384 with one tile per workgroup, 4 rows at K 6144
+# with five); two LDS chunks (16 rows, K 3072); partial workgroups (N not a
+# multiple of 64)
 @pytest.mark.parametrize("M,K,N,scaled,bias", [(1, 128, 16, False, False), (16, 256, 48, True, True),
                                                (16, 3072, 80, True, True), (5, 1024, 32, True, True),
                                                (7, 2176, 32, True, False), (3, 8192, 64, True, True),
-                                               (2, 3072, 18432 - 64 * 3 + 16, True, True)])
+                                               (2, 3072, 18432 - 64 * 3 + 16, True, True),
+                                               (1, 16384, 32, True, True),
+                                               (4, 6144, 18432 - 64 * 3 + 16, True, False)])
 def test_awq_shapes(M, K, N, scaled, bias):
     note(f"awq gemv M={M} K={K} N={N}")
     rng = np.random.default_rng(M * 1000 + K)
