@@ -23,24 +23,48 @@ def hipcc() -> str:
     return os.path.join(rocm, "bin", "hipcc")
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every HIP source into bit_quantized_diffusion_svdq_amd/libsvdq.so."""
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB + ".tmp"
-    cmd = [hipcc()] + HIPCC_FLAGS + srcs + ["-o", tmp]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    r = subprocess.run(cmd, capture_output=True, text=True)
+def _filter(text: str) -> str:
     # The feature flag is meant for the device pass; the host pass also sees
     # it and prints a notice that it does not know it (one line per source),
     # which carries no information: drop exactly that line.
-    out = "".join(l for l in (r.stdout + r.stderr).splitlines(keepends=True)
-                  if "'-packed-fp32-ops' is not a recognized feature" not in l)
-    if r.returncode != 0:
-        sys.stderr.write(out)
-        raise RuntimeError("hipcc failed building libsvdq.so")
-    if verbose and out.strip():
-        sys.stderr.write(out)
+    return "".join(l for l in text.splitlines(keepends=True)
+                   if "'-packed-fp32-ops' is not a recognized feature" not in l)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every HIP source (in parallel, one hipcc per source) and link
+    them into bit_quantized_diffusion_svdq_amd/libsvdq.so."""
+    import concurrent.futures
+    import tempfile
+
+    compile_flags = [f for f in HIPCC_FLAGS if f != "-shared"]
+    with tempfile.TemporaryDirectory(prefix="svdq_build_") as tmpdir:
+        def compile_one(src):
+            obj = os.path.join(tmpdir, src + ".o")
+            cmd = [hipcc()] + compile_flags + ["-c", os.path.join(CSRC, src), "-o", obj]
+            if verbose:
+                print(" ".join(cmd), flush=True)
+            r = subprocess.run(cmd, capture_output=True, text=True)
+            return obj, r.returncode, _filter(r.stdout + r.stderr)
+
+        jobs = max(1, min(len(SOURCES), os.cpu_count() or 1, 16))
+        with concurrent.futures.ThreadPoolExecutor(jobs) as ex:
+            results = list(ex.map(compile_one, SOURCES))
+        failed = False
+        for (obj, rc, out), src in zip(results, SOURCES):
+            if out.strip() and (rc != 0 or verbose):
+                sys.stderr.write(out)
+            failed |= rc != 0
+        if failed:
+            raise RuntimeError("hipcc failed building libsvdq.so")
+        tmp = LIB + ".tmp"
+        cmd = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC"] + [r[0] for r in results] + ["-o", tmp]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            sys.stderr.write(_filter(r.stdout + r.stderr))
+            raise RuntimeError("linking libsvdq.so failed")
     os.replace(tmp, LIB)
     return LIB
 
