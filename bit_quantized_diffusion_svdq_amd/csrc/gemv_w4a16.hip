@@ -115,6 +115,9 @@ __global__ __launch_bounds__(64 * nw_of(NQ, TPW), nw_of(NQ, TPW) == 12 ? 1 : 2) 
 {
     constexpr int LNQ = NQ == 1 ? 0 : (NQ == 2 ? 1 : 2);
     constexpr int NW = nw_of(NQ, TPW), NT = 64 * NW, BTMAX = btmax_of(NQ, TPW);
+    // token rows per x~ preparation item (8 channels each): two with 12 waves
+    // (whose two pairs of one row quad are then 64 items, one per lane), else four
+    constexpr int RPI = NW == 12 ? 2 : 4, LRH = RPI == 2 ? 1 : 0;
     constexpr int PB = ((BTMAX / NQ) / TPW > 0) ? (BTMAX / NQ) / TPW : 1;   // pairs per batch
     constexpr int BT = PB * TPW;                                           // tasks per batch
     constexpr int TC = TPW * 16;                                           // columns per workgroup
@@ -166,19 +169,21 @@ __global__ __launch_bounds__(64 * nw_of(NQ, TPW), nw_of(NQ, TPW) == 12 ? 1 : 2) 
         const int ps = (wave * np) / NW, pe = ((wave + 1) * np) / NW;
         const int plast = pe > ps ? pe - 1 : ps;
         const int gs = 2 * ps, ng = 2 * (pe - ps), ngd = ng > 0 ? ng : 1;
-        const int xitems = ng * NQ * 8;                         // (group, quad, 8 channels)
+        const int xitems = ng * NQ * 8 * (4 / RPI);             // (group, quad, RPI rows, 8 channels)
         const int sitems = TPW * ng * 2;                        // (tile, group, 8 columns) uint4
 
         // ---- 1. preparation loads (x, inv_s; scales, zero points), issued first
-        auto xload = [&](int it, uint4 (&xr)[4], uint4& s0, uint4& s1) {
+        auto xload = [&](int it, uint4 (&xr)[RPI], uint4& s0, uint4& s1) {
             const int itc = it < xitems ? it : (xitems > 0 ? xitems - 1 : 0);   // clamped: in bounds
-            const int sub = itc & 7, q = (itc >> 3) & (NQ - 1), gl = gs + (itc >> (3 + LNQ));
+            const int sub = itc & 7, rh = (itc >> 3) & (4 / RPI - 1), q = (itc >> (3 + LRH)) & (NQ - 1);
+            const int gl = gs + (itc >> (3 + LRH + LNQ));
             const int k = (g0 + gl) * 64 + sub * 8;
 #pragma unroll
-            for (int rr = 0; rr < 4; ++rr) {
+            for (int j = 0; j < RPI; ++j) {
+                const int rr = rh * RPI + j;
                 const int m = 4 * q + rr;
                 const int mr = m < M ? m : M - 1;               // padded rows read a real row
-                xr[rr] = ld128(rx, (mr * K + k) * 2, 0);
+                xr[j] = ld128(rx, (mr * K + k) * 2, 0);
             }
             if (inv_s) {
                 s0 = ld128(rs, k * 4, 0);
@@ -204,7 +209,7 @@ __global__ __launch_bounds__(64 * nw_of(NQ, TPW), nw_of(NQ, TPW) == 12 ? 1 : 2) 
             sb = ld128_stream(rsc, off, 0);
             zb = ld128_stream(rzr, off, 0);
         };
-        uint4 xr0[4], xs0, xs1, sb0, zb0, sb1, zb1;
+        uint4 xr0[RPI], xs0, xs1, sb0, zb0, sb1, zb1;
         xload(lane, xr0, xs0, xs1);
         sload(lane, sb0, zb0);
         sload(lane + 64, sb1, zb1);
@@ -214,16 +219,18 @@ __global__ __launch_bounds__(64 * nw_of(NQ, TPW), nw_of(NQ, TPW) == 12 ? 1 : 2) 
 
         // preparation into LDS: x~ = x inv_s as bf16 hi/lo in A-operand
         // order, and (scale, 128 + zero) per (group, column)
-        auto xprep = [&](const uint4 (&xr)[4], const uint4& s0, const uint4& s1, int it) {
+        auto xprep = [&](const uint4 (&xr)[RPI], const uint4& s0, const uint4& s1, int it) {
             if (it >= xitems) return;
-            const int sub = it & 7, q = (it >> 3) & (NQ - 1), gl = gs + (it >> (3 + LNQ));
+            const int sub = it & 7, rh = (it >> 3) & (4 / RPI - 1), q = (it >> (3 + LRH)) & (NQ - 1);
+            const int gl = gs + (it >> (3 + LRH + LNQ));
             // channels 8 sub .. 8 sub + 7 of group gl: lane p = 2 (gl & 1) + (sub >> 2), step sub & 3
             const int pl = 2 * (gl & 1) + (sub >> 2), st = sub & 3;
             char* blk = s_a + ((q * CP + (gl >> 1)) * 4 + st) * ABLK;
             const uint32_t sr[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
 #pragma unroll
-            for (int rr = 0; rr < 4; ++rr) {
-                const uint32_t w[4] = {xr[rr].x, xr[rr].y, xr[rr].z, xr[rr].w};
+            for (int j = 0; j < RPI; ++j) {
+                const int rr = rh * RPI + j;
+                const uint32_t w[4] = {xr[j].x, xr[j].y, xr[j].z, xr[j].w};
                 uint16_t hi[8], lo[8];
 #pragma unroll
                 for (int o = 0; o < 8; ++o) {
@@ -258,7 +265,7 @@ __global__ __launch_bounds__(64 * nw_of(NQ, TPW), nw_of(NQ, TPW) == 12 ? 1 : 2) 
         // never waits for the weight stream, and no control-flow merge
         // happens while weights are in flight)
         for (int it0 = 64; it0 < xitems; it0 += 64) {
-            uint4 xr[4], s0, s1;
+            uint4 xr[RPI], s0, s1;
             xload(it0 + lane, xr, s0, s1);
             xprep(xr, s0, s1, it0 + lane);
         }
