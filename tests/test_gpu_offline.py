@@ -273,3 +273,28 @@ def test_quantize_layer_end_to_end(name, M):
     _, y64_ref = osv.forward(ref, xs)
     e_gpu, e_ref = rel_fro(y, exact), rel_fro(y64_ref, exact)
     assert abs(e_gpu - e_ref) <= 0.02 * e_ref, (e_gpu, e_ref)
+
+
+def test_packaged_layer_round_trip(tmp_path):
+    """Quantize on the GPU, package (save_layer), load back (load_layer): the
+    loaded layer's arrays are the quantiser's, byte for byte, and the online
+    path on it gives bit-identical outputs."""
+    li, x, w = _layer("tiny", None)
+    cfg = li.cfg
+    note(f"packaged layer tiny K={cfg.K} N={cfg.N} r={cfg.rank}")
+    out = lib.quantize_layer(dev_u16(li.w), dev_u16(li.x), cfg.rank, alpha=cfg.alpha, bias=dev_u16(li.bias))
+    layer = lib.SvdqLinear.from_quantized(out)
+    p = str(tmp_path / "tiny.safetensors")
+    lib.save_layer(p, layer, alpha=cfg.alpha, seed=0)
+    back = lib.load_layer(p, device="cuda")
+    for name in ("inv_lambda", "l1t", "l2t", "qw", "sw", "bias"):
+        a, b = getattr(layer, name), getattr(back, name)
+        assert b.device.type == "cuda" and a.dtype == b.dtype
+        assert torch.equal(a.contiguous().view(torch.uint8), b.contiguous().view(torch.uint8)), name
+    xs = dev_u16(li.x[:64])
+    ys = []
+    for l in (layer, back):
+        qx, sx, xl1 = lib.quantize_act(xs, l.inv_lambda, l.l1t, l.rank)
+        ys.append(lib.w4a4_linear(qx, sx, xl1, l.qw, l.sw, l.l2t, l.bias, l.rank))
+    torch.cuda.synchronize()
+    assert torch.equal(ys[0].view(torch.int16), ys[1].view(torch.int16))
