@@ -528,7 +528,12 @@ def main():
     act_bytes = M * K * 2 + M * K // 2 + M * (K // 64) * 2 + M * R * 4 + K * 4 + R * K * 2
     import statistics
     act_med = statistics.median(act_rot_ms)
+    props = torch.cuda.get_device_properties(dev)
     extra = {
+        "device": {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
+                   "compute_units": props.multi_processor_count,
+                   "hbm_GiB": round(props.total_memory / 2**30, 1), "hip": torch.version.hip,
+                   "torch": torch.__version__, "library_version": lib.load_library().svdq_version()},
         "gemm_us": round(gemm_ms * 1e3, 2),
         "step_with_gemm_events_us": round(steps_ev_ms * 1e3, 2),
         "gemm_frac_of_int8_peak": round(gemm_tflops / PEAK_INT8_TOPS, 4),
