@@ -54,8 +54,8 @@ PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 # traffic is reported as null.
 GEMM_TRAFFIC = {
     "source_sha256": "1ea68aef412184ed85ff3f62452ab3ef0c8a6a3872eee4c84e684c0e7d328026",
-    "fetch_kib": 64111.7, "write_kib": 73728.0,          # QKV GEMM, mean of 3476 / 3716 dispatches
-    "fetch_factor": 128134.0 / 64078.6,                   # device copies: bytes written / FETCH_SIZE
+    "fetch_kib": 64083.6, "write_kib": 73728.0,          # QKV GEMM, mean of 3236 / 3616 dispatches
+    "fetch_factor": 128134.0 / 64078.7,                   # device copies: bytes written / FETCH_SIZE
     "write_factor": 1.0,                                  # WRITE_SIZE reads the bytes written
 }
 
