@@ -46,6 +46,7 @@ _SIGS = {
     "svdq_lowrank_workspace_size": [_I64, _I64, _I32, _I32, _P],
     "svdq_lowrank": [_P, _I64, _I64, _I32, _P, _I32, _I32, _P, _P, _P, _P, _I64, _P],
     "svdq_quantize_residual": [_P, _I64, _I64, _P, _P, _I32, _P, _P, _P],
+    "svdq_quantize_residual_mxfp4": [_P, _I64, _I64, _P, _P, _I32, _P, _P, _P],
     "svdq_pack_lowrank": [_P, _P, _I64, _I64, _I32, _P, _P, _P],
     "svdq_gemm_w4a4_quant_next_workspace_size": [_I64, _I64, _I32, _P],
     "svdq_gemm_w4a4_quant_next": [_P, _P, _I64, _I64, _P, _P, _I64, _P, _P, _I32, _P, _I32,
@@ -236,6 +237,11 @@ def svdq_lowrank(w_hat, K, N, rank, omega, l, power_iters, l1, l2, sigma, worksp
 def svdq_quantize_residual(w_hat, K, N, l1, l2, rank, qw, sw, stream=None):
     _check(load_library().svdq_quantize_residual(_ptr(w_hat), K, N, _ptr(l1), _ptr(l2), rank, _ptr(qw),
                                                  _ptr(sw), _stream(stream)), "svdq_quantize_residual")
+
+
+def svdq_quantize_residual_mxfp4(w_hat, K, N, l1, l2, rank, qw, sw, stream=None):
+    _check(load_library().svdq_quantize_residual_mxfp4(_ptr(w_hat), K, N, _ptr(l1), _ptr(l2), rank, _ptr(qw),
+                                                       _ptr(sw), _stream(stream)), "svdq_quantize_residual_mxfp4")
 
 
 def svdq_pack_lowrank(l1, l2, K, N, rank, l1t, l2t, stream=None):

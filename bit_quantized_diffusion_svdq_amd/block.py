@@ -49,7 +49,7 @@ class SvdqLinear:
         """From the dict quantize_layer() returns."""
         r = d["rank"]
         return cls(d["inv_lambda"], d["l1t"] if r else None, d["l2t"] if r else None, d["qw"], d["sw"],
-                   d.get("bias"), r)
+                   d.get("bias"), r, d.get("fmt", "int4"))
 
 
 class SvdqMLP:

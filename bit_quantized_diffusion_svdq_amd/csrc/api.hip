@@ -46,6 +46,8 @@ hipError_t launch_lowrank(const double* w_hat, int64_t K, int64_t N, int r, cons
                           hipStream_t stream);
 hipError_t launch_quantize_residual(const double* w_hat, int64_t K, int64_t N, const uint16_t* l1,
                                     const uint16_t* l2, int r, uint8_t* qw, uint16_t* sw, hipStream_t stream);
+hipError_t launch_quantize_residual_mxfp4(const double* w_hat, int64_t K, int64_t N, const uint16_t* l1,
+                                          const uint16_t* l2, int r, uint8_t* qw, uint8_t* se, hipStream_t stream);
 hipError_t launch_pack_lowrank(const uint16_t* l1, const uint16_t* l2, int64_t K, int64_t N, int r, uint16_t* l1t,
                                uint16_t* l2t, hipStream_t stream);
 int64_t gemm_next_partial_bytes(int64_t M, int64_t N, int rank_next);
@@ -295,7 +297,7 @@ const char* svdq_status_string(svdq_status s) {
 
 const char* svdq_last_error(void) { return g_last_error.c_str(); }
 
-int svdq_version(void) { return 402; }
+int svdq_version(void) { return 403; }
 
 svdq_status svdq_check_device(int device) {
     svdq_status s = check_device_id(device);
@@ -522,6 +524,24 @@ svdq_status svdq_quantize_residual(const double* w_hat, int64_t K, int64_t N, co
     return launched(launch_quantize_residual(w_hat, K, N, (const uint16_t*)l1, (const uint16_t*)l2, rank, qw,
                                              (uint16_t*)sw_f16, (hipStream_t)stream),
                     "svdq_quantize_residual launch");
+}
+
+svdq_status svdq_quantize_residual_mxfp4(const double* w_hat, int64_t K, int64_t N, const void* l1, const void* l2,
+                                         int32_t rank, uint8_t* qw, uint8_t* sw_e8m0, void* stream) {
+    svdq_status s;
+    if ((s = check_dims(K, N, "svdq_quantize_residual_mxfp4")) != SVDQ_OK) return s;
+    if ((s = check_k(K)) != SVDQ_OK) return s;
+    if (K / 64 > 65535) return fail(SVDQ_ERR_SHAPE, "K = %lld: more than 65535 groups", (long long)K);
+    if (N < 1) return fail(SVDQ_ERR_SHAPE, "N must be >= 1");
+    if (rank < 0 || rank > 112 || rank % 16) return fail(SVDQ_ERR_SHAPE, "rank %d must be a multiple of 16 in [0, 112]", rank);
+    if (!w_hat || !qw || !sw_e8m0 || (rank > 0 && (!l1 || !l2)))
+        return fail(SVDQ_ERR_NULL, "w_hat, qw, sw (and l1, l2 when rank > 0) are required");
+    if (!aligned(w_hat, 8) || !aligned(qw, 16) || (l1 && !aligned(l1, 2)) || (l2 && !aligned(l2, 2)))
+        return fail(SVDQ_ERR_ALIGN, "w_hat 8-byte, qw 16-byte, l1, l2 2-byte alignment");
+    if ((s = check_current_device()) != SVDQ_OK) return s;
+    return launched(launch_quantize_residual_mxfp4(w_hat, K, N, (const uint16_t*)l1, (const uint16_t*)l2, rank, qw,
+                                                   sw_e8m0, (hipStream_t)stream),
+                    "svdq_quantize_residual_mxfp4 launch");
 }
 
 svdq_status svdq_pack_lowrank(const void* l1, const void* l2, int64_t K, int64_t N, int32_t rank, void* l1t,

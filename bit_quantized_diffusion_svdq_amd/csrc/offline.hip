@@ -506,6 +506,58 @@ __global__ __launch_bounds__(256) void residual_q_kernel(const double* __restric
     sw[((g >> 2) * N + n) * 4 + (g & 3)] = __builtin_bit_cast(uint16_t, s16);
 }
 
+// The MXFP4 form of the residual quantisation (the number format of the
+// MXFP4 layer, OCP Microscaling Formats v1.0): the same residual values of
+// one (output column n, group g of 64), then per 32-value block its E8M0
+// exponent e = floor(log2 amax) - 2 (clamped; -127 for a zero block) and the
+// E2M1 codes of R * 2^-e, rounded to nearest with ties to mantissa 0 and
+// saturating at 6, a zero with sign 0 (the activation kernel's MXFP4 step).
+// The 64 nibbles go to qw[n][32 g ..] (element 2i in bits 0-3 of byte i),
+// the two exponent bytes (e + 127) to the group's places in the records
+// [ceil(G/4)][N][8]: block 2 (g % 4) at byte g % 4, block 2 (g % 4) + 1 at
+// byte 4 + g % 4.
+template <int RT>
+__global__ __launch_bounds__(256) void residual_mx_kernel(const double* __restrict__ w_hat, int64_t K, int64_t N,
+                                                          const uint16_t* __restrict__ l1,
+                                                          const uint16_t* __restrict__ l2,
+                                                          uint8_t* __restrict__ qw, uint8_t* __restrict__ se) {
+    constexpr int R = RT * 16;
+    __shared__ float s_l1[64][R > 0 ? R : 1];
+    const int64_t g = blockIdx.y;
+    const int64_t n = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    for (int e = threadIdx.x; e < 64 * R; e += 256) {
+        const int kk = e / (R > 0 ? R : 1), j = e % (R > 0 ? R : 1);
+        s_l1[kk][j] = __uint_as_float((uint32_t)l1[(g * 64 + kk) * R + j] << 16);
+    }
+    __syncthreads();
+    if (n >= N) return;
+    float l2c[R > 0 ? R : 1];
+#pragma unroll
+    for (int j = 0; j < R; ++j) l2c[j] = __uint_as_float((uint32_t)l2[(int64_t)j * N + n] << 16);
+    uint8_t* dst = qw + n * (K / 2) + g * 32;
+    uint8_t* rec = se + ((g >> 2) * N + n) * 8 + (g & 3);
+    for (int b = 0; b < 2; ++b) {
+        float v[32];
+        float amax = 0.0f;
+#pragma unroll
+        for (int kk = 0; kk < 32; ++kk) {
+            const int64_t k = g * 64 + 32 * b + kk;
+            double s = 0.0;
+#pragma unroll
+            for (int j = 0; j < R; ++j) s = fma((double)s_l1[32 * b + kk][j], (double)l2c[j], s);
+            v[kk] = (float)(w_hat[k * N + n] - s);
+            amax = fmaxf(amax, fabsf(v[kk]));
+        }
+        const int e = mx_block_exponent(amax);
+        const float sc = mx_inv_scale(e);
+        float t[32];
+#pragma unroll
+        for (int kk = 0; kk < 32; ++kk) t[kk] = v[kk] * sc;
+        *(uint4*)(dst + 16 * b) = make_uint4(e2m1_x8(t), e2m1_x8(t + 8), e2m1_x8(t + 16), e2m1_x8(t + 24));
+        rec[4 * b] = (uint8_t)(e + 127);
+    }
+}
+
 // groups past the last one in the quad-major scale array hold 0
 __global__ void sw_pad_kernel(uint16_t* __restrict__ sw, int64_t N, int G) {
     const int64_t n = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -704,6 +756,36 @@ hipError_t launch_quantize_residual(const double* w_hat, int64_t K, int64_t N, c
     }
     const int G = (int)(K / 64);
     if (G % 4) hipLaunchKernelGGL(sw_pad_kernel, dim3(blocks_for(N, 256)), dim3(256), 0, stream, sw, N, G);
+    return hipGetLastError();
+}
+
+// exponent bytes of groups past the last one hold 0 (as the packers write them)
+__global__ void se_pad_kernel(uint8_t* __restrict__ se, int64_t N, int G) {
+    const int64_t n = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (n >= N) return;
+    for (int g = G; g < ((G + 3) & ~3); ++g) {
+        uint8_t* rec = se + ((int64_t)(g >> 2) * N + n) * 8 + (g & 3);
+        rec[0] = 0;
+        rec[4] = 0;
+    }
+}
+
+hipError_t launch_quantize_residual_mxfp4(const double* w_hat, int64_t K, int64_t N, const uint16_t* l1,
+                                          const uint16_t* l2, int r, uint8_t* qw, uint8_t* se, hipStream_t stream) {
+    const dim3 grid((unsigned)blocks_for(N, 256), (unsigned)(K / 64));
+    switch (r / 16) {
+        case 0: hipLaunchKernelGGL(residual_mx_kernel<0>, grid, dim3(256), 0, stream, w_hat, K, N, l1, l2, qw, se); break;
+        case 1: hipLaunchKernelGGL(residual_mx_kernel<1>, grid, dim3(256), 0, stream, w_hat, K, N, l1, l2, qw, se); break;
+        case 2: hipLaunchKernelGGL(residual_mx_kernel<2>, grid, dim3(256), 0, stream, w_hat, K, N, l1, l2, qw, se); break;
+        case 3: hipLaunchKernelGGL(residual_mx_kernel<3>, grid, dim3(256), 0, stream, w_hat, K, N, l1, l2, qw, se); break;
+        case 4: hipLaunchKernelGGL(residual_mx_kernel<4>, grid, dim3(256), 0, stream, w_hat, K, N, l1, l2, qw, se); break;
+        case 5: hipLaunchKernelGGL(residual_mx_kernel<5>, grid, dim3(256), 0, stream, w_hat, K, N, l1, l2, qw, se); break;
+        case 6: hipLaunchKernelGGL(residual_mx_kernel<6>, grid, dim3(256), 0, stream, w_hat, K, N, l1, l2, qw, se); break;
+        case 7: hipLaunchKernelGGL(residual_mx_kernel<7>, grid, dim3(256), 0, stream, w_hat, K, N, l1, l2, qw, se); break;
+        default: return hipErrorInvalidValue;
+    }
+    const int G = (int)(K / 64);
+    if (G % 4) hipLaunchKernelGGL(se_pad_kernel, dim3(blocks_for(N, 256)), dim3(256), 0, stream, se, N, G);
     return hipGetLastError();
 }
 

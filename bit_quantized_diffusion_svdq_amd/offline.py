@@ -34,18 +34,22 @@ def block_width(K: int, N: int, rank: int, oversample: int = 16) -> int:
 
 def quantize_layer(w: torch.Tensor, x_calib, rank: int, alpha: float = 0.5, bias=None,
                    power_iters: int = 4, oversample: int = 16, seed: int = 0, smooth: bool = True,
-                   omega=None, keep_factors: bool = False, stream=None) -> dict:
+                   omega=None, keep_factors: bool = False, fmt: str = "int4", stream=None) -> dict:
     """w: bf16 [K, N] on the GPU (K a multiple of 64, N of 8); x_calib: one
     bf16 [M, K] calibration batch or an iterable of them (None with
-    smooth=False). Returns the layer's device arrays: inv_lambda fp32 [K],
-    l1t (tile layout), l2t bf16 [N, r], qw uint8 [N, K/2], sw fp16
-    [ceil(K/256), N, 4], bias; with keep_factors also l1 [K, r], l2 [r, N]
-    (bf16), sigma fp64 [r], w_hat fp64 [K, N]."""
+    smooth=False); fmt "int4" (symmetric INT4, fp16 scale per 64) or "mxfp4"
+    (E2M1 codes, E8M0 exponent per 32; the same smoothing and low-rank
+    branch). Returns the layer's device arrays: inv_lambda fp32 [K], l1t
+    (tile layout), l2t bf16 [N, r], qw uint8 [N, K/2], sw (INT4: fp16
+    [ceil(K/256), N, 4]; MXFP4: uint8 exponent records [ceil(K/256), N, 8]),
+    bias, rank, fmt; with keep_factors also l1 [K, r], l2 [r, N] (bf16),
+    sigma fp64 [r], w_hat fp64 [K, N]."""
     _lib._check_rows(w, "w", torch.bfloat16)
     K, N = w.shape
     dev = w.device
     _lib._require(K % 64 == 0 and N % 8 == 0, f"w must be [K, N] with K % 64 == 0 and N % 8 == 0, got {(K, N)}")
     _lib._require(rank == 0 or (rank % 16 == 0 and 16 <= rank <= 80), f"rank {rank} must be 0 or a multiple of 16 up to 80")
+    _lib._require(fmt in ("int4", "mxfp4"), f"fmt must be 'int4' or 'mxfp4', got {fmt!r}")
     out = {}
     if smooth:
         _lib._require(x_calib is not None, "calibration activations are required when smoothing")
@@ -84,12 +88,17 @@ def quantize_layer(w: torch.Tensor, x_calib, rank: int, alpha: float = 0.5, bias
         _lib.svdq_lowrank(w_hat, K, N, rank, omega, l, power_iters, l1, l2, sigma, ws, nbytes, stream)
     G4 = (K // 64 + 3) // 4
     qw = torch.empty((N, K // 2), dtype=torch.uint8, device=dev)
-    sw = torch.empty((G4, N, 4), dtype=torch.float16, device=dev)
-    _lib.svdq_quantize_residual(w_hat, K, N, l1 if rank else None, l2 if rank else None, rank, qw, sw, stream)
+    if fmt == "int4":
+        sw = torch.empty((G4, N, 4), dtype=torch.float16, device=dev)
+        _lib.svdq_quantize_residual(w_hat, K, N, l1 if rank else None, l2 if rank else None, rank, qw, sw, stream)
+    else:
+        sw = torch.empty((G4, N, 8), dtype=torch.uint8, device=dev)
+        _lib.svdq_quantize_residual_mxfp4(w_hat, K, N, l1 if rank else None, l2 if rank else None, rank, qw, sw,
+                                          stream)
     l1t = torch.empty(K * rank, dtype=torch.bfloat16, device=dev)
     l2t = torch.empty((N, rank), dtype=torch.bfloat16, device=dev)
     _lib.svdq_pack_lowrank(l1, l2, K, N, rank, l1t, l2t, stream)
-    out.update(inv_lambda=inv_lambda, l1t=l1t, l2t=l2t, qw=qw, sw=sw, bias=bias, rank=rank)
+    out.update(inv_lambda=inv_lambda, l1t=l1t, l2t=l2t, qw=qw, sw=sw, bias=bias, rank=rank, fmt=fmt)
     if keep_factors:
         out.update(l1=l1, l2=l2, sigma=sigma, w_hat=w_hat)
     return out

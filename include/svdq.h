@@ -147,8 +147,9 @@ const char* svdq_status_string(svdq_status s);
 /* Detail of the last failure on the calling thread ("" if none). */
 const char* svdq_last_error(void);
 
-/* Library version: format version * 100 + revision (402: format 4, revision 2,
- * which adds svdq_gemm_mxfp4_quant_next; the formats are unchanged). */
+/* Library version: format version * 100 + revision (403: format 4, revision 3,
+ * which adds svdq_quantize_residual_mxfp4; revision 2 added
+ * svdq_gemm_mxfp4_quant_next; the formats are unchanged). */
 int svdq_version(void);
 
 /*
@@ -459,6 +460,20 @@ svdq_status svdq_lowrank(const double* w_hat, int64_t K, int64_t N, int32_t rank
  *   aligned. */
 svdq_status svdq_quantize_residual(const double* w_hat, int64_t K, int64_t N, const void* l1, const void* l2,
                                    int32_t rank, uint8_t* qw, void* sw_f16, void* stream);
+
+/* svdq_quantize_residual_mxfp4 -- the same residual R as svdq_quantize_residual,
+ *   quantised in the MXFP4 layer's number format (OCP Microscaling Formats
+ *   v1.0) per output column n and 32-value block along K: E8M0 exponent
+ *   e = floor(log2 amax) - 2 clamped to [-127, 127] (-127 for a zero block),
+ *   codes = E2M1(R * 2^-e) rounded to nearest, ties to mantissa 0, saturating
+ *   at 6, zero with sign 0. Writes qw [N][K/2] (E2M1 nibbles, element 2i in
+ *   bits 0-3 of byte i; 16-byte aligned) and sw_e8m0, the exponent records
+ *   [ceil(K/256)][N][8] (bytes e + 127; block 8q + 2j + h of a column at byte
+ *   4h + j of record (q, n); blocks past K hold 0): the weight operands of
+ *   svdq_gemm_mxfp4. K a multiple of 64; rank as above. Errors as
+ *   svdq_quantize_residual. */
+svdq_status svdq_quantize_residual_mxfp4(const double* w_hat, int64_t K, int64_t N, const void* l1, const void* l2,
+                                         int32_t rank, uint8_t* qw, uint8_t* sw_e8m0, void* stream);
 
 /* svdq_pack_lowrank -- L1 [K][rank] and L2 [rank][N] (bf16) into the layouts
  *   the online kernels read: l1t (format v4 tiles, 16-byte aligned) for

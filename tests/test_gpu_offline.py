@@ -13,6 +13,7 @@ import torch
 
 import synth
 from oracle import linalg as olin
+from oracle import mxfp4 as omx
 from oracle import svdq as osv
 from oracle.numfmt import bf16_bits_to_f32
 from gpu_util import dev, dev_u16, host_u16, note, rel_fro
@@ -213,6 +214,76 @@ def test_residual_codes_bit_exact_given_factors(K, N, rank):
     qw_ref, sw_ref = _oracle_residual(w_hat, l1, l2, rank)
     assert np.array_equal(qw, qw_ref)
     assert np.array_equal(sw.view(np.uint16), sw_ref.view(np.uint16))
+
+
+def _gpu_residual_mx(w_hat, l1, l2, rank):
+    K, N = w_hat.shape
+    qw = torch.empty((N, K // 2), dtype=torch.uint8, device="cuda")
+    # filled with a pattern: the padding of the last record must be written too
+    se = torch.full(((K // 64 + 3) // 4, N, 8), 0xAB, dtype=torch.uint8, device="cuda")
+    lib.svdq_quantize_residual_mxfp4(dev(w_hat), K, N, dev_u16(l1) if rank else None, dev_u16(l2) if rank else None,
+                                     rank, qw, se)
+    return qw.cpu().numpy(), se.cpu().numpy()
+
+
+def _oracle_residual_mx(w_hat, l1, l2, rank):
+    r = osv.residual(w_hat, l1, l2) if rank else w_hat.astype(np.float32)
+    codes, exps = omx.quantize_rows(np.ascontiguousarray(r.T))
+    return omx.pack_fp4(codes), omx.pack_scales(exps)
+
+
+@pytest.mark.parametrize("K,N,rank", [(512, 512, 16), (192, 200, 32), (320, 8, 0), (256, 264, 112), (3072, 9216, 32)])
+def test_residual_mxfp4_bit_exact_given_factors(K, N, rank):
+    """The MXFP4 residual quantisation: E2M1 codes and E8M0 exponent records
+    bit-exact against the oracle's per-column MXFP4 quantisation of the same
+    residual (ragged N, K not a multiple of 256 (padded records), rank 0 and
+    112, an all-zero column (exponent -127, codes 0), and at rank 0 a column
+    of fp32-subnormal values (clamped exponent)."""
+    note(f"offline residual mxfp4 K={K} N={N} r={rank}")
+    rng = np.random.default_rng(K + N + rank + 1)
+    w_hat = rng.standard_normal((K, N)) * 0.03 * rng.uniform(0.2, 5.0, K)[:, None]
+    w_hat[:, 3 % N] = 0.0
+    l1 = synth.bf16_round((rng.standard_normal((K, rank)) * 0.05).astype(np.float32)) if rank else None
+    l2 = synth.bf16_round((rng.standard_normal((rank, N)) * 0.05).astype(np.float32)) if rank else None
+    if rank:
+        w_hat[:, 3 % N] = (bf16_bits_to_f32(l1).astype(np.float64) @ bf16_bits_to_f32(l2).astype(np.float64))[:, 3 % N]
+    else:
+        w_hat[:, 5 % N] *= 1e-38
+    qw, se = _gpu_residual_mx(w_hat, l1, l2, rank)
+    qw_ref, se_ref = _oracle_residual_mx(w_hat, l1, l2, rank)
+    assert np.array_equal(qw, qw_ref)
+    assert np.array_equal(se, se_ref)
+
+
+def test_quantize_layer_mxfp4_end_to_end():
+    """quantize_layer(fmt="mxfp4") on the tiny layer: smoothing and factors as
+    the INT4 form, the residual in MXFP4 exactly as the oracle quantises the
+    GPU's own factors; the MXFP4 online path on the quantised layer matches the
+    oracle's MXFP4 forward on the same arrays."""
+    li, x, w = _layer("tiny", None)
+    cfg = li.cfg
+    note(f"offline quantize_layer mxfp4 tiny K={cfg.K} N={cfg.N} r={cfg.rank}")
+    out = lib.quantize_layer(dev_u16(li.w), dev_u16(li.x), cfg.rank, alpha=cfg.alpha, bias=dev_u16(li.bias),
+                             keep_factors=True, fmt="mxfp4")
+    torch.cuda.synchronize()
+    l1, l2 = host_u16(out["l1"]), host_u16(out["l2"])
+    w_hat = out["w_hat"].cpu().numpy()
+    qw_ref, se_ref = _oracle_residual_mx(w_hat, l1, l2, cfg.rank)
+    assert out["fmt"] == "mxfp4"
+    assert np.array_equal(out["qw"].cpu().numpy(), qw_ref)
+    assert np.array_equal(out["sw"].cpu().numpy(), se_ref)
+    layer = lib.SvdqLinear.from_quantized(out)
+    assert layer.fmt == "mxfp4"
+    xs = li.x[:64]
+    qx, sx, xl1 = lib.quantize_act_mxfp4(dev_u16(xs), layer.inv_lambda, layer.l1t, cfg.rank)
+    y = lib.mxfp4_linear(qx, sx, xl1, layer.qw, layer.sw, layer.l2t, layer.bias, cfg.rank,
+                         out_dtype=torch.float32).cpu().numpy()
+    codes = omx.unpack_fp4(qw_ref)
+    exps = omx.unpack_scales(se_ref, cfg.K // 32)
+    inv = out["inv_lambda"].cpu().numpy()
+    mw = omx.MxWeights(cfg.K, cfg.N, cfg.rank, inv, l1, l2, codes, exps, li.bias)
+    _, y64 = omx.forward(mw, xs)
+    assert rel_fro(y, y64) < 1e-5
 
 
 @pytest.mark.parametrize("K,N,rank", [(512, 512, 16), (3072, 9216, 32), (192, 24, 48)])

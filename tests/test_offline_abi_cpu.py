@@ -103,6 +103,17 @@ def test_quantize_residual_rejects(lib, kw, status):
 
 
 @pytest.mark.parametrize("kw,status", [
+    (dict(K=96), SHAPE), (dict(N=0), SHAPE), (dict(r=128), SHAPE), (dict(r=8), SHAPE), (dict(qw=None), NULL),
+    (dict(l1=None), NULL), (dict(sw=None), NULL), (dict(qw=C + 8), ALIGN), (dict(w_hat=A + 4), ALIGN),
+])
+def test_quantize_residual_mxfp4_rejects(lib, kw, status):
+    a = dict(w_hat=A, K=256, N=64, l1=B, l2=E, r=16, qw=C, sw=D)
+    a.update(kw)
+    assert lib.svdq_quantize_residual_mxfp4(a["w_hat"], a["K"], a["N"], a["l1"], a["l2"], a["r"], a["qw"], a["sw"],
+                                            None) == status
+
+
+@pytest.mark.parametrize("kw,status", [
     (dict(K=96), SHAPE), (dict(r=20), SHAPE), (dict(N=0), SHAPE), (dict(l1t=None), NULL), (dict(l1t=C + 2), ALIGN),
 ])
 def test_pack_lowrank_rejects(lib, kw, status):
@@ -115,6 +126,7 @@ def test_rank_zero_residual_and_pack_need_no_factors(lib):
     _no_gpu()
     assert lib.svdq_pack_lowrank(None, None, 256, 64, 0, None, None, None) == OK
     assert lib.svdq_quantize_residual(A, 256, 64, None, None, 0, C, D, None) == DEVICE
+    assert lib.svdq_quantize_residual_mxfp4(A, 256, 64, None, None, 0, C, D, None) == DEVICE
 
 
 def test_valid_offline_calls_without_gpu_report_device_error(lib):
