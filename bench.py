@@ -199,11 +199,12 @@ def gemm_traffic_bytes():
     return int(round(1024 * (t["fetch_kib"] * t["fetch_factor"] + t["write_kib"] * t["write_factor"])))
 
 
-def offline_quantize_timing(lib, dev, reps=5):
+def offline_quantize_timing(lib, dev, reps=5, fmt="int4"):
     """The GPU offline quantiser on the QKV weight (3072 x 9216, bf16) with a
     4096-token calibration batch: calibration maxima, smoothing, W_hat, the
-    rank-32 range finder (4 power iterations) and residual packing. Time per
-    layer by HIP events around quantize_layer (its host work included)."""
+    rank-32 range finder (4 power iterations) and residual packing (INT4 or
+    MXFP4). Time per layer by HIP events around quantize_layer (its host work
+    included)."""
     import statistics
 
     import numpy as np
@@ -215,7 +216,7 @@ def offline_quantize_timing(lib, dev, reps=5):
     w, x = bf(li.w), bf(li.x)
     l = min(32 + 16, 3072)
     omega = torch.from_numpy(np.random.default_rng(0).standard_normal((9216, l))).to(dev)
-    run = lambda: lib.quantize_layer(w, x, 32, omega=omega)
+    run = lambda: lib.quantize_layer(w, x, 32, omega=omega, fmt=fmt)
     run()
     torch.cuda.synchronize()
     ms = []
@@ -638,6 +639,7 @@ def main():
             f"unfused graph {statistics.median(pair_graph) * 1e3:.1f})")
         del fc1, fc2, h, y2, blk
         extra["offline_quantize_qkv"] = offline_quantize_timing(lib, dev)
+        extra["offline_quantize_qkv_mxfp4"] = offline_quantize_timing(lib, dev, fmt="mxfp4")
         log(f"offline quantiser, QKV layer: {extra['offline_quantize_qkv']['median_ms']} ms")
         extra["mxfp4_block"] = mxfp4_block(lib, dev)
         log(f"mxfp4 block {extra['mxfp4_block']['block_us']} us, with the fused MLP "
