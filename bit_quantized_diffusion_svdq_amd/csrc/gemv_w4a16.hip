@@ -161,6 +161,11 @@ __global__ __launch_bounds__(64 * nw_of(NQ, TPW), nw_of(NQ, TPW) == 12 ? 1 : 2) 
         for (int q = 0; q < NQ; ++q) acc[t][q] = v4f{0.f, 0.f, 0.f, 0.f};
 
     for (int pc0 = 0; pc0 < KP; pc0 += CP) {
+        // A wave's preparation (its loads, x~ and the scales into LDS) runs at
+        // a raised issue priority, so waves still preparing are not held back
+        // by waves already streaming tasks on the same SIMD; it drops back
+        // before the task stream (measured: 2.5 % per launch).
+        __builtin_amdgcn_s_setprio(3);
         const int np = (KP - pc0) < CP ? (KP - pc0) : CP;       // pairs in this chunk
         const int g0 = 2 * pc0;                                 // first group of this chunk
         // this wave's pairs [ps, pe) of the chunk = its groups [gs, gs + ng); the
@@ -309,6 +314,7 @@ __global__ __launch_bounds__(64 * nw_of(NQ, TPW), nw_of(NQ, TPW) == 12 ? 1 : 2) 
         sprep(sb0, zb0, lane);
         sprep(sb1, zb1, lane + 64);
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        __builtin_amdgcn_s_setprio(0);
 
         // ---- 4. stream the tasks, pair by pair: the pair's A fragments are
         // read once and serve its TPW tiles; X (the per-row group sums of
