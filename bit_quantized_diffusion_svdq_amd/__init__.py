@@ -12,10 +12,10 @@ from ._lib import (SvdqError, awq_gemv_w4a16, check_device, library_path, load_l
                    LayerDesc, LayerSizes, layer_desc, layer_sizes, svdq_validate_desc, validate_desc,
                    svdq_probe_clock, svdq_probe_read, svdq_calib_absmax, svdq_smoothing,
                    svdq_smooth_weight, svdq_lowrank_workspace_size, svdq_lowrank, svdq_quantize_residual,
-                   svdq_quantize_residual_mxfp4,
+                   svdq_quantize_residual_mxfp4, awq_quantize_weight,
                    svdq_pack_lowrank, svdq_gemm_w4a4_quant_next, svdq_gemm_w4a4_quant_next_workspace_size,
                    w4a4_linear_quant_next, svdq_gemm_mxfp4_quant_next, mxfp4_linear_quant_next)
-from .offline import quantize_layer
+from .offline import quantize_awq, quantize_layer
 from .fused import column_offsets, column_slice, projection_weights, split_columns
 from .graph import CapturedSequence
 from .block import SvdqLinear, SvdqMLP
@@ -28,7 +28,8 @@ __all__ = ["SvdqError", "awq_gemv_w4a16", "check_device", "library_path", "load_
            "LayerDesc", "LayerSizes", "layer_desc", "layer_sizes", "svdq_validate_desc", "validate_desc",
            "svdq_probe_clock", "svdq_probe_read", "svdq_calib_absmax", "svdq_smoothing",
            "svdq_smooth_weight", "svdq_lowrank_workspace_size", "svdq_lowrank", "svdq_quantize_residual",
-           "svdq_pack_lowrank", "svdq_quantize_residual_mxfp4", "quantize_layer", "svdq_gemm_w4a4_quant_next",
+           "svdq_pack_lowrank", "svdq_quantize_residual_mxfp4", "awq_quantize_weight", "quantize_layer",
+           "quantize_awq", "svdq_gemm_w4a4_quant_next",
            "svdq_gemm_w4a4_quant_next_workspace_size", "w4a4_linear_quant_next", "svdq_gemm_mxfp4_quant_next",
            "mxfp4_linear_quant_next", "SvdqLinear", "SvdqMLP",
            "column_offsets", "column_slice", "projection_weights", "split_columns", "CapturedSequence",

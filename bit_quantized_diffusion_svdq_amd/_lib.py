@@ -47,6 +47,7 @@ _SIGS = {
     "svdq_lowrank": [_P, _I64, _I64, _I32, _P, _I32, _I32, _P, _P, _P, _P, _I64, _P],
     "svdq_quantize_residual": [_P, _I64, _I64, _P, _P, _I32, _P, _P, _P],
     "svdq_quantize_residual_mxfp4": [_P, _I64, _I64, _P, _P, _I32, _P, _P, _P],
+    "awq_quantize_weight": [_P, _I64, _I64, _I64, _P, _P, _P, _P, _P],
     "svdq_pack_lowrank": [_P, _P, _I64, _I64, _I32, _P, _P, _P],
     "svdq_gemm_w4a4_quant_next_workspace_size": [_I64, _I64, _I32, _P],
     "svdq_gemm_w4a4_quant_next": [_P, _P, _I64, _I64, _P, _P, _I64, _P, _P, _I32, _P, _I32,
@@ -242,6 +243,11 @@ def svdq_quantize_residual(w_hat, K, N, l1, l2, rank, qw, sw, stream=None):
 def svdq_quantize_residual_mxfp4(w_hat, K, N, l1, l2, rank, qw, sw, stream=None):
     _check(load_library().svdq_quantize_residual_mxfp4(_ptr(w_hat), K, N, _ptr(l1), _ptr(l2), rank, _ptr(qw),
                                                        _ptr(sw), _stream(stream)), "svdq_quantize_residual_mxfp4")
+
+
+def awq_quantize_weight(w, K, N, ldw, inv_s, qwt, scale, zero, stream=None):
+    _check(load_library().awq_quantize_weight(_ptr(w), K, N, ldw, _ptr(inv_s), _ptr(qwt), _ptr(scale), _ptr(zero),
+                                              _stream(stream)), "awq_quantize_weight")
 
 
 def svdq_pack_lowrank(l1, l2, K, N, rank, l1t, l2t, stream=None):

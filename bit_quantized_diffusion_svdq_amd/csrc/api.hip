@@ -48,6 +48,8 @@ hipError_t launch_quantize_residual(const double* w_hat, int64_t K, int64_t N, c
                                     const uint16_t* l2, int r, uint8_t* qw, uint16_t* sw, hipStream_t stream);
 hipError_t launch_quantize_residual_mxfp4(const double* w_hat, int64_t K, int64_t N, const uint16_t* l1,
                                           const uint16_t* l2, int r, uint8_t* qw, uint8_t* se, hipStream_t stream);
+hipError_t launch_awq_quantize(const uint16_t* w, int64_t K, int64_t N, int64_t ldw, const float* inv_s,
+                               uint8_t* qwt, uint16_t* sc, uint16_t* zr, hipStream_t stream);
 hipError_t launch_pack_lowrank(const uint16_t* l1, const uint16_t* l2, int64_t K, int64_t N, int r, uint16_t* l1t,
                                uint16_t* l2t, hipStream_t stream);
 int64_t gemm_next_partial_bytes(int64_t M, int64_t N, int rank_next);
@@ -297,7 +299,7 @@ const char* svdq_status_string(svdq_status s) {
 
 const char* svdq_last_error(void) { return g_last_error.c_str(); }
 
-int svdq_version(void) { return 403; }
+int svdq_version(void) { return 404; }
 
 svdq_status svdq_check_device(int device) {
     svdq_status s = check_device_id(device);
@@ -542,6 +544,23 @@ svdq_status svdq_quantize_residual_mxfp4(const double* w_hat, int64_t K, int64_t
     return launched(launch_quantize_residual_mxfp4(w_hat, K, N, (const uint16_t*)l1, (const uint16_t*)l2, rank, qw,
                                                    sw_e8m0, (hipStream_t)stream),
                     "svdq_quantize_residual_mxfp4 launch");
+}
+
+svdq_status awq_quantize_weight(const void* w_bf16, int64_t K, int64_t N, int64_t ldw, const float* inv_s,
+                                uint8_t* qwt, void* scale_f16, void* zero_f16, void* stream) {
+    svdq_status s;
+    if (K < 128 || K % 128) return fail(SVDQ_ERR_SHAPE, "K = %lld must be a positive multiple of 128", (long long)K);
+    if (N < 16 || N % 16) return fail(SVDQ_ERR_SHAPE, "N = %lld must be a positive multiple of 16", (long long)N);
+    if (ldw < N) return fail(SVDQ_ERR_SHAPE, "ldw = %lld is below N = %lld", (long long)ldw, (long long)N);
+    if (K / 64 > 65535) return fail(SVDQ_ERR_SHAPE, "K = %lld: more than 65535 groups", (long long)K);
+    if (!w_bf16 || !qwt || !scale_f16 || !zero_f16) return fail(SVDQ_ERR_NULL, "w, qwt, scale and zero are required");
+    if (!aligned(w_bf16, 2) || !aligned(qwt, 16) || !aligned(scale_f16, 2) || !aligned(zero_f16, 2) ||
+        (inv_s && !aligned(inv_s, 4)))
+        return fail(SVDQ_ERR_ALIGN, "qwt needs 16-byte alignment, inv_s 4, w, scale and zero 2");
+    if ((s = check_current_device()) != SVDQ_OK) return s;
+    return launched(launch_awq_quantize((const uint16_t*)w_bf16, K, N, ldw, inv_s, qwt, (uint16_t*)scale_f16,
+                                        (uint16_t*)zero_f16, (hipStream_t)stream),
+                    "awq_quantize_weight launch");
 }
 
 svdq_status svdq_pack_lowrank(const void* l1, const void* l2, int64_t K, int64_t N, int32_t rank, void* l1t,

@@ -759,6 +759,57 @@ hipError_t launch_quantize_residual(const double* w_hat, int64_t K, int64_t N, c
     return hipGetLastError();
 }
 
+// AWQ W4A16 weight quantisation (the textbook asymmetric min/max group
+// quantiser the GEMV consumes, with the activation-aware channel scale folded
+// into the weight): one thread per (output column n, group g of 64 input
+// channels). W' = fp32(W / inv_s) (the division in fp64, one rounding); mn,
+// mx of the group; s = fp16(max(mx - mn, 1e-5) / 15) in fp32; z =
+// clamp(rtne(-mn * fp32(1 / s)), 0, 15) kept as an fp16 integer; q =
+// clamp(rtne(W' * fp32(1 / s)) + z, 0, 15). The 32 code bytes of the group go
+// to their place in the GEMV tile layout [N/16][K/128][16][64 B] (block
+// (t, j, c) = bytes 64 j .. 64 j + 63 of column 16 t + c's packed row, element
+// 2i in bits 0-3 of byte i), s and z to [N/16][K/64][16].
+__global__ __launch_bounds__(256) void awq_quantize_kernel(const uint16_t* __restrict__ w, int64_t K, int64_t N,
+                                                           int64_t ldw, const float* __restrict__ inv_s,
+                                                           uint8_t* __restrict__ qwt, uint16_t* __restrict__ sc,
+                                                           uint16_t* __restrict__ zr) {
+    const int64_t g = blockIdx.y;
+    const int64_t n = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (n >= N) return;
+    float v[64];
+    float mn = 0.0f, mx = 0.0f;
+#pragma unroll
+    for (int kk = 0; kk < 64; ++kk) {
+        const int64_t k = g * 64 + kk;
+        const double wv = (double)__uint_as_float((uint32_t)w[k * ldw + n] << 16);
+        v[kk] = inv_s ? (float)(wv / (double)inv_s[k]) : (float)wv;
+        mn = kk == 0 ? v[kk] : fminf(mn, v[kk]);
+        mx = kk == 0 ? v[kk] : fmaxf(mx, v[kk]);
+    }
+    const float rng = fmaxf(mx - mn, 1e-5f);
+    const _Float16 s16 = (_Float16)(rng / 15.0f);
+    const float inv = 1.0f / (float)s16;
+    const float z = fminf(fmaxf(rintf(-mn * inv), 0.0f), 15.0f);
+    uint32_t wd[8];
+#pragma unroll
+    for (int d = 0; d < 8; ++d) {
+        uint32_t word = 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float q = fminf(fmaxf(rintf(v[8 * d + e] * inv) + z, 0.0f), 15.0f);
+            word |= (uint32_t)q << (4 * e);
+        }
+        wd[d] = word;
+    }
+    const int64_t t = n >> 4, c = n & 15, j = g >> 1;
+    uint8_t* dst = qwt + ((t * (K / 128) + j) * 16 + c) * 64 + (g & 1) * 32;
+    *(uint4*)dst = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+    *(uint4*)(dst + 16) = make_uint4(wd[4], wd[5], wd[6], wd[7]);
+    const int64_t o = (t * (K / 64) + g) * 16 + c;
+    sc[o] = __builtin_bit_cast(uint16_t, s16);
+    zr[o] = __builtin_bit_cast(uint16_t, (_Float16)z);
+}
+
 // exponent bytes of groups past the last one hold 0 (as the packers write them)
 __global__ void se_pad_kernel(uint8_t* __restrict__ se, int64_t N, int G) {
     const int64_t n = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -786,6 +837,13 @@ hipError_t launch_quantize_residual_mxfp4(const double* w_hat, int64_t K, int64_
     }
     const int G = (int)(K / 64);
     if (G % 4) hipLaunchKernelGGL(se_pad_kernel, dim3(blocks_for(N, 256)), dim3(256), 0, stream, se, N, G);
+    return hipGetLastError();
+}
+
+hipError_t launch_awq_quantize(const uint16_t* w, int64_t K, int64_t N, int64_t ldw, const float* inv_s,
+                               uint8_t* qwt, uint16_t* sc, uint16_t* zr, hipStream_t stream) {
+    hipLaunchKernelGGL(awq_quantize_kernel, dim3((unsigned)blocks_for(N, 256), (unsigned)(K / 64)), dim3(256), 0,
+                       stream, w, K, N, ldw, inv_s, qwt, sc, zr);
     return hipGetLastError();
 }
 

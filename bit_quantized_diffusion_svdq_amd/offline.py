@@ -102,3 +102,24 @@ def quantize_layer(w: torch.Tensor, x_calib, rank: int, alpha: float = 0.5, bias
     if keep_factors:
         out.update(l1=l1, l2=l2, sigma=sigma, w_hat=w_hat)
     return out
+
+
+def quantize_awq(w: torch.Tensor, inv_s=None, stream=None) -> dict:
+    """The AWQ W4A16 weight quantisation on the GPU: w bf16 [K, N] (K a
+    multiple of 128, N of 16; rows may be strided), inv_s fp32 [K] (the
+    reciprocal activation-aware channel scales) or None. Returns the operands
+    of awq_gemv in its tile layouts: qwt uint8 [N * K / 2], scale_t and
+    zero_t fp16 [N * K / 64], and inv_s."""
+    _lib._check_rows(w, "w", torch.bfloat16)
+    K, N = w.shape
+    dev = w.device
+    _lib._require(K % 128 == 0 and N % 16 == 0, f"w must be [K, N] with K % 128 == 0 and N % 16 == 0, got {(K, N)}")
+    if inv_s is not None:
+        _lib._require(inv_s.dtype == torch.float32 and inv_s.numel() == K and inv_s.is_contiguous(),
+                      f"inv_s must be a contiguous fp32 vector of K = {K} values")
+        _lib._check_same_device(w, inv_s=inv_s)
+    qwt = torch.empty(N * K // 2, dtype=torch.uint8, device=dev)
+    scale_t = torch.empty(N * K // 64, dtype=torch.float16, device=dev)
+    zero_t = torch.empty(N * K // 64, dtype=torch.float16, device=dev)
+    _lib.awq_quantize_weight(w, K, N, w.stride(0), inv_s, qwt, scale_t, zero_t, stream)
+    return dict(qwt=qwt, scale_t=scale_t, zero_t=zero_t, inv_s=inv_s, K=K, N=N)

@@ -147,9 +147,10 @@ const char* svdq_status_string(svdq_status s);
 /* Detail of the last failure on the calling thread ("" if none). */
 const char* svdq_last_error(void);
 
-/* Library version: format version * 100 + revision (403: format 4, revision 3,
- * which adds svdq_quantize_residual_mxfp4; revision 2 added
- * svdq_gemm_mxfp4_quant_next; the formats are unchanged). */
+/* Library version: format version * 100 + revision (404: format 4, revision 4,
+ * which adds awq_quantize_weight; revision 3 added
+ * svdq_quantize_residual_mxfp4, revision 2 svdq_gemm_mxfp4_quant_next; the
+ * formats are unchanged). */
 int svdq_version(void);
 
 /*
@@ -474,6 +475,24 @@ svdq_status svdq_quantize_residual(const double* w_hat, int64_t K, int64_t N, co
  *   svdq_quantize_residual. */
 svdq_status svdq_quantize_residual_mxfp4(const double* w_hat, int64_t K, int64_t N, const void* l1, const void* l2,
                                          int32_t rank, uint8_t* qw, uint8_t* sw_e8m0, void* stream);
+
+/* awq_quantize_weight -- the AWQ W4A16 weight quantisation on the GPU, into
+ *   the operands of awq_gemv_w4a16 (the textbook asymmetric min/max group
+ *   quantiser with the activation-aware channel scale folded into the
+ *   weight):
+ *   w        bf16 [K][ldw] weight (row k = input channel, N <= ldw columns)
+ *   inv_s    fp32 [K] reciprocal channel scales, or NULL (no scaling)
+ *   W' = fp32(W / inv_s) (division in fp64, one rounding); per (output
+ *   column n, group g of 64 input channels): mn, mx of the group,
+ *   s = fp16(max(mx - mn, 1e-5) / 15) in fp32, z = clamp(rtne(-mn * fp32(1 / s)),
+ *   0, 15), q = clamp(rtne(W' * fp32(1 / s)) + z, 0, 15).
+ *   Writes qwt (codes in the GEMV tile layout, [N/16][K/128][16][64 bytes],
+ *   16-byte aligned) and scale_f16 / zero_f16 ([N/16][K/64][16] fp16; z is
+ *   an integer). K a positive multiple of 128, N of 16. Errors: shapes ->
+ *   SVDQ_ERR_SHAPE, NULL pointers -> SVDQ_ERR_NULL, alignment ->
+ *   SVDQ_ERR_ALIGN, no gfx950 device -> SVDQ_ERR_DEVICE. */
+svdq_status awq_quantize_weight(const void* w_bf16, int64_t K, int64_t N, int64_t ldw, const float* inv_s,
+                                uint8_t* qwt, void* scale_f16, void* zero_f16, void* stream);
 
 /* svdq_pack_lowrank -- L1 [K][rank] and L2 [rank][N] (bf16) into the layouts
  *   the online kernels read: l1t (format v4 tiles, 16-byte aligned) for

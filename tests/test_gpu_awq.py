@@ -67,3 +67,44 @@ def test_awq_shapes(M, K, N, scaled, bias):
     y = run(x, w)
     torch.cuda.synchronize()
     check(y, x, w)
+
+
+
+# ---------------------------------------------------------------- weight quantisation on the GPU
+
+@pytest.mark.parametrize("K,N,scaled,strided", [(3072, 18432, True, False), (256, 48, False, False),
+                                                (640, 64, True, True), (128, 16, True, False)])
+def test_awq_quantize_weight_bit_exact(K, N, scaled, strided):
+    """quantize_awq on the GPU gives the oracle's codes, scales and zero
+    points in the GEMV tile layouts bit for bit (full adaLN size; no channel
+    scale; strided weight rows; one group pair), including groups the test
+    makes degenerate: a constant group (range below the 1e-5 floor), an
+    all-negative and an all-positive group (zero point clamped at 15 / 0);
+    the GEMV on the GPU-quantised weights then equals the GEMV on the
+    oracle's arrays bit for bit."""
+    note(f"awq quantize weight K={K} N={N} scaled={scaled} strided={strided}")
+    rng = np.random.default_rng(K + N)
+    wb = synth.make_matrix_bf16(K, N, seed=K * 3 + N, std=0.02)
+    w64 = numfmt.bf16_bits_to_f32(wb).astype(np.float64)
+    w64[0:64, 1] = 0.0125                        # constant group
+    w64[64:128, 2] = -np.abs(w64[64:128, 2]) - 0.01   # all negative
+    w64[0:64, 3] = np.abs(w64[0:64, 3]) + 0.01        # all positive
+    wb = synth.bf16_round(w64.astype(np.float32))
+    sc = rng.uniform(0.5, 2.0, K).astype(np.float32) if scaled else None
+    ref = oawq.prepare_awq(wb, sc)
+    wt = dev_u16(wb)
+    if strided:
+        big = torch.zeros((K, N + 24), dtype=torch.bfloat16, device="cuda")
+        big[:, :N] = wt
+        wt = big[:, :N]
+    out = lib.quantize_awq(wt, dev(ref.inv_s) if scaled else None)
+    torch.cuda.synchronize()
+    assert np.array_equal(out["qwt"].cpu().numpy(), ref.qwt)
+    assert np.array_equal(out["scale_t"].cpu().numpy().view(np.uint16), np.asarray(ref.scale_t, np.float16).view(np.uint16))
+    assert np.array_equal(out["zero_t"].cpu().numpy().view(np.uint16), np.asarray(ref.zero_t, np.float16).view(np.uint16))
+    x = synth.make_matrix_bf16(4, K, seed=K + 1)
+    inv = dev(ref.inv_s)
+    y_gpu = lib.awq_gemv(dev_u16(x), inv, out["qwt"], out["scale_t"], out["zero_t"], None, N=N)
+    y_ref = lib.awq_gemv(dev_u16(x), inv, dev(ref.qwt), dev_f16(ref.scale_t), dev_f16(ref.zero_t), None, N=N)
+    torch.cuda.synchronize()
+    assert torch.equal(y_gpu.view(torch.int16), y_ref.view(torch.int16))

@@ -114,6 +114,23 @@ def test_quantize_residual_mxfp4_rejects(lib, kw, status):
 
 
 @pytest.mark.parametrize("kw,status", [
+    (dict(K=192), SHAPE), (dict(K=0), SHAPE), (dict(N=24), SHAPE), (dict(N=0), SHAPE), (dict(ldw=48), SHAPE),
+    (dict(w=None), NULL), (dict(qwt=None), NULL), (dict(scale=None), NULL), (dict(zero=None), NULL),
+    (dict(qwt=C + 8), ALIGN), (dict(w=A + 1), ALIGN), (dict(inv_s=B + 2), ALIGN), (dict(zero=E + 1), ALIGN),
+])
+def test_awq_quantize_weight_rejects(lib, kw, status):
+    a = dict(w=A, K=256, N=64, ldw=64, inv_s=B, qwt=C, scale=D, zero=E)
+    a.update(kw)
+    assert lib.awq_quantize_weight(a["w"], a["K"], a["N"], a["ldw"], a["inv_s"], a["qwt"], a["scale"], a["zero"],
+                                   None) == status
+
+
+def test_awq_quantize_weight_without_gpu_reports_device_error(lib):
+    _no_gpu()
+    assert lib.awq_quantize_weight(A, 256, 64, 64, None, C, D, E, None) == DEVICE
+
+
+@pytest.mark.parametrize("kw,status", [
     (dict(K=96), SHAPE), (dict(r=20), SHAPE), (dict(N=0), SHAPE), (dict(l1t=None), NULL), (dict(l1t=C + 2), ALIGN),
 ])
 def test_pack_lowrank_rejects(lib, kw, status):
