@@ -164,3 +164,93 @@ def load_layer(path: str, device="cuda") -> SvdqLinear:
     dev = torch.device(device)
     t = {k: v.to(dev) for k, v in tensors.items()}
     return SvdqLinear(t["inv_lambda"], t.get("l1t"), t.get("l2t"), t["qw"], t["sw"], t.get("bias"), rank, fmt)
+
+
+# ---------------------------------------------------------------- AWQ W4A16 layers
+
+AWQ_FORMAT_NAME = "awq-w4a16-layer"
+_AWQ_SPECS = {
+    "qwt": (torch.uint8, "unsigned 4-bit codes in the GEMV tile layout [N/16][K/128][16][64 B]"),
+    "scale_t": (torch.float16, "scales [N/16][K/64][16] fp16"),
+    "zero_t": (torch.float16, "zero points (integers 0..15) [N/16][K/64][16] fp16"),
+    "inv_s": (torch.float32, "reciprocal activation-aware channel scales fp32 [K]"),
+    "bias": (torch.bfloat16, "bias bf16 [N]"),
+}
+
+
+def _awq_sizes(K: int, N: int) -> dict:
+    if K < 128 or K % 128 or N < 16 or N % 16:
+        raise ValueError(f"AWQ layer needs K a positive multiple of 128 and N of 16, got K {K}, N {N}")
+    return {"qwt": N * K // 2, "scale_t": N * (K // 64) * 2, "zero_t": N * (K // 64) * 2, "inv_s": K * 4,
+            "bias": N * 2}
+
+
+def save_awq_layer(path: str, layer: dict, bias=None, **provenance) -> dict:
+    """Write an AWQ W4A16 layer (the dict quantize_awq returns: qwt, scale_t,
+    zero_t, inv_s (or None), K, N; plus an optional bf16 bias) with its
+    metadata record. Returns the record."""
+    from safetensors.torch import save_file
+
+    K, N = int(layer["K"]), int(layer["N"])
+    sizes = _awq_sizes(K, N)
+    arrays = {"qwt": layer["qwt"], "scale_t": layer["scale_t"], "zero_t": layer["zero_t"]}
+    if layer.get("inv_s") is not None:
+        arrays["inv_s"] = layer["inv_s"]
+    if bias is not None:
+        arrays["bias"] = bias
+    tensors = {}
+    for name, t in arrays.items():
+        dtype, _ = _AWQ_SPECS[name]
+        if t.dtype != dtype or _nbytes(t) != sizes[name]:
+            raise ValueError(f"{name}: expected {dtype} with {sizes[name]} bytes, got {(t.dtype, _nbytes(t))}")
+        tensors[name] = t.detach().to("cpu").contiguous().reshape(-1)
+    meta = {
+        "format": AWQ_FORMAT_NAME, "format_version": str(FORMAT_VERSION),
+        "library_version": str(_library_version()), "K": str(K), "N": str(N), "group": "64",
+        "layouts": json.dumps({n: _AWQ_SPECS[n][1] for n in tensors}),
+        "provenance": json.dumps(provenance, sort_keys=True),
+    }
+    save_file(tensors, path, metadata=meta)
+    return meta
+
+
+def load_awq_layer(path: str, device="cuda") -> dict:
+    """Read a packaged AWQ W4A16 layer, check it, and return the dict the GEMV
+    takes (qwt, scale_t, zero_t, inv_s or None, bias or None, K, N) on
+    ``device``."""
+    from safetensors.torch import load_file
+
+    meta = read_metadata(path)
+    if meta.get("format") != AWQ_FORMAT_NAME:
+        raise ValueError(f"{path}: format {meta.get('format')!r} is not {AWQ_FORMAT_NAME!r}")
+    if _int_field(meta, "format_version") != FORMAT_VERSION:
+        raise ValueError(f"{path}: format version {meta['format_version']} is not {FORMAT_VERSION}")
+    lib_v = _int_field(meta, "library_version")
+    if lib_v // 100 != _library_version() // 100:
+        raise ValueError(f"{path}: arrays use the layouts of library version {lib_v}, this library "
+                         f"reads format {_library_version() // 100}")
+    if _int_field(meta, "group") != 64:
+        raise ValueError(f"{path}: group {meta['group']} is not 64")
+    K, N = _int_field(meta, "K"), _int_field(meta, "N")
+    try:
+        sizes = _awq_sizes(K, N)
+    except ValueError as e:
+        raise ValueError(f"{path}: malformed layer record ({e})") from None
+    tensors = load_file(path, device="cpu")
+    for name in ("qwt", "scale_t", "zero_t"):
+        if name not in tensors:
+            raise ValueError(f"{path}: array {name!r} is missing")
+    for name, t in tensors.items():
+        if name not in _AWQ_SPECS:
+            raise ValueError(f"{path}: unexpected array {name!r}")
+        dtype, _ = _AWQ_SPECS[name]
+        if t.dtype != dtype:
+            raise ValueError(f"{path}: {name} has dtype {t.dtype}, expected {dtype}")
+        if _nbytes(t) != sizes[name]:
+            raise ValueError(f"{path}: {name} has {_nbytes(t)} bytes, the record (K {K}, N {N}) needs {sizes[name]}")
+    dev = torch.device(device)
+    out = {k: v.to(dev) for k, v in tensors.items()}
+    out.setdefault("inv_s", None)
+    out.setdefault("bias", None)
+    out.update(K=K, N=N)
+    return out

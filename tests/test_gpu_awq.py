@@ -108,3 +108,26 @@ def test_awq_quantize_weight_bit_exact(K, N, scaled, strided):
     y_ref = lib.awq_gemv(dev_u16(x), inv, dev(ref.qwt), dev_f16(ref.scale_t), dev_f16(ref.zero_t), None, N=N)
     torch.cuda.synchronize()
     assert torch.equal(y_gpu.view(torch.int16), y_ref.view(torch.int16))
+
+
+def test_awq_packaged_layer_round_trip(tmp_path):
+    """quantize_awq on the GPU, save_awq_layer, load_awq_layer: the loaded
+    arrays are the quantiser's byte for byte and the GEMV gives bit-identical
+    outputs."""
+    K, N = 512, 64
+    note(f"awq packaged layer K={K} N={N}")
+    wb = synth.make_matrix_bf16(K, N, seed=11, std=0.02)
+    sc = np.random.default_rng(12).uniform(0.5, 2.0, K).astype(np.float32)
+    inv = dev((1.0 / sc.astype(np.float64)).astype(np.float32))
+    b = dev_u16(synth.make_matrix_bf16(1, N, seed=13, std=0.02)[0])
+    out = lib.quantize_awq(dev_u16(wb), inv)
+    p = str(tmp_path / "awq.safetensors")
+    lib.save_awq_layer(p, out, bias=b)
+    back = lib.load_awq_layer(p, device="cuda")
+    for name in ("qwt", "scale_t", "zero_t", "inv_s"):
+        assert torch.equal(out[name].view(torch.uint8), back[name].view(torch.uint8)), name
+    x = dev_u16(synth.make_matrix_bf16(3, K, seed=14))
+    ya = lib.awq_gemv(x, out["inv_s"], out["qwt"], out["scale_t"], out["zero_t"], b, N=N)
+    yb = lib.awq_gemv(x, back["inv_s"], back["qwt"], back["scale_t"], back["zero_t"], back["bias"], N=N)
+    torch.cuda.synchronize()
+    assert torch.equal(ya.view(torch.int16), yb.view(torch.int16))

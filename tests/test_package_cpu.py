@@ -1,6 +1,7 @@
-"""Packaged layers (save_layer / load_layer) on the host: round trips in both
-number formats, the metadata record, and every malformed-file error the
-loader documents. No GPU: arrays stay on the CPU and the library is used
+"""Packaged layers (save_layer / load_layer for SVDQ layers, save_awq_layer /
+load_awq_layer for AWQ W4A16 layers) on the host: round trips in both SVDQ
+number formats and for AWQ, the metadata record, and every malformed-file
+error the loaders document. No GPU: arrays stay on the CPU and the library is used
 only for its host-side checks (svdq_validate_desc, svdq_layer_sizes_of)."""
 import json
 
@@ -112,3 +113,58 @@ def test_load_rejects_files_that_are_not_packaged_layers(tmp_path):
     junk.write_bytes(b"\x10\x00\x00\x00\x00\x00\x00\x00not json at all!")
     with pytest.raises(ValueError, match="not a safetensors file"):
         load_layer(str(junk), device="cpu")
+
+
+# ---------------------------------------------------------------- AWQ W4A16 layers
+
+def make_awq(K=256, N=48, scaled=True, seed=1):
+    g = torch.Generator().manual_seed(seed)
+    return dict(qwt=torch.randint(0, 256, (N * K // 2,), generator=g, dtype=torch.uint8),
+                scale_t=torch.rand(N * K // 64, generator=g).to(torch.float16),
+                zero_t=torch.randint(0, 16, (N * K // 64,), generator=g).to(torch.float16),
+                inv_s=(torch.rand(K, generator=g) + 0.5) if scaled else None, K=K, N=N)
+
+
+@pytest.mark.parametrize("scaled,bias", [(True, True), (False, False)])
+def test_awq_round_trip(tmp_path, scaled, bias):
+    layer = make_awq(scaled=scaled)
+    b = torch.randn(48).to(torch.bfloat16) if bias else None
+    p = str(tmp_path / "awq.safetensors")
+    meta = svdq.save_awq_layer(p, layer, bias=b, seed=3)
+    back = svdq.load_awq_layer(p, device="cpu")
+    assert (back["K"], back["N"]) == (256, 48)
+    for name in ("qwt", "scale_t", "zero_t", "inv_s"):
+        assert same(back[name], layer[name]), name
+    assert same(back["bias"], b)
+    assert read_metadata(p) == meta and meta["format"] == "awq-w4a16-layer"
+
+
+@pytest.mark.parametrize("case,match", [
+    ("format", "format"), ("N_ragged", "malformed layer record"), ("K_mismatch", "bytes"),
+    ("missing", "missing"), ("dtype", "dtype"), ("group", "group"),
+])
+def test_awq_load_rejects(tmp_path, case, match):
+    good = str(tmp_path / "good.safetensors")
+    svdq.save_awq_layer(good, make_awq())
+    edits = {
+        "format": dict(meta=lambda m: m.update(format="svdq-layer")),
+        "N_ragged": dict(meta=lambda m: m.update(N="40")),
+        "K_mismatch": dict(meta=lambda m: m.update(K="512")),
+        "missing": dict(tensors=lambda t: t.pop("zero_t")),
+        "dtype": dict(tensors=lambda t: t.update(scale_t=t["scale_t"].view(torch.bfloat16))),
+        "group": dict(meta=lambda m: m.update(group="128")),
+    }
+    p = rewrite(tmp_path, good, **edits[case])
+    with pytest.raises(ValueError, match=match):
+        svdq.load_awq_layer(p, device="cpu")
+
+
+def test_layer_kinds_are_not_interchangeable(tmp_path):
+    a = str(tmp_path / "awq.safetensors")
+    s = str(tmp_path / "svdq.safetensors")
+    svdq.save_awq_layer(a, make_awq())
+    save_layer(s, make_layer())
+    with pytest.raises(ValueError, match="format"):
+        load_layer(a, device="cpu")
+    with pytest.raises(ValueError, match="format"):
+        svdq.load_awq_layer(s, device="cpu")
