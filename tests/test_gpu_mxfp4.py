@@ -53,21 +53,27 @@ def check_act(qa, qx, sx, xl1, rank):
 
 
 def magnitude(qa_codes, qa_exps, w_codes, w_exps, xl1, l2_bits, bias_bits):
-    """sum of |terms| per output (the scale of the fp32 accumulation error)."""
+    """(T, T_lr): the sum of |terms| per output (the scale of the fp32
+    accumulation error) and its low-rank part alone (whose fp32 input xl1 the
+    GPU splits into bf16 hi + lo, which keeps 16-17 bits)."""
     a = np.abs(omx.dequantize_rows(qa_codes, qa_exps))
     w = np.abs(omx.dequantize_rows(w_codes, w_exps))
     t = a @ w.T
+    t_lr = np.zeros_like(t)
     if xl1 is not None and xl1.shape[1]:
-        t += np.abs(xl1.astype(np.float64)) @ np.abs(numfmt.bf16_bits_to_f32(l2_bits).astype(np.float64))
+        t_lr = np.abs(xl1.astype(np.float64)) @ np.abs(numfmt.bf16_bits_to_f32(l2_bits).astype(np.float64))
+        t += t_lr
     if bias_bits is not None:
         t += np.abs(numfmt.bf16_bits_to_f32(bias_bits).astype(np.float64))[None, :]
-    return t
+    return t, t_lr
 
 
 def fp32_bound_mx(tmag, K, rank):
     # fp32 sums of K / 64 MFMA steps, the low-rank MFMAs, bias: a few ulps of
-    # the magnitude per term that meets the accumulator
-    return 2.0 * (K // 64 + rank + 4) * 2.0 ** -24 * tmag
+    # the magnitude per term that meets the accumulator; plus the residual of
+    # the bf16 hi/lo split of the low-rank input (as for the INT4 form)
+    t, t_lr = tmag
+    return 2.0 * (K // 64 + rank + 4) * 2.0 ** -24 * t + 2.0 ** -16 * t_lr
 
 
 def assert_fp32(y32, y64, tmag, K, rank):
@@ -150,8 +156,11 @@ def test_mx_gemm_tiny(act, bias):
 
 def test_mx_gemm_ragged_and_ranks():
     """Ragged M and N against the tile, rank 0, the maximum rank, a half rank
-    chunk, and K with a partly filled scale quad."""
-    for (M, K, N, r) in [(77, 192, 200, 0), (130, 320, 136, 128), (300, 704, 264, 48)]:
+    chunk, rank 64 (ranks above 32 take the register form of the activation
+    kernel and several low-rank chunks in the GEMM), one row with one group,
+    and K with a partly filled scale quad."""
+    for (M, K, N, r) in [(77, 192, 200, 0), (130, 320, 136, 128), (300, 704, 264, 48), (1, 64, 16, 16),
+                         (64, 512, 96, 64)]:
         note(f"mxfp4 ragged M={M} K={K} N={N} r={r}")
         x = synth.make_matrix_bf16(M, K, seed=M, std=1.0)
         wb = synth.make_matrix_bf16(K, N, seed=N, std=0.05)
