@@ -5,14 +5,16 @@ rank 32) captured into one HIP graph with the library's CapturedSequence.
 Every replay must give outputs bit-identical to the eager launches (the graph
 holds the same launches); replays are interleaved with eager work and
 synchronisations and each one is checked. The eager outputs themselves meet
-the oracle on sampled rows (bf16 within the 2e-3 gate, GELU included)."""
+the oracle on sampled rows, element by element: within half a bf16 ulp of
+the fp64 result plus 1e-4 of its rms (the fp32 accumulation and GELU), GELU
+included."""
 import numpy as np
 import pytest
 import torch
 
 import synth
 from oracle import mxfp4 as omx
-from gpu_util import dev_u16, host_bf16_f64, host_u16, note, rel_fro, sample_rows
+from gpu_util import assert_bf16_output, dev_u16, host_bf16_f64, host_u16, note, sample_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -76,8 +78,9 @@ def test_mx_block_graph_replay_matches_eager():
     for i, (x, w) in enumerate(layers):
         qa = omx.quantize_act(x[rows], w.inv_lambda, w.l1)
         y64 = omx.linear_output(qa.codes, qa.exps, w.qw_codes, w.qw_exps, qa.xl1, w.l2, w.bias, acts[i])
-        assert rel_fro(host_bf16_f64(eager[i])[rows], y64) <= 2e-3, i
+        note(f"mxfp4 block graph: layer {i} against the oracle")
+        assert_bf16_output(host_bf16_f64(eager[i])[rows], y64, 1e-4)
     h = host_u16(eager[2])
     qa = omx.quantize_act(h[rows], w2.inv_lambda, w2.l1)
     y64 = omx.linear_output(qa.codes, qa.exps, w2.qw_codes, w2.qw_exps, qa.xl1, w2.l2, w2.bias)
-    assert rel_fro(host_bf16_f64(eager[3])[rows], y64) <= 2e-3
+    assert_bf16_output(host_bf16_f64(eager[3])[rows], y64, 1e-4)
