@@ -51,6 +51,20 @@ class SvdqLinear:
         return cls(d["inv_lambda"], d["l1t"] if r else None, d["l2t"] if r else None, d["qw"], d["sw"],
                    d.get("bias"), r, d.get("fmt", "int4"))
 
+    def __call__(self, x: torch.Tensor, act: str = "none", out_dtype=torch.bfloat16, y=None,
+                 stream=None) -> torch.Tensor:
+        """Y for bf16 activations x [M, K] (rows may be strided): the
+        activation pass, then the 4-bit GEMM, of this layer's number format,
+        on one stream. Allocates qx, sx, xl1 and (unless y is given) Y."""
+        if self.fmt == "int4":
+            qx, sx, xl1 = _lib.quantize_act(x, self.inv_lambda, self.l1t, self.rank, stream)
+            return _lib.w4a4_linear(qx, sx, xl1, self.qw, self.sw, self.l2t, self.bias, self.rank, act,
+                                    out_dtype, y, stream)
+        _lib._require(self.fmt == "mxfp4", f"unknown number format {self.fmt!r}")
+        qx, sx, xl1 = _lib.quantize_act_mxfp4(x, self.inv_lambda, self.l1t, self.rank, stream)
+        return _lib.mxfp4_linear(qx, sx, xl1, self.qw, self.sw, self.l2t, self.bias, self.rank, act,
+                                 out_dtype, y, stream)
+
 
 class SvdqMLP:
     """fc1 (GELU) -> fc2 on M tokens, both INT4 or both MXFP4. ``forward(x)``

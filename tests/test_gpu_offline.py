@@ -369,3 +369,26 @@ def test_packaged_layer_round_trip(tmp_path):
         ys.append(lib.w4a4_linear(qx, sx, xl1, l.qw, l.sw, l.l2t, l.bias, l.rank))
     torch.cuda.synchronize()
     assert torch.equal(ys[0].view(torch.int16), ys[1].view(torch.int16))
+
+
+@pytest.mark.parametrize("fmt,act", [("int4", "none"), ("mxfp4", "gelu_tanh")])
+def test_layer_call_matches_explicit_launches(fmt, act):
+    """SvdqLinear(x) runs the activation pass and the GEMM of its format:
+    outputs bit-identical to the two explicit calls, bf16 and fp32, on a
+    strided row view."""
+    li, x, w = _layer("tiny", None)
+    cfg = li.cfg
+    note(f"layer call {fmt} act={act}")
+    layer = lib.SvdqLinear.from_quantized(
+        lib.quantize_layer(dev_u16(li.w), dev_u16(li.x), cfg.rank, alpha=cfg.alpha, bias=dev_u16(li.bias), fmt=fmt))
+    big = dev_u16(np.concatenate([li.x[:77], li.x[:77]], axis=1))
+    xs = big[:, :cfg.K]                                   # ldx = 2K
+    qa = lib.quantize_act if fmt == "int4" else lib.quantize_act_mxfp4
+    lin = lib.w4a4_linear if fmt == "int4" else lib.mxfp4_linear
+    for dt in (torch.bfloat16, torch.float32):
+        y = layer(xs, act=act, out_dtype=dt)
+        qx, sx, xl1 = qa(xs, layer.inv_lambda, layer.l1t, layer.rank)
+        y_ref = lin(qx, sx, xl1, layer.qw, layer.sw, layer.l2t, layer.bias, layer.rank, act=act, out_dtype=dt)
+        torch.cuda.synchronize()
+        assert y.dtype == dt and y.shape == (77, cfg.N)
+        assert torch.equal(y.view(torch.uint8), y_ref.view(torch.uint8))
