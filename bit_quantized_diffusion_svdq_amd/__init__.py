@@ -18,7 +18,7 @@ from ._lib import (SvdqError, awq_gemv_w4a16, check_device, library_path, load_l
 from .offline import quantize_awq, quantize_layer
 from .fused import column_offsets, column_slice, projection_weights, split_columns
 from .graph import CapturedSequence
-from .block import SvdqLinear, SvdqMLP
+from .block import SvdqLinear, SvdqMLP, awq_linear
 from .package import load_awq_layer, load_layer, read_metadata, save_awq_layer, save_layer
 
 __all__ = ["SvdqError", "awq_gemv_w4a16", "check_device", "library_path", "load_library",
@@ -33,4 +33,4 @@ __all__ = ["SvdqError", "awq_gemv_w4a16", "check_device", "library_path", "load_
            "svdq_gemm_w4a4_quant_next_workspace_size", "w4a4_linear_quant_next", "svdq_gemm_mxfp4_quant_next",
            "mxfp4_linear_quant_next", "SvdqLinear", "SvdqMLP",
            "column_offsets", "column_slice", "projection_weights", "split_columns", "CapturedSequence",
-           "save_layer", "load_layer", "read_metadata", "save_awq_layer", "load_awq_layer"]
+           "save_layer", "load_layer", "read_metadata", "save_awq_layer", "load_awq_layer", "awq_linear"]

@@ -66,6 +66,14 @@ class SvdqLinear:
                                  out_dtype, y, stream)
 
 
+def awq_linear(x: torch.Tensor, layer: dict, y=None, stream=None) -> torch.Tensor:
+    """Y = (x diag(inv_s)) deq(W) + bias for an AWQ W4A16 layer as
+    quantize_awq() or load_awq_layer() return it (bias from the dict, if
+    any): one GEMV launch. x bf16 [M, K] with M <= 16, contiguous."""
+    return _lib.awq_gemv(x, layer.get("inv_s"), layer["qwt"], layer["scale_t"], layer["zero_t"], layer.get("bias"),
+                         N=layer["N"], y=y, stream=stream)
+
+
 class SvdqMLP:
     """fc1 (GELU) -> fc2 on M tokens, both INT4 or both MXFP4. ``forward(x)``
     copies x into the block's input buffer and runs the three launches;

@@ -129,5 +129,7 @@ def test_awq_packaged_layer_round_trip(tmp_path):
     x = dev_u16(synth.make_matrix_bf16(3, K, seed=14))
     ya = lib.awq_gemv(x, out["inv_s"], out["qwt"], out["scale_t"], out["zero_t"], b, N=N)
     yb = lib.awq_gemv(x, back["inv_s"], back["qwt"], back["scale_t"], back["zero_t"], back["bias"], N=N)
+    yc = lib.awq_linear(x, back)                            # the dict's own bias
     torch.cuda.synchronize()
     assert torch.equal(ya.view(torch.int16), yb.view(torch.int16))
+    assert torch.equal(ya.view(torch.int16), yc.view(torch.int16))
